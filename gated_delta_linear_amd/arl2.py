@@ -1,0 +1,217 @@
+"""Python binding of libarl2 (include/arl2.h): argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels; torch supplies device memory and
+the current stream.  Importing works without a GPU; using a layer requires the built
+library (``python -m gated_delta_linear_amd.build``) and an MI355X (gfx950) device, and
+fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
+
+ARL2_OK = 0
+ARL2_E_INVALID_ARG = 1
+ARL2_E_UNSUPPORTED = 2
+ARL2_E_NO_DEVICE = 3
+ARL2_E_OUT_OF_MEMORY = 4
+ARL2_E_HIP = 5
+ARL2_E_PROTOCOL = 6
+ARL2_BF16 = 0
+ARL2_F32 = 1
+ARL2_MAX_TOKENS = 1 << 20
+
+# every function declared in include/arl2.h, with its ctypes signature
+SIGNATURES = {
+    "arl2_layer_create": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_void_p)]),
+    "arl2_denoise_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_commit_frame": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_destroy": (c_int, [c_void_p]),
+    "arl2_state_read": (c_int, [c_void_p, c_void_p, c_void_p]),
+    "arl2_state_write": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "arl2_frame_index": (c_int64, [c_void_p]),
+    "arl2_device_bytes": (c_size_t, [c_void_p]),
+    "arl2_status_string": (c_char_p, [c_int]),
+    "arl2_last_error": (c_char_p, []),
+}
+
+
+class Arl2Config(Structure):
+    _fields_ = [
+        ("batch", c_int32),
+        ("heads", c_int32),
+        ("head_dim", c_int32),
+        ("tokens_per_frame", c_int32),
+        ("io_dtype", c_int32),
+        ("out_dtype", c_int32),
+        ("softmax_scale", c_float),
+        ("knorm_eps", c_float),
+    ]
+
+
+class Arl2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libarl2.so and attach the C signatures; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_linear_amd.build` "
+                           "(the ARL2 layer has no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().arl2_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load_library().arl2_last_error().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != ARL2_OK:
+        raise Arl2Error(status, f"{what}: {status_string(status)}: {last_error()}")
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev_tensor(x: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> int:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x.data_ptr()
+
+
+class Arl2Layer:
+    """One ARL2 layer on the current GPU (see include/arl2.h for the exact semantics).
+
+    phi_q, phi_k, phi_v: bf16 [H, d, d] device tensors (copied at creation).  Frame tensors
+    q, k, v are bf16 [B, T, H, d]; beta fp32 [B, T, H]; alpha fp32 [B, H]."""
+
+    def __init__(self, phi_q: torch.Tensor, phi_k: torch.Tensor, phi_v: torch.Tensor, batch: int, tokens: int,
+                 out_dtype: torch.dtype = torch.float32, softmax_scale: float = 0.0, knorm_eps: float = 0.0,
+                 stream=None):
+        self._lib = load_library()
+        self._handle = c_void_p()
+        heads, d, _ = phi_q.shape
+        for name, t in (("phi_q", phi_q), ("phi_k", phi_k), ("phi_v", phi_v)):
+            _dev_tensor(t, name, torch.bfloat16, (heads, d, d))
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+        self.batch, self.heads, self.head_dim, self.tokens = int(batch), int(heads), int(d), int(tokens)
+        self.out_dtype = out_dtype
+        self.device = phi_q.device
+        cfg = Arl2Config(self.batch, self.heads, self.head_dim, self.tokens, ARL2_BF16,
+                         ARL2_F32 if out_dtype == torch.float32 else ARL2_BF16, float(softmax_scale), float(knorm_eps))
+        with torch.cuda.device(self.device):
+            st = self._lib.arl2_layer_create(byref(cfg), phi_q.data_ptr(), phi_k.data_ptr(), phi_v.data_ptr(),
+                                             _stream_handle(stream), byref(self._handle))
+        _check(st, "arl2_layer_create")
+
+    # --- shapes -------------------------------------------------------------------------
+    @property
+    def frame_shape(self) -> tuple:
+        return (self.batch, self.tokens, self.heads, self.head_dim)
+
+    @property
+    def state_shape(self) -> tuple:
+        return (self.batch, self.heads, self.head_dim, self.head_dim)
+
+    def _ptr(self):
+        if not self._handle:
+            raise Arl2Error(ARL2_E_PROTOCOL, "layer has been closed")
+        return self._handle
+
+    def new_output(self) -> torch.Tensor:
+        return torch.empty(self.frame_shape, dtype=self.out_dtype, device=self.device)
+
+    # --- the protocol -------------------------------------------------------------------
+    def denoise_step(self, q, k, v, out=None, stream=None) -> torch.Tensor:
+        out = self.new_output() if out is None else out
+        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        _check(self._lib.arl2_denoise_step(self._ptr(), *args, po, _stream_handle(stream)), "arl2_denoise_step")
+        return out
+
+    def commit_frame(self, q, k, v, beta, alpha, out=None, want_output: bool = True, stream=None):
+        B, T, H, _ = self.frame_shape
+        pk = _dev_tensor(k, "k", torch.bfloat16, self.frame_shape)
+        pv = _dev_tensor(v, "v", torch.bfloat16, self.frame_shape)
+        pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
+        pa = _dev_tensor(alpha, "alpha", torch.float32, (B, H))
+        if want_output or out is not None:
+            out = self.new_output() if out is None else out
+            pq = _dev_tensor(q, "q", torch.bfloat16, self.frame_shape)
+            po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        else:
+            pq, po = (q.data_ptr() if isinstance(q, torch.Tensor) else None), None
+        _check(self._lib.arl2_commit_frame(self._ptr(), pq, pk, pv, pb, pa, po, _stream_handle(stream)),
+               "arl2_commit_frame")
+        return out
+
+    # --- checkpoint hooks ---------------------------------------------------------------
+    def state(self, stream=None) -> torch.Tensor:
+        dst = torch.empty(self.state_shape, dtype=torch.float32, device=self.device)
+        _check(self._lib.arl2_state_read(self._ptr(), dst.data_ptr(), _stream_handle(stream)), "arl2_state_read")
+        return dst
+
+    def load_state(self, src: torch.Tensor, frame_index: int, stream=None) -> None:
+        p = _dev_tensor(src, "state", torch.float32, self.state_shape)
+        _check(self._lib.arl2_state_write(self._ptr(), p, int(frame_index), _stream_handle(stream)),
+               "arl2_state_write")
+
+    @property
+    def frame_index(self) -> int:
+        return int(self._lib.arl2_frame_index(self._ptr()))
+
+    @property
+    def device_bytes(self) -> int:
+        return int(self._lib.arl2_device_bytes(self._ptr()))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            h, self._handle = self._handle, c_void_p()
+            _check(self._lib.arl2_destroy(h), "arl2_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -1,0 +1,340 @@
+// State write of the ARL2 layer, once per frame after the clean pass:
+//   S_N = alpha S_{N-1} + K'^T diag(beta) (V' - K' S_{N-1}),
+//   K' = rows of K phi_k scaled to unit length,  V' = V phi_v
+// ("Attend Locally, Remember Linearly", gist.science technical summary, section 2.1: the
+// gated update and the per-head 1x1 maps; section 2.2: one write per frame, after the clean
+// pass, with every token's residual taken against the same S_{N-1}).
+//
+// Two launches.  arl2_commit_partial: one work-group per (stream, head, 128-token chunk)
+// forms the chunk's K', V' and residual in registers and reduces K'^T diag(beta) R over the
+// chunk into a d x d partial.  arl2_commit_reduce: one work-group per (stream, head, 32
+// value columns) adds alpha S_{N-1} and the partials in a fixed order (bitwise
+// reproducible), stores S_N, and prepares what the next frame reads: -S_N as MFMA B
+// fragments (for the next write's K' S product) and (phi_q S_N)^T (for the passes' inter
+// read).
+//
+// Precision: K', S and the residual enter MFMAs as bf16 hi + lo pairs (x = hi + lo to about
+// 16 mantissa bits; products hi*hi + hi*lo + lo*hi), because a single bf16 rounding of any of
+// them costs more than the state tolerance over a long stream.  K, V and the maps are exact
+// in bf16 and need no split.
+#include "arl2_device.h"
+#include "arl2_kernels.h"
+
+namespace arl2 {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+struct CommitShape {
+  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int KS = D / 16;   // k-steps over input features
+  static constexpr int MB = DP / 32;  // 32-blocks over key features (rows of S)
+  static constexpr int NB = DP / 32;  // 32-blocks over value features (columns of S)
+};
+
+// LDS fragment store: [wave][block][k-step of 16 tokens][hi/lo][lane][8]
+template <int D>
+struct PartialSmem {
+  static constexpr int MB = CommitShape<D>::MB;
+  bf16x8 kfrag[4][MB][2][2][64];
+  bf16x8 rfrag[4][MB][2][2][64];
+  float beta[kCommitChunk];
+  float inv_norm[kCommitChunk];
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ beta,
+    const bf16* __restrict__ pkt, const bf16* __restrict__ pvt, const bf16* __restrict__ sneg_hi,
+    const bf16* __restrict__ sneg_lo, float* __restrict__ partial, int T, int H, float eps) {
+  using S = CommitShape<D>;
+  constexpr int DP = S::DP, KS = S::KS, MB = S::MB, NB = S::NB;
+  __shared__ PartialSmem<D> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int chunks = gridDim.x;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t base = ((int64_t)b * T * H + h) * D;
+  const int t0 = chunk * kCommitChunk;
+
+  if (tid < kCommitChunk) {
+    const int t = t0 + tid;
+    sm.beta[tid] = t < T ? beta[((int64_t)b * T + t) * H + h] : 0.f;
+  }
+
+  // This lane's token for the A/B fragments of K and V (row-major, 8 features per lane).
+  const int tok = t0 + 32 * wave + (lane & 31);
+  const bool tok_ok = tok < T;
+  const bf16* pk = pkt + (int64_t)h * DP * D;
+  const bf16* pv = pvt + (int64_t)h * DP * D;
+  const int64_t sb = ((int64_t)b * H + h) * (KS * NB * 64);  // fragment index base
+
+  bf16x8 kf[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    kf[st] = tok_ok ? ld_bf16x8(k + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+
+  // K'^T = phi_k^T K^T (rows = key features, lane column = token) and K' = K phi_k (rows =
+  // tokens, lane column = key feature): the same operands in swapped MFMA slots.
+  f32x16 kt[MB], kk[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    kt[mb] = zero16();
+    kk[mb] = zero16();
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      bf16x8 pf = ld_bf16x8(pk + (32 * mb + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
+      kt[mb] = mfma32(pf, kf[st], kt[mb]);
+      kk[mb] = mfma32(kf[st], pf, kk[mb]);
+    }
+  }
+
+  // Unit rows: this lane holds half of its token's features; the other half is in lane ^ 32.
+  float ss = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss = fmaf(kt[mb][i], kt[mb][i], ss);
+  ss += other_half(ss, lane);
+  const float inv = 1.f / fmaxf(sqrtf(ss), eps);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kt[mb][i] *= inv;
+  if (lane < 32) sm.inv_norm[32 * wave + lane] = inv;
+
+  // R = V' - K' S: first K' (-S) with split operands, then V phi_v accumulated on top.
+  // A fragment of K' for k-step st: register 8 (st % 2) + j of block st / 2.
+  f32x16 r[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) r[nb] = zero16();
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    bf16x8 khi, klo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(kt[st >> 1][8 * (st & 1) + j]); khi[j] = sp_.hi; klo[j] = sp_.lo; }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t fo = (sb + (st * NB + nb) * 64 + lane) * 8;
+      bf16x8 shi = ld_bf16x8(sneg_hi + fo), slo = ld_bf16x8(sneg_lo + fo);
+      r[nb] = mfma32(khi, shi, r[nb]);
+      r[nb] = mfma32(khi, slo, r[nb]);
+      r[nb] = mfma32(klo, shi, r[nb]);
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    bf16x8 vf = tok_ok ? ld_bf16x8(v + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bf16x8 pf = ld_bf16x8(pv + (32 * nb + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
+      r[nb] = mfma32(vf, pf, r[nb]);
+    }
+  }
+  __syncthreads();  // beta and inverse norms of all waves are in LDS
+
+  // beta R and K' (rows = tokens) carry a token per register; scale and store both as
+  // fragments whose contraction runs over the wave's 32 tokens.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tl = 32 * wave + c_row(i, lane);
+    const float bt = sm.beta[tl], in = sm.inv_norm[tl];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) r[nb][i] *= bt;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) kk[mb][i] *= in;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) {
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(kk[mb][8 * ts + j]); hi[j] = sp_.hi; lo[j] = sp_.lo; }
+      sm.kfrag[wave][mb][ts][0][lane] = hi;
+      sm.kfrag[wave][mb][ts][1][lane] = lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(r[mb][8 * ts + j]); hi[j] = sp_.hi; lo[j] = sp_.lo; }
+      sm.rfrag[wave][mb][ts][0][lane] = hi;
+      sm.rfrag[wave][mb][ts][1][lane] = lo;
+    }
+  __syncthreads();
+
+  // P_chunk = sum over the chunk's tokens of K'^T (beta R): wave w owns key-feature blocks
+  // w, w + 4, ...; token blocks are summed in a fixed order.
+  const int nsrc = min(4, (T - t0 + 31) / 32);
+  for (int mb = wave; mb < MB; mb += 4) {
+    f32x16 p[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) p[nb] = zero16();
+    for (int src = 0; src < nsrc; ++src)
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) {
+        const bf16x8 ah = sm.kfrag[src][mb][ts][0][lane], al = sm.kfrag[src][mb][ts][1][lane];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 bh = sm.rfrag[src][nb][ts][0][lane], bl = sm.rfrag[src][nb][ts][1][lane];
+          p[nb] = mfma32(ah, bh, p[nb]);
+          p[nb] = mfma32(ah, bl, p[nb]);
+          p[nb] = mfma32(al, bh, p[nb]);
+        }
+      }
+    float* pb = partial + (((int64_t)b * H + h) * chunks + chunk) * DP * DP;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pb[(32 * mb + c_row(i, lane)) * DP + 32 * nb + (lane & 31)] = p[nb][i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void arl2_commit_reduce_kernel(
+    const float* __restrict__ s_prev, const float* __restrict__ alpha, const float* __restrict__ partial,
+    int chunks, const bf16* __restrict__ pq, float* __restrict__ s_new, bf16* __restrict__ sneg_hi,
+    bf16* __restrict__ sneg_lo, bf16* __restrict__ wt_hi, bf16* __restrict__ wt_lo, int H) {
+  using S = CommitShape<D>;
+  constexpr int DP = S::DP, KS = S::KS, MB = S::MB, NB = S::NB;
+  __shared__ float tile[DP][33];  // S_new[:, 32 nb .. 32 nb + 31], padded against bank conflicts
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * H + h;
+  const float a = alpha ? alpha[bh] : 1.f;
+
+  // S_new = alpha S_prev + sum_c P_c, fixed order over chunks.
+  for (int e = tid; e < DP * 32; e += kThreads) {
+    const int row = e >> 5, col = 32 * nb + (e & 31);
+    float acc = 0.f;
+    if (row < D && col < D) {
+      acc = a * s_prev[(bh * D + row) * D + col];
+      const float* pp = partial + bh * chunks * DP * DP + row * DP + col;
+      for (int c = 0; c < chunks; ++c) acc += pp[(int64_t)c * DP * DP];
+      s_new[(bh * D + row) * D + col] = acc;
+    }
+    tile[row][e & 31] = acc;
+  }
+  __syncthreads();
+
+  // -S_new as B fragments for the next write: k-step st, element j <-> key feature
+  // 16 st + 8 (j / 4) + 4 (l / 32) + j % 4 (the row order of a C block), lane column = value feature.
+  for (int e = tid; e < KS * 64; e += kThreads) {
+    const int st = e >> 6, l = e & 63;
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(-tile[16 * st + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3)][l & 31]); hi[j] = sp_.hi; lo[j] = sp_.lo; }
+    const int64_t fo = ((bh * KS + st) * NB + nb) * 64 + l;
+    reinterpret_cast<bf16x8*>(sneg_hi)[fo] = hi;
+    reinterpret_cast<bf16x8*>(sneg_lo)[fo] = lo;
+  }
+
+  // W = phi_q S_new on this column block; stored transposed and split: W^T [j][i].
+  const bf16* pqh = pq + (int64_t)h * DP * D;
+  for (int mb = wave; mb < MB; mb += 4) {
+    f32x16 w = zero16();
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const bf16x8 af = ld_bf16x8(pqh + (32 * mb + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
+      bf16x8 bhi, blo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(tile[16 * st + 8 * (lane >> 5) + j][lane & 31]); bhi[j] = sp_.hi; blo[j] = sp_.lo; }
+      w = mfma32(af, bhi, w);
+      w = mfma32(af, blo, w);
+    }
+    const int col = 32 * nb + (lane & 31);  // value feature j = row of W^T
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int i0 = 32 * mb + 8 * g + 4 * (lane >> 5);
+      if (i0 < D) {
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { const Bf16Pair sp_ = split_bf16(w[4 * g + e]); hi[e] = sp_.hi; lo[e] = sp_.lo; }
+        const int64_t o = (bh * DP + col) * D + i0;
+        *reinterpret_cast<bf16x4*>(wt_hi + o) = hi;
+        *reinterpret_cast<bf16x4*>(wt_lo + o) = lo;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ void arl2_prep_maps_kernel(const bf16* __restrict__ phi_q, const bf16* __restrict__ phi_k,
+                                      const bf16* __restrict__ phi_v, bf16* __restrict__ pq, bf16* __restrict__ pkt,
+                                      bf16* __restrict__ pvt, int H) {
+  constexpr int DP = CommitShape<D>::DP;
+  const int64_t n = (int64_t)H * DP * D;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int col = e % D, row = (e / D) % DP;
+    const int64_t hh = e / ((int64_t)DP * D);
+    const bool ok = row < D;
+    const int64_t src = (hh * D + row) * D + col;   // phi[h][row][col]
+    const int64_t srt = (hh * D + col) * D + row;   // phi[h][col][row]
+    pq[e] = ok ? phi_q[src] : (bf16)0.f;
+    pkt[e] = ok ? phi_k[srt] : (bf16)0.f;
+    pvt[e] = ok ? phi_v[srt] : (bf16)0.f;
+  }
+}
+
+template <int D>
+hipError_t launch_partial_d(const CommitPartialArgs& a, hipStream_t stream) {
+  dim3 grid(commit_chunks(a.T), a.H, a.B);
+  hipLaunchKernelGGL((arl2_commit_partial_kernel<D>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v), a.beta,
+                     static_cast<const bf16*>(a.pkt), static_cast<const bf16*>(a.pvt),
+                     static_cast<const bf16*>(a.sneg_hi), static_cast<const bf16*>(a.sneg_lo), a.partial, a.T,
+                     a.H, a.knorm_eps);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_reduce_d(const CommitReduceArgs& a, hipStream_t stream) {
+  dim3 grid(CommitShape<D>::NB, a.H, a.B);
+  hipLaunchKernelGGL((arl2_commit_reduce_kernel<D>), grid, dim3(kThreads), 0, stream, a.s_prev, a.alpha,
+                     a.partial, a.chunks, static_cast<const bf16*>(a.pq), a.s_new, static_cast<bf16*>(a.sneg_hi),
+                     static_cast<bf16*>(a.sneg_lo), static_cast<bf16*>(a.wt_hi), static_cast<bf16*>(a.wt_lo),
+                     a.H);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prep_d(const PrepMapsArgs& a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.H * CommitShape<D>::DP * D;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL((arl2_prep_maps_kernel<D>), dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const bf16*>(a.phi_q), static_cast<const bf16*>(a.phi_k),
+                     static_cast<const bf16*>(a.phi_v), static_cast<bf16*>(a.pq), static_cast<bf16*>(a.pkt),
+                     static_cast<bf16*>(a.pvt), a.H);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_commit_partial(int d, const CommitPartialArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_partial_d<16>(a, stream);
+    case 64: return launch_partial_d<64>(a, stream);
+    case 128: return launch_partial_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_commit_reduce(int d, const CommitReduceArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_reduce_d<16>(a, stream);
+    case 64: return launch_reduce_d<64>(a, stream);
+    case 128: return launch_reduce_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prep_maps(int d, const PrepMapsArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_prep_d<16>(a, stream);
+    case 64: return launch_prep_d<64>(a, stream);
+    case 128: return launch_prep_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace arl2

@@ -1,0 +1,350 @@
+// Host runtime of the ARL2 layer library: the C interface declared in include/arl2.h.
+//
+// It owns the protocol of "Attend Locally, Remember Linearly" (gist.science technical
+// summary, section 2.2): passes of a frame only read the state, the clean pass writes it
+// once, and every pass of frame N reads S_{N-1}.  S is double-buffered: the write reads one
+// buffer and fills the other, and the buffers swap when the frame index advances.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/arl2.h"
+#include "arl2_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+arl2_status fail(arl2_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+arl2_status fail(arl2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("ARL2_DEBUG_SYNC");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+}  // namespace
+
+struct arl2_layer {
+  arl2_config cfg;
+  int device = 0;
+  int d = 0, dp = 0, chunks = 0;
+  float scale_log2 = 0.f, eps = 0.f;
+  // one device slab, carved into the regions below
+  void* slab = nullptr;
+  size_t bytes = 0;
+  float* s[2] = {nullptr, nullptr};  // S, fp32 [B][H][d][d], ping-pong
+  int cur = 0;                       // index of S_{N-1} (the state every pass reads)
+  float* partial = nullptr;          // [B][H][chunks][dp][dp]
+  void* sneg_hi = nullptr;           // -S as B fragments, bf16 [B][H][d/16][dp/32][64][8]
+  void* sneg_lo = nullptr;
+  void* wt_hi = nullptr;             // (phi_q S)^T, bf16 [B][H][dp][d]
+  void* wt_lo = nullptr;
+  void* pq = nullptr;                // maps' working layouts, bf16 [H][dp][d]
+  void* pkt = nullptr;
+  void* pvt = nullptr;
+  int64_t frame = 0;
+  bool poisoned = false;
+  hipStream_t last_stream = nullptr;
+  bool have_last_stream = false;
+  hipEvent_t handoff = nullptr;
+};
+
+namespace {
+
+arl2_status hip_fail(arl2_layer* L, hipError_t e, const char* what) {
+  if (L) L->poisoned = true;
+  return fail(ARL2_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Make `stream` the layer's stream, ordering it after the previous one when it differs.
+arl2_status use_stream(arl2_layer* L, hipStream_t stream) {
+  if (L->have_last_stream && L->last_stream != stream) {
+    hipError_t e = hipEventRecord(L->handoff, L->last_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, L->handoff, 0);
+    if (e != hipSuccess) return hip_fail(L, e, "stream handoff");
+  }
+  L->last_stream = stream;
+  L->have_last_stream = true;
+  return ARL2_OK;
+}
+
+arl2_status after_launch(arl2_layer* L, hipError_t e, hipStream_t stream, const char* what) {
+  if (e != hipSuccess) return hip_fail(L, e, what);
+  if (debug_sync()) {
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(L, e, what);
+  }
+  return ARL2_OK;
+}
+
+arl2_status check_layer(arl2_layer* L) {
+  if (!L) return fail(ARL2_E_INVALID_ARG, "layer is NULL");
+  if (L->poisoned) return fail(ARL2_E_PROTOCOL, "layer is poisoned by an earlier failure; restore a state first");
+  return ARL2_OK;
+}
+
+arl2_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(ARL2_E_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(ARL2_E_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return ARL2_OK;
+}
+
+arl2_status launch_pass(arl2_layer* L, const void* q, const void* k, const void* v, void* out,
+                        hipStream_t stream) {
+  arl2::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.wt_hi = L->wt_hi;
+  a.wt_lo = L->wt_lo;
+  a.out = out;
+  a.B = L->cfg.batch;
+  a.H = L->cfg.heads;
+  a.T = L->cfg.tokens_per_frame;
+  a.scale_log2 = L->scale_log2;
+  a.out_bf16 = L->cfg.out_dtype == ARL2_BF16;
+  return after_launch(L, arl2::launch_fwd(L->d, a, stream), stream, "pass kernel launch");
+}
+
+// Derive S_N = alpha S_prev + partials (chunks may be 0) into s[dst], plus its derived forms.
+arl2_status launch_reduce(arl2_layer* L, const float* s_prev, const float* alpha, int chunks, int dst,
+                          hipStream_t stream) {
+  arl2::CommitReduceArgs r;
+  r.s_prev = s_prev;
+  r.alpha = alpha;
+  r.partial = L->partial;
+  r.chunks = chunks;
+  r.pq = L->pq;
+  r.s_new = L->s[dst];
+  r.sneg_hi = L->sneg_hi;
+  r.sneg_lo = L->sneg_lo;
+  r.wt_hi = L->wt_hi;
+  r.wt_lo = L->wt_lo;
+  r.B = L->cfg.batch;
+  r.H = L->cfg.heads;
+  return after_launch(L, arl2::launch_commit_reduce(L->d, r, stream), stream, "state reduce kernel launch");
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* arl2_status_string(arl2_status st) {
+  switch (st) {
+    case ARL2_OK: return "ok";
+    case ARL2_E_INVALID_ARG: return "invalid argument";
+    case ARL2_E_UNSUPPORTED: return "unsupported configuration or device";
+    case ARL2_E_NO_DEVICE: return "no HIP device";
+    case ARL2_E_OUT_OF_MEMORY: return "out of device memory";
+    case ARL2_E_HIP: return "HIP runtime error";
+    case ARL2_E_PROTOCOL: return "protocol error (layer poisoned)";
+  }
+  return "unknown status";
+}
+
+const char* arl2_last_error(void) { return g_last_error.c_str(); }
+
+arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const void* phi_k, const void* phi_v,
+                              void* stream_, arl2_layer** out_layer) {
+  if (!out_layer) return fail(ARL2_E_INVALID_ARG, "out_layer is NULL");
+  *out_layer = nullptr;
+  if (!cfg) return fail(ARL2_E_INVALID_ARG, "config is NULL");
+  const arl2_config c = *cfg;
+  if (c.batch < 1 || c.heads < 1 || c.batch > 65535 || c.heads > 65535)
+    return fail(ARL2_E_INVALID_ARG, "batch and heads must be in [1, 65535]");
+  if (c.tokens_per_frame < 1 || c.tokens_per_frame > ARL2_MAX_TOKENS)
+    return fail(ARL2_E_INVALID_ARG, "tokens_per_frame must be in [1, %d]", ARL2_MAX_TOKENS);
+  if (c.head_dim != 16 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(ARL2_E_UNSUPPORTED, "head_dim %d not supported (16, 64, 128)", c.head_dim);
+  if (c.io_dtype != ARL2_BF16) return fail(ARL2_E_UNSUPPORTED, "io_dtype must be ARL2_BF16");
+  if (c.out_dtype != ARL2_F32 && c.out_dtype != ARL2_BF16) return fail(ARL2_E_INVALID_ARG, "bad out_dtype");
+  if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
+    return fail(ARL2_E_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!(c.knorm_eps >= 0.f) || !std::isfinite(c.knorm_eps))
+    return fail(ARL2_E_INVALID_ARG, "knorm_eps must be finite and >= 0");
+  const int64_t elems = (int64_t)c.batch * c.tokens_per_frame * c.heads * c.head_dim;
+  if (elems > (int64_t(1) << 40)) return fail(ARL2_E_INVALID_ARG, "frame tensor too large");
+  arl2_status st;
+  if ((st = check_ptr(phi_q, "phi_q")) || (st = check_ptr(phi_k, "phi_k")) || (st = check_ptr(phi_v, "phi_v")))
+    return st;
+
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(ARL2_E_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+  }
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return fail(ARL2_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
+    return fail(ARL2_E_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(ARL2_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+
+  arl2_layer* L = new arl2_layer();
+  L->cfg = c;
+  L->device = dev;
+  L->d = c.head_dim;
+  L->dp = arl2::padded_dim(c.head_dim);
+  L->chunks = arl2::commit_chunks(c.tokens_per_frame);
+  const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.f / std::sqrt((float)c.head_dim);
+  L->scale_log2 = scale * 1.4426950408889634f;
+  L->eps = c.knorm_eps > 0.f ? c.knorm_eps : 1e-6f;
+
+  const size_t BH = (size_t)c.batch * c.heads, d = L->d, dp = L->dp;
+  const size_t s_bytes = align_up(BH * d * d * sizeof(float));
+  const size_t part_bytes = align_up(BH * L->chunks * dp * dp * sizeof(float));
+  const size_t frag_bytes = align_up(BH * d * dp * 2);   // [B][H][d/16][dp/32][64][8] bf16
+  const size_t wt_bytes = align_up(BH * dp * d * 2);
+  const size_t map_bytes = align_up((size_t)c.heads * dp * d * 2);
+  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + 3 * map_bytes;
+  if ((e = hipMalloc(&L->slab, L->bytes)) != hipSuccess) {
+    (void)hipGetLastError();
+    const size_t want = L->bytes;
+    delete L;
+    return fail(ARL2_E_OUT_OF_MEMORY, "hipMalloc(%zu bytes): %s", want, hipGetErrorString(e));
+  }
+  char* p = static_cast<char*>(L->slab);
+  L->s[0] = reinterpret_cast<float*>(p); p += s_bytes;
+  L->s[1] = reinterpret_cast<float*>(p); p += s_bytes;
+  L->partial = reinterpret_cast<float*>(p); p += part_bytes;
+  L->sneg_hi = p; p += frag_bytes;
+  L->sneg_lo = p; p += frag_bytes;
+  L->wt_hi = p; p += wt_bytes;
+  L->wt_lo = p; p += wt_bytes;
+  L->pq = p; p += map_bytes;
+  L->pkt = p; p += map_bytes;
+  L->pvt = p; p += map_bytes;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  auto bail = [&](hipError_t err, const char* what) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(L->slab);
+    if (L->handoff) (void)hipEventDestroy(L->handoff);
+    delete L;
+    return fail(ARL2_E_HIP, "%s: %s", what, hipGetErrorString(err));
+  };
+  if ((e = hipEventCreateWithFlags(&L->handoff, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
+  // S_0 = 0 and everything derived from it is 0 as well.
+  if ((e = hipMemsetAsync(L->slab, 0, L->bytes - 3 * map_bytes, stream)) != hipSuccess) return bail(e, "hipMemsetAsync");
+  arl2::PrepMapsArgs pm{phi_q, phi_k, phi_v, L->pq, L->pkt, L->pvt, c.heads};
+  if ((e = arl2::launch_prep_maps(L->d, pm, stream)) != hipSuccess) return bail(e, "map preparation launch");
+  if (debug_sync() && (e = hipStreamSynchronize(stream)) != hipSuccess) return bail(e, "map preparation");
+  L->last_stream = stream;
+  L->have_last_stream = true;
+  *out_layer = L;
+  return ARL2_OK;
+}
+
+arl2_status arl2_denoise_step(arl2_layer* L, const void* q, const void* k, const void* v, void* out, void* stream_) {
+  arl2_status st;
+  if ((st = check_layer(L))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
+    return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if ((st = use_stream(L, stream))) return st;
+  return launch_pass(L, q, k, v, out, stream);
+}
+
+arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
+                              const float* alpha, void* out, void* stream_) {
+  arl2_status st;
+  if ((st = check_layer(L))) return st;
+  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(beta, "beta")) ||
+      (st = check_ptr(alpha, "alpha")))
+    return st;
+  if (out && (st = check_ptr(q, "q"))) return st;
+  if (out && !aligned16(out)) return fail(ARL2_E_INVALID_ARG, "out is not 16-byte aligned");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if ((st = use_stream(L, stream))) return st;
+  if (out && (st = launch_pass(L, q, k, v, out, stream))) return st;
+
+  arl2::CommitPartialArgs pa;
+  pa.k = k;
+  pa.v = v;
+  pa.beta = beta;
+  pa.pkt = L->pkt;
+  pa.pvt = L->pvt;
+  pa.sneg_hi = L->sneg_hi;
+  pa.sneg_lo = L->sneg_lo;
+  pa.partial = L->partial;
+  pa.B = L->cfg.batch;
+  pa.H = L->cfg.heads;
+  pa.T = L->cfg.tokens_per_frame;
+  pa.knorm_eps = L->eps;
+  if ((st = after_launch(L, arl2::launch_commit_partial(L->d, pa, stream), stream, "state write kernel launch")))
+    return st;
+  if ((st = launch_reduce(L, L->s[L->cur], alpha, L->chunks, L->cur ^ 1, stream))) return st;
+  L->cur ^= 1;
+  L->frame += 1;
+  return ARL2_OK;
+}
+
+arl2_status arl2_destroy(arl2_layer* L) {
+  if (!L) return ARL2_OK;
+  hipError_t e = hipSuccess;
+  if (L->have_last_stream) e = hipStreamSynchronize(L->last_stream);
+  hipError_t e2 = L->slab ? hipFree(L->slab) : hipSuccess;
+  if (L->handoff) (void)hipEventDestroy(L->handoff);
+  delete L;
+  if (e != hipSuccess) return fail(ARL2_E_HIP, "destroy: synchronise: %s", hipGetErrorString(e));
+  if (e2 != hipSuccess) return fail(ARL2_E_HIP, "destroy: hipFree: %s", hipGetErrorString(e2));
+  return ARL2_OK;
+}
+
+arl2_status arl2_state_read(arl2_layer* L, float* dst, void* stream_) {
+  arl2_status st;
+  if ((st = check_layer(L))) return st;
+  if ((st = check_ptr(dst, "dst"))) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if ((st = use_stream(L, stream))) return st;
+  const size_t n = (size_t)L->cfg.batch * L->cfg.heads * L->d * L->d * sizeof(float);
+  hipError_t e = hipMemcpyAsync(dst, L->s[L->cur], n, hipMemcpyDeviceToDevice, stream);
+  return after_launch(L, e, stream, "state read copy");
+}
+
+arl2_status arl2_state_write(arl2_layer* L, const float* src, int64_t frame_index, void* stream_) {
+  if (!L) return fail(ARL2_E_INVALID_ARG, "layer is NULL");
+  arl2_status st;
+  if ((st = check_ptr(src, "src"))) return st;
+  if (frame_index < 0) return fail(ARL2_E_INVALID_ARG, "frame_index must be >= 0");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  L->poisoned = false;
+  if ((st = use_stream(L, stream))) return st;
+  // S = 1 * src with no partials, stored into the buffer the next pass reads.
+  if ((st = launch_reduce(L, src, nullptr, 0, L->cur, stream))) {
+    L->poisoned = true;
+    return st;
+  }
+  L->frame = frame_index;
+  return ARL2_OK;
+}
+
+int64_t arl2_frame_index(const arl2_layer* L) { return L ? L->frame : -1; }
+
+size_t arl2_device_bytes(const arl2_layer* L) { return L ? L->bytes : 0; }
+
+}  // extern "C"

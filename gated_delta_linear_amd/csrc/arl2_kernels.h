@@ -1,0 +1,78 @@
+// Host-side launchers of the ARL2 kernels.  All pointers are device pointers; shapes are
+// validated by the caller (arl2_host.cpp) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace arl2 {
+
+// Feature dimension padded to a whole 32-row MFMA block.
+inline int padded_dim(int d) { return d < 32 ? 32 : d; }
+// Tokens per work-group of the state-write kernel, and the number of such chunks.
+constexpr int kCommitChunk = 128;
+inline int commit_chunks(int T) { return (T + kCommitChunk - 1) / kCommitChunk; }
+
+// Per-pass output: out = softmax(Q K^T * scale) V + Q (phi_q S).  wt_hi / wt_lo hold
+// (phi_q S)^T split into two bf16 terms, layout [B][H][dp][d].
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* wt_hi;
+  const void* wt_lo;
+  void* out;
+  int B, H, T;
+  float scale_log2;  // softmax scale * log2(e)
+  bool out_bf16;
+};
+hipError_t launch_fwd(int d, const FwdArgs& a, hipStream_t stream);
+
+// Per-chunk partial sums of the state write, P_c = K'_c^T diag(beta_c) (V'_c - K'_c S),
+// written to partial [B][H][chunks][dp][dp].
+struct CommitPartialArgs {
+  const void* k;
+  const void* v;
+  const float* beta;
+  const void* pkt;      // phi_k^T, [H][dp][d]
+  const void* pvt;      // phi_v^T, [H][dp][d]
+  const void* sneg_hi;  // -S_{N-1} as MFMA B fragments, [B][H][d/16][dp/32][64][8]
+  const void* sneg_lo;
+  float* partial;
+  int B, H, T;
+  float knorm_eps;
+};
+hipError_t launch_commit_partial(int d, const CommitPartialArgs& a, hipStream_t stream);
+
+// S_new = alpha S_prev + sum over chunks of the partials (fixed order), then the derived
+// forms of S_new: -S_new as B fragments (hi/lo) and (phi_q S_new)^T (hi/lo).
+// alpha == nullptr means alpha = 1; chunks == 0 means no partials (used to load a state).
+struct CommitReduceArgs {
+  const float* s_prev;  // [B][H][d][d]
+  const float* alpha;   // [B][H] or nullptr
+  const float* partial; // [B][H][chunks][dp][dp]
+  int chunks;
+  const void* pq;       // phi_q, [H][dp][d] (rows >= d zero)
+  float* s_new;         // [B][H][d][d]
+  void* sneg_hi;
+  void* sneg_lo;
+  void* wt_hi;
+  void* wt_lo;
+  int B, H;
+};
+hipError_t launch_commit_reduce(int d, const CommitReduceArgs& a, hipStream_t stream);
+
+// Working layouts of the maps from the caller's phi_q, phi_k, phi_v (bf16 [H][d][d]):
+// pq = phi_q padded to [H][dp][d]; pkt = phi_k^T and pvt = phi_v^T padded to [H][dp][d].
+struct PrepMapsArgs {
+  const void* phi_q;
+  const void* phi_k;
+  const void* phi_v;
+  void* pq;
+  void* pkt;
+  void* pvt;
+  int H;
+};
+hipError_t launch_prep_maps(int d, const PrepMapsArgs& a, hipStream_t stream);
+
+}  // namespace arl2

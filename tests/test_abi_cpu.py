@@ -1,0 +1,107 @@
+"""The C interface on the CPU: the library loads, exports every function include/arl2.h
+declares, and rejects bad arguments before touching a device.  No kernel runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gated_delta_linear_amd.arl2 as A
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.LIB_PATH):
+        from gated_delta_linear_amd.build import build_library
+        build_library()
+    return A.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(arl2_[a-z_]+)\s*\(", text))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == set(A.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in range(7):
+        assert lib.arl2_status_string(st)
+    assert lib.arl2_status_string(99) == b"unknown status"
+
+
+def test_null_layer_queries(lib):
+    assert lib.arl2_frame_index(None) == -1
+    assert lib.arl2_device_bytes(None) == 0
+    assert lib.arl2_destroy(None) == A.ARL2_OK
+    assert lib.arl2_denoise_step(None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_commit_frame(None, None, None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_state_read(None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_state_write(None, None, 0, None) == A.ARL2_E_INVALID_ARG
+    assert b"NULL" in lib.arl2_last_error()
+
+
+def _cfg(**kw):
+    c = dict(batch=1, heads=2, head_dim=128, tokens_per_frame=64, io_dtype=A.ARL2_BF16, out_dtype=A.ARL2_F32,
+             softmax_scale=0.0, knorm_eps=0.0)
+    c.update(kw)
+    return A.Arl2Config(**c)
+
+
+# Aligned but never dereferenced: every case below is rejected by argument checks that run
+# before the device is queried.
+FAKE = 0x10000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), A.ARL2_E_INVALID_ARG),
+    (dict(heads=0), A.ARL2_E_INVALID_ARG),
+    (dict(tokens_per_frame=0), A.ARL2_E_INVALID_ARG),
+    (dict(tokens_per_frame=A.ARL2_MAX_TOKENS + 1), A.ARL2_E_INVALID_ARG),
+    (dict(head_dim=32), A.ARL2_E_UNSUPPORTED),
+    (dict(head_dim=96), A.ARL2_E_UNSUPPORTED),
+    (dict(io_dtype=A.ARL2_F32), A.ARL2_E_UNSUPPORTED),
+    (dict(out_dtype=7), A.ARL2_E_INVALID_ARG),
+    (dict(softmax_scale=-1.0), A.ARL2_E_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), A.ARL2_E_INVALID_ARG),
+    (dict(knorm_eps=float("inf")), A.ARL2_E_INVALID_ARG),
+])
+def test_create_rejects_bad_config(lib, kw, status):
+    h = ctypes.c_void_p(123)
+    assert lib.arl2_layer_create(ctypes.byref(_cfg(**kw)), FAKE, FAKE, FAKE, None, ctypes.byref(h)) == status
+    assert not h.value  # set to NULL on failure
+    assert lib.arl2_last_error()
+
+
+def test_create_rejects_bad_pointers(lib):
+    h = ctypes.c_void_p()
+    assert lib.arl2_layer_create(None, FAKE, FAKE, FAKE, None, ctypes.byref(h)) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_layer_create(ctypes.byref(_cfg()), None, FAKE, FAKE, None, ctypes.byref(h)) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_layer_create(ctypes.byref(_cfg()), FAKE, FAKE + 8, FAKE, None, ctypes.byref(h)) == \
+        A.ARL2_E_INVALID_ARG
+    assert b"aligned" in lib.arl2_last_error()
+    assert lib.arl2_layer_create(ctypes.byref(_cfg()), FAKE, FAKE, FAKE, None, None) == A.ARL2_E_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path; a GPU is present")
+def test_create_without_device_fails_cleanly(lib):
+    h = ctypes.c_void_p()
+    assert lib.arl2_layer_create(ctypes.byref(_cfg()), FAKE, FAKE, FAKE, None, ctypes.byref(h)) == A.ARL2_E_NO_DEVICE
+    assert not h.value
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        A.load_library(str(tmp_path / "libarl2.so"))
