@@ -1,0 +1,399 @@
+"""Throughput of one ARL2 layer on one MI355X: frame-tokens/s at the 1.3B DiT 480p layer shape.
+
+A step is one latent frame of the protocol: 4 denoising passes (query only) + 1 clean pass
+(output with S_{N-1}, then the state write), for 1 stream x 12 heads x 1560 tokens x d=128.
+Inputs are synthetic (seeded, the shapes and distributions of the workload), pre-staged in
+HBM as a ring of 8 unique frames that the timed steps cycle through, so no host work or
+PCIe transfer is inside the timed region and the state keeps evolving.
+
+Prints one JSON line.  Also reports, for the dominant kernel (the fused per-pass kernel),
+its average duration measured with HIP events around each pass launch on the layer's
+stream, against the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--workload dit480p|chunked|long_stream]
+  python bench.py --series            per-frame GPU time over the whole stream
+  python bench.py --pmc-target        a short run for rocprofv3 counter passes (kernels + a copy)
+  python bench.py --summarize-pmc DIR rocprofv3 counter CSVs -> profiles/ traffic summary
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "frame-tokens/sec per ARL2 layer at 1560 tok/frame, H=12, d=128; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FWD_KERNEL = "arl2_fwd_kernel"
+KERNEL_SOURCES = ["gated_delta_linear_amd/csrc/arl2_fwd.hip", "gated_delta_linear_amd/csrc/arl2_device.h",
+                  "gated_delta_linear_amd/csrc/arl2_kernels.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "arl2_fwd_dit480p_traffic.json")
+RING = 8
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pass_flops(w) -> float:
+    """Algorithmic FLOPs of one pass: per (stream, head) 4 T^2 d (scores and P V) + 2 T d^2
+    (the inter-frame read as Q (phi_q S))."""
+    T, d = w.tokens, w.head_dim
+    return float(w.batch * w.heads * (4 * T * T * d + 2 * T * d * d))
+
+
+def commit_flops(w) -> float:
+    """The state write: per (stream, head) K phi_k, V phi_v, K' S, K'^T (beta R) = 8 T d^2, plus
+    2 d^3 for phi_q S."""
+    T, d = w.tokens, w.head_dim
+    return float(w.batch * w.heads * (8 * T * d * d + 2 * d ** 3))
+
+
+def frame_flops(w) -> float:
+    return (w.denoise_steps + 1) * pass_flops(w) + commit_flops(w)
+
+
+def stage_ring(w, torch):
+    """Device-resident inputs for RING frames: per frame, each pass's q, k, v and the gates."""
+    from synth import make_gates, make_pass_inputs
+
+    dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dt)
+    ring = []
+    for f in range(RING):
+        passes = [tuple(dev(x, torch.bfloat16) for x in make_pass_inputs(w, f, p)) for p in range(w.denoise_steps + 1)]
+        beta, alpha = make_gates(w, f)
+        ring.append((passes, dev(beta, torch.float32), dev(alpha, torch.float32)))
+    torch.cuda.synchronize()
+    return ring
+
+
+def make_layer(w, torch):
+    from gated_delta_linear_amd import Arl2Layer
+    from synth import make_phi
+
+    phis = [torch.from_numpy(p).to("cuda").to(torch.bfloat16) for p in make_phi(w)]
+    return Arl2Layer(*phis, batch=w.batch, tokens=w.tokens)
+
+
+def run_frames(layer, ring, w, n, out, stream, first=0):
+    """Enqueue n frames of the protocol, frame i using ring slot (first + i) % RING: the
+    denoising passes, then the clean pass (output with S_{N-1}, then the state write)."""
+    for i in range(n):
+        passes, beta, alpha = ring[(first + i) % RING]
+        for p, (q, k, v) in enumerate(passes):
+            if p < w.denoise_steps:
+                layer.denoise_step(q, k, v, out=out, stream=stream)
+            else:
+                layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
+
+
+def capture_frames(layer, ring, w, out, stream, torch):
+    """One HIP graph per ring slot, each holding one whole frame (5 pass launches + the
+    state write), captured on `stream` (the stream the layer already uses, so no cross-
+    stream ordering is recorded).  Replaying graph i % RING for frame i continues the same
+    stream of frames: the state buffers alternate with every frame, and RING is even."""
+    graphs = []
+    for i in range(RING):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            run_frames(layer, ring, w, 1, out, stream, first=i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_region(stream, torch, enqueue):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    enqueue()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), time.perf_counter() - wall0
+
+
+def pass_launch_us(layer, ring, w, out, stream, torch, n=40):
+    """Average duration of the pass kernel: HIP events around each denoising-pass launch."""
+    evs = []
+    for i in range(n):
+        q, k, v = ring[i % RING][0][i % w.denoise_steps]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        layer.denoise_step(q, k, v, out=out, stream=stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
+def write_launch_us(layer, ring, w, stream, torch, n=16):
+    """Average duration of the state write (its two kernels): events around commit_frame
+    without an output."""
+    evs = []
+    for i in range(n):
+        passes, beta, alpha = ring[i % RING]
+        q, k, v = passes[-1]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        layer.commit_frame(q, k, v, beta, alpha, want_output=False, stream=stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
+def load_traffic():
+    """HBM bytes per launch of the pass kernel from committed counter passes, if they were
+    taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (numpy fp64) on the first frames of the same stream, in full: every pass's
+    output and the state write, until the time budget is spent (at least one frame)."""
+    from oracle import Arl2Oracle
+    from synth import make_gates, make_pass_inputs, make_phi
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    orc = Arl2Oracle(*[p.astype(np.float64) for p in make_phi(w)], batch=w.batch)
+    frames, busy = 0, 0.0
+    while frames < w.frames and (frames == 0 or busy < budget_s):
+        inputs = [make_pass_inputs(w, frames, p) for p in range(w.denoise_steps + 1)]
+        beta, alpha = make_gates(w, frames)
+        t0 = time.perf_counter()
+        for p, (q, k, v) in enumerate(inputs):
+            if p < w.denoise_steps:
+                orc.denoise_step(q, k, v)
+            else:
+                orc.commit(q, k, v, beta, alpha)
+        busy += time.perf_counter() - t0
+        frames += 1
+    return {"value": w.batch * w.tokens * frames / busy, "unit": "frame-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{w.name} frames 0..{frames - 1} in full ({w.denoise_steps} denoising passes + clean pass "
+                      f"+ state write each), numpy fp64, {busy:.1f} s of CPU work, input generation excluded"}
+
+
+def bench(args):
+    import torch
+
+    from synth import WORKLOADS
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU (MI355X)")
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(stream):
+        layer = make_layer(w, torch)
+        ring = stage_ring(w, torch)
+        out = layer.new_output()
+        run_frames(layer, ring, w, args.warmup, out, stream)
+        torch.cuda.synchronize()
+
+        # eager: every launch enqueued from Python, timed over exactly `steps` frames
+        eager_ms, eager_wall = time_region(stream, torch, lambda: run_frames(layer, ring, w, args.steps, out, stream))
+
+        # graphs: the same frames replayed from captured HIP graphs (no host work per launch)
+        graphs = capture_frames(layer, ring, w, out, stream, torch)
+        for i in range(RING):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        graph_ms, graph_wall = time_region(stream, torch, lambda: [graphs[i % RING].replay() for i in range(args.steps)])
+
+        # kernel timing: events around each launch, outside the two timed regions above
+        pass_us = pass_launch_us(layer, ring, w, out, stream, torch)
+        write_us = write_launch_us(layer, ring, w, stream, torch)
+        torch.cuda.synchronize()
+        device_bytes = layer.device_bytes
+        layer.close()
+
+    use_graph = not args.eager
+    elapsed_ms = graph_ms if use_graph else eager_ms
+    ms_per_step = elapsed_ms / args.steps
+    value = w.batch * w.tokens * args.steps / (elapsed_ms / 1e3)
+    achieved = pass_flops(w) / (pass_us * 1e-6) / 1e12
+    traffic = load_traffic()
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "frame-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.batch} stream(s) x {w.heads} heads x {w.tokens} tokens/frame, d={w.head_dim}, "
+                        f"{w.denoise_steps} denoising passes + 1 clean pass with state write per frame",
+            "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "tokens_per_frame": w.tokens,
+            "denoise_steps": w.denoise_steps, "beta": f"sigmoid(N(0,1)) * {w.beta_scale:.6g}",
+            "input_ring_frames": RING, "launch": "hip_graph_per_frame" if use_graph else "eager",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": FWD_KERNEL, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic["bytes_per_launch"] if traffic else None,
+            "flops_per_launch": pass_flops(w), "avg_launch_us": pass_us,
+        },
+        "breakdown": {
+            "pass_us": pass_us, "state_write_us": write_us,
+            "frame_us_graph": graph_ms / args.steps * 1e3, "frame_us_eager": eager_ms / args.steps * 1e3,
+            "host_wall_s_graph": graph_wall, "host_wall_s_eager": eager_wall,
+            "frame_mfma_frac": frame_flops(w) / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "device_bytes": device_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def series(args):
+    """Per-frame GPU time and device memory over a whole stream (constant-cost check)."""
+    import torch
+
+    from synth import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    layer = make_layer(w, torch)
+    ring = stage_ring(w, torch)
+    out = layer.new_output()
+    stream = torch.cuda.current_stream()
+    times, mem = [], []
+    for f in range(w.frames):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run_frames(layer, ring, w, 1, out, stream, first=f)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+        mem.append(torch.cuda.mem_get_info()[0])
+        if f % 50 == 0:
+            print(f"frame {f}: {times[-1]:.1f} us", flush=True)
+    t = np.array(times[2:])
+    x = np.arange(len(t))
+    slope = float(np.polyfit(x, t, 1)[0]) if len(t) > 2 else 0.0
+    print(json.dumps({"workload": w.name, "frames": w.frames, "median_us": float(np.median(t)),
+                      "p10_us": float(np.percentile(t, 10)), "p90_us": float(np.percentile(t, 90)),
+                      "slope_us_per_100_frames": slope * 100, "free_mem_bytes_min": int(min(mem)),
+                      "free_mem_bytes_max": int(max(mem)), "device_bytes": layer.device_bytes}), flush=True)
+    layer.close()
+
+
+def pmc_target(args):
+    """A short, fixed run for counter passes: a plain copy of known size (the calibration of
+    FETCH_SIZE / WRITE_SIZE), then a few frames of the layer."""
+    import torch
+
+    from synth import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    n = 256 * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    layer = make_layer(w, torch)
+    ring = stage_ring(w, torch)
+    out = layer.new_output()
+    run_frames(layer, ring, w, 2, out, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    layer.close()
+    print(json.dumps({"copy_bytes_each_way": n * 4, "frames": 2, "kernel_source_hash": kernel_source_hash()}))
+
+
+def summarize_pmc(args):
+    """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into HBM bytes
+    per launch of the pass kernel, each scaled by the counter's reading for the plain copy
+    (256 MiB read + 256 MiB written).  Writes the JSON bench.py reads and a text summary."""
+    import csv
+
+    def per_kernel(counter):
+        rows = []
+        for path in glob.glob(os.path.join(args.summarize_pmc, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = per_kernel(counter)
+        copy = [v for k, v in rows if "elementwise" in k.lower() or "copy" in k.lower()]
+        fwd = [v for k, v in rows if FWD_KERNEL in k]
+        if not copy or not fwd:
+            sys.exit(f"{counter}: copy kernel or {FWD_KERNEL} not found in {args.summarize_pmc}")
+        expect_kib = 256 * 1024.0
+        factor = float(np.median(copy)) / expect_kib
+        res[counter] = {"copy_kib_median": float(np.median(copy)), "scale": factor,
+                        "fwd_kib_mean": float(np.mean(fwd)), "fwd_bytes": float(np.mean(fwd)) / factor * 1024,
+                        "fwd_dispatches": len(fwd)}
+    total = res["FETCH_SIZE"]["fwd_bytes"] + res["WRITE_SIZE"]["fwd_bytes"]
+    out = {"kernel": FWD_KERNEL, "workload": args.workload, "kernel_source_hash": kernel_source_hash(),
+           "bytes_per_launch": total, "counters": res}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit480p", choices=["dit480p", "long_stream", "chunked"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="report the eager (per-launch) rate as the value")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work (min one frame)")
+    ap.add_argument("--series", action="store_true")
+    ap.add_argument("--pmc-target", action="store_true")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        sys.exit("bench.py measures one GPU: this layer runs without sharding or collectives on a "
+                 "single MI355X; --gpus must be 1")
+    if args.summarize_pmc:
+        summarize_pmc(args)
+    elif args.pmc_target:
+        pmc_target(args)
+    elif args.series:
+        series(args)
+    else:
+        bench(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -181,9 +181,10 @@ class Arl2Layer:
         return out
 
     # --- checkpoint hooks ---------------------------------------------------------------
-    def state(self, stream=None) -> torch.Tensor:
-        dst = torch.empty(self.state_shape, dtype=torch.float32, device=self.device)
-        _check(self._lib.arl2_state_read(self._ptr(), dst.data_ptr(), _stream_handle(stream)), "arl2_state_read")
+    def state(self, out=None, stream=None) -> torch.Tensor:
+        dst = torch.empty(self.state_shape, dtype=torch.float32, device=self.device) if out is None else out
+        p = _dev_tensor(dst, "out", torch.float32, self.state_shape)
+        _check(self._lib.arl2_state_read(self._ptr(), p, _stream_handle(stream)), "arl2_state_read")
         return dst
 
     def load_state(self, src: torch.Tensor, frame_index: int, stream=None) -> None:

@@ -203,17 +203,29 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_reduce_kernel(
   const int64_t bh = (int64_t)b * H + h;
   const float a = alpha ? alpha[bh] : 1.f;
 
-  // S_new = alpha S_prev + sum_c P_c, fixed order over chunks.
-  for (int e = tid; e < DP * 32; e += kThreads) {
-    const int row = e >> 5, col = 32 * nb + (e & 31);
-    float acc = 0.f;
+  // S_new = alpha S_prev + sum_c P_c, fixed order over chunks.  Each thread owns 4 adjacent
+  // columns of a row (float4) and keeps 8 chunk loads in flight.
+  for (int e = tid; e < DP * 8; e += kThreads) {
+    const int row = e >> 3, c4 = (e & 7) * 4, col = 32 * nb + c4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (row < D && col < D) {
-      acc = a * s_prev[(bh * D + row) * D + col];
-      const float* pp = partial + bh * chunks * DP * DP + row * DP + col;
-      for (int c = 0; c < chunks; ++c) acc += pp[(int64_t)c * DP * DP];
-      s_new[(bh * D + row) * D + col] = acc;
+      const f32x4 sp = *reinterpret_cast<const f32x4*>(s_prev + (bh * D + row) * D + col);
+      acc = a * sp;
+      const f32x4* pp = reinterpret_cast<const f32x4*>(partial + bh * chunks * DP * DP + row * DP + col);
+      constexpr int kStride = DP * DP / 4;  // float4 between consecutive chunks
+      int c = 0;
+      for (; c + 8 <= chunks; c += 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = pp[(int64_t)(c + u) * kStride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += x[u];
+      }
+      for (; c < chunks; ++c) acc += pp[(int64_t)c * kStride];
+      *reinterpret_cast<f32x4*>(s_new + (bh * D + row) * D + col) = acc;
     }
-    tile[row][e & 31] = acc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tile[row][c4 + u] = acc[u];
   }
   __syncthreads();
 

@@ -184,8 +184,10 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
     return fail(ARL2_E_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (!(c.knorm_eps >= 0.f) || !std::isfinite(c.knorm_eps))
     return fail(ARL2_E_INVALID_ARG, "knorm_eps must be finite and >= 0");
-  const int64_t elems = (int64_t)c.batch * c.tokens_per_frame * c.heads * c.head_dim;
-  if (elems > (int64_t(1) << 40)) return fail(ARL2_E_INVALID_ARG, "frame tensor too large");
+  // the kernels address one stream's frame slice [T][H][d] with 32-bit byte offsets
+  const int64_t slice_bytes = ((int64_t)c.tokens_per_frame + 256) * c.heads * c.head_dim * 2;
+  if (slice_bytes >= (int64_t(1) << 31))
+    return fail(ARL2_E_UNSUPPORTED, "one stream's frame (T x H x d bf16) must stay below 2 GiB");
   arl2_status st;
   if ((st = check_ptr(phi_q, "phi_q")) || (st = check_ptr(phi_k, "phi_k")) || (st = check_ptr(phi_v, "phi_v")))
     return st;

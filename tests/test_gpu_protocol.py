@@ -157,8 +157,12 @@ def test_token_permutation():
                              dev(beta[:, perm], torch.float32), dev(alpha, torch.float32))
     s1, s2 = layer.state().double().cpu().numpy(), layer2.state().double().cpu().numpy()
     o1, o2 = o1.double().cpu().numpy(), o2.double().cpu().numpy()
-    assert out_err(o2, o1[:, perm]) <= 1e-4
-    assert state_err(s2, s1) <= 1e-5
+    # Reordering changes which keys share a 64-key tile, hence the running max that bf16 P is
+    # rounded against: differences at the 1e-4 level are rounding; a token-sequential write
+    # would differ at order 1.
+    e_out, e_state = out_err(o2, o1[:, perm]), state_err(s2, s1)
+    assert e_out <= 2e-3, e_out
+    assert e_state <= 1e-4, e_state
 
 
 def test_device_memory_is_constant():
@@ -190,3 +194,42 @@ def test_bad_arguments_leave_layer_usable():
     layer.close()
     with pytest.raises(Arl2Error):
         layer.denoise_step(q, k, v)
+
+
+def test_graph_replays_match_eager():
+    """Frames captured in HIP graphs (one per input slot, including the state read) and
+    replayed repeatedly, with eager work and synchronisation between replays, give bitwise
+    the eager results of the same frames."""
+    frames = 6
+    ref_out, ref_st = _run(_layer(W), W, frames)
+    per = W.denoise_steps + 1
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        layer = _layer(W)
+        slots = [[(_frame_tensors(W, f, p), _gates(W, f)) for p in range(per)] for f in range(frames)]
+        out = layer.new_output()
+        st = torch.empty(layer.state_shape, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        graphs = []
+        for f in range(frames):  # one graph per frame: inputs differ per frame
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for p in range(per):
+                    (q, k, v), (beta, alpha) = slots[f][p]
+                    if p < W.denoise_steps:
+                        layer.denoise_step(q, k, v, out=out, stream=stream)
+                    else:
+                        layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
+                layer.state(out=st, stream=stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for rep in range(2):  # replay the whole stream twice from S_0
+            layer.load_state(torch.zeros_like(st), 0, stream=stream)
+            for f in range(frames):
+                graphs[f].replay()
+                torch.cuda.synchronize()
+                scratch = (out.float().sum() + st.sum()).item()  # eager work between replays
+                assert scratch == scratch
+                assert torch.equal(out, ref_out[(f + 1) * per - 1]), (rep, f)
+                assert torch.equal(st, ref_st[f]), (rep, f)
+        layer.close()
