@@ -33,15 +33,38 @@ struct CommitShape {
   static constexpr int NB = DP / 32;  // 32-blocks over value features (columns of S)
 };
 
-// LDS fragment store: [wave][block][k-step of 16 tokens][hi/lo][lane][8]
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS of the partial kernel.  Phase 1 reads the operands shared by all waves as MFMA
+// fragments (1 KB per fragment, 16 bytes per lane): phi_k^T and phi_v^T [block][k-step] and
+// -S hi/lo [k-step][block].  Phase 2 reuses the space for the fragments whose contraction runs
+// over tokens: [wave][block][k-step of 16 tokens][hi/lo][lane].
 template <int D>
 struct PartialSmem {
-  static constexpr int MB = CommitShape<D>::MB;
-  bf16x8 kfrag[4][MB][2][2][64];
-  bf16x8 rfrag[4][MB][2][2][64];
+  static constexpr int MB = CommitShape<D>::MB, KS = CommitShape<D>::KS;
+  union {
+    struct {
+      bf16x8 pk[MB][KS][64];
+      bf16x8 pv[MB][KS][64];
+      bf16x8 shi[KS][MB][64];
+      bf16x8 slo[KS][MB][64];
+    } op;
+    struct {
+      bf16x8 kfrag[4][MB][2][2][64];
+      bf16x8 rfrag[4][MB][2][2][64];
+    } fr;
+  };
   float beta[kCommitChunk];
   float inv_norm[kCommitChunk];
 };
+
+// 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
@@ -52,7 +75,8 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, NB = S::NB;
   __shared__ PartialSmem<D> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int chunks = gridDim.x;
   const int64_t rs = (int64_t)H * D;
@@ -67,28 +91,42 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
   // This lane's token for the A/B fragments of K and V (row-major, 8 features per lane).
   const int tok = t0 + 32 * wave + (lane & 31);
   const bool tok_ok = tok < T;
-  const bf16* pk = pkt + (int64_t)h * DP * D;
-  const bf16* pv = pvt + (int64_t)h * DP * D;
   const int64_t sb = ((int64_t)b * H + h) * (KS * NB * 64);  // fragment index base
 
-  bf16x8 kf[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st)
-    kf[st] = tok_ok ? ld_bf16x8(k + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+  // Shared operands into LDS: 4 * MB * KS fragments of 1 KB, spread over the 4 waves.
+  {
+    const __amdgpu_buffer_rsrc_t rk = rsrc(pkt + (int64_t)h * DP * D, DP * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(pvt + (int64_t)h * DP * D, DP * D * 2);
+    const __amdgpu_buffer_rsrc_t rh = rsrc(sneg_hi + sb * 8, KS * NB * 1024);
+    const __amdgpu_buffer_rsrc_t rl = rsrc(sneg_lo + sb * 8, KS * NB * 1024);
+    const int map_lane = ((lane & 31) * D + 8 * (lane >> 5)) * 2;  // row l % 32, features 8 (l / 32) ..
+    for (int f = wave; f < MB * KS; f += 4) {
+      const int mb = f / KS, st = f % KS;
+      dma16(rk, &sm.op.pk[mb][st][0], map_lane + (32 * mb * D + 16 * st) * 2);
+      dma16(rv, &sm.op.pv[mb][st][0], map_lane + (32 * mb * D + 16 * st) * 2);
+      dma16(rh, &sm.op.shi[0][0][0] + 64 * f, f * 1024 + lane * 16);
+      dma16(rl, &sm.op.slo[0][0][0] + 64 * f, f * 1024 + lane * 16);
+    }
+  }
 
-  // K'^T = phi_k^T K^T (rows = key features, lane column = token) and K' = K phi_k (rows =
-  // tokens, lane column = key feature): the same operands in swapped MFMA slots.
-  f32x16 kt[MB], kk[MB];
+  // All global loads of the wave are issued before the first wait: this lane's token row of
+  // K and of V (8 features per lane and k-step).
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    kf[st] = tok_ok ? ld_bf16x8(k + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+    vf[st] = tok_ok ? ld_bf16x8(v + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads into LDS are done
+  __syncthreads();
+
+  // K'^T = phi_k^T K^T: rows = key features, lane column = token.
+  f32x16 kt[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     kt[mb] = zero16();
-    kk[mb] = zero16();
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      bf16x8 pf = ld_bf16x8(pk + (32 * mb + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
-      kt[mb] = mfma32(pf, kf[st], kt[mb]);
-      kk[mb] = mfma32(kf[st], pf, kk[mb]);
-    }
+    for (int st = 0; st < KS; ++st) kt[mb] = mfma32(sm.op.pk[mb][st][lane], kf[st], kt[mb]);
   }
 
   // Unit rows: this lane holds half of its token's features; the other half is in lane ^ 32.
@@ -114,26 +152,34 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
   for (int st = 0; st < KS; ++st) {
     bf16x8 khi, klo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(kt[st >> 1][8 * (st & 1) + j]); khi[j] = sp_.hi; klo[j] = sp_.lo; }
+    for (int j = 0; j < 8; ++j) {
+      const Bf16Pair sp = split_bf16(kt[st >> 1][8 * (st & 1) + j]);
+      khi[j] = sp.hi;
+      klo[j] = sp.lo;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int64_t fo = (sb + (st * NB + nb) * 64 + lane) * 8;
-      bf16x8 shi = ld_bf16x8(sneg_hi + fo), slo = ld_bf16x8(sneg_lo + fo);
+      const bf16x8 shi = sm.op.shi[st][nb][lane], slo = sm.op.slo[st][nb][lane];
       r[nb] = mfma32(khi, shi, r[nb]);
       r[nb] = mfma32(khi, slo, r[nb]);
       r[nb] = mfma32(klo, shi, r[nb]);
     }
   }
 #pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    bf16x8 vf = tok_ok ? ld_bf16x8(v + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+  for (int st = 0; st < KS; ++st)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      bf16x8 pf = ld_bf16x8(pv + (32 * nb + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
-      r[nb] = mfma32(vf, pf, r[nb]);
-    }
+    for (int nb = 0; nb < NB; ++nb) r[nb] = mfma32(vf[st], sm.op.pv[nb][st][lane], r[nb]);
+
+  // K' = K phi_k (rows = tokens, lane column = key feature): the operands of K'^T in swapped
+  // MFMA slots; it is the A operand of the token contraction below.
+  f32x16 kk[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    kk[mb] = zero16();
+#pragma unroll
+    for (int st = 0; st < KS; ++st) kk[mb] = mfma32(kf[st], sm.op.pk[mb][st][lane], kk[mb]);
   }
-  __syncthreads();  // beta and inverse norms of all waves are in LDS
+  __syncthreads();  // beta and inverse norms of all waves are in LDS; the operands are no longer read
 
   // beta R and K' (rows = tokens) carry a token per register; scale and store both as
   // fragments whose contraction runs over the wave's 32 tokens.
@@ -152,13 +198,21 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
     for (int ts = 0; ts < 2; ++ts) {
       bf16x8 hi, lo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(kk[mb][8 * ts + j]); hi[j] = sp_.hi; lo[j] = sp_.lo; }
-      sm.kfrag[wave][mb][ts][0][lane] = hi;
-      sm.kfrag[wave][mb][ts][1][lane] = lo;
+      for (int j = 0; j < 8; ++j) {
+        const Bf16Pair sp = split_bf16(kk[mb][8 * ts + j]);
+        hi[j] = sp.hi;
+        lo[j] = sp.lo;
+      }
+      sm.fr.kfrag[wave][mb][ts][0][lane] = hi;
+      sm.fr.kfrag[wave][mb][ts][1][lane] = lo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(r[mb][8 * ts + j]); hi[j] = sp_.hi; lo[j] = sp_.lo; }
-      sm.rfrag[wave][mb][ts][0][lane] = hi;
-      sm.rfrag[wave][mb][ts][1][lane] = lo;
+      for (int j = 0; j < 8; ++j) {
+        const Bf16Pair sp = split_bf16(r[mb][8 * ts + j]);
+        hi[j] = sp.hi;
+        lo[j] = sp.lo;
+      }
+      sm.fr.rfrag[wave][mb][ts][0][lane] = hi;
+      sm.fr.rfrag[wave][mb][ts][1][lane] = lo;
     }
   __syncthreads();
 
@@ -172,10 +226,10 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
     for (int src = 0; src < nsrc; ++src)
 #pragma unroll
       for (int ts = 0; ts < 2; ++ts) {
-        const bf16x8 ah = sm.kfrag[src][mb][ts][0][lane], al = sm.kfrag[src][mb][ts][1][lane];
+        const bf16x8 ah = sm.fr.kfrag[src][mb][ts][0][lane], al = sm.fr.kfrag[src][mb][ts][1][lane];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 bh = sm.rfrag[src][nb][ts][0][lane], bl = sm.rfrag[src][nb][ts][1][lane];
+          const bf16x8 bh = sm.fr.rfrag[src][nb][ts][0][lane], bl = sm.fr.rfrag[src][nb][ts][1][lane];
           p[nb] = mfma32(ah, bh, p[nb]);
           p[nb] = mfma32(ah, bl, p[nb]);
           p[nb] = mfma32(al, bh, p[nb]);
@@ -189,53 +243,75 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
   }
 }
 
+constexpr int kReduceThreads = 512;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void arl2_commit_reduce_kernel(
+__global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
     const float* __restrict__ s_prev, const float* __restrict__ alpha, const float* __restrict__ partial,
     int chunks, const bf16* __restrict__ pq, float* __restrict__ s_new, bf16* __restrict__ sneg_hi,
     bf16* __restrict__ sneg_lo, bf16* __restrict__ wt_hi, bf16* __restrict__ wt_lo, int H) {
   using S = CommitShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, NB = S::NB;
+  constexpr int V4 = DP * 8;  // float4 groups of the 32-column block
+  constexpr int PER = (V4 + kReduceThreads - 1) / kReduceThreads;
+  constexpr int kUnroll = 8;  // chunk loads in flight per group
   __shared__ float tile[DP][33];  // S_new[:, 32 nb .. 32 nb + 31], padded against bank conflicts
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
   const float a = alpha ? alpha[bh] : 1.f;
+  constexpr int kStride = DP * DP / 4;  // float4 between consecutive chunks
 
-  // S_new = alpha S_prev + sum_c P_c, fixed order over chunks.  Each thread owns 4 adjacent
-  // columns of a row (float4) and keeps 8 chunk loads in flight.
-  for (int e = tid; e < DP * 8; e += kThreads) {
+  // S_new = alpha S_prev + sum_c P_c, chunks added in a fixed order.  Each thread owns PER
+  // float4 groups (4 adjacent columns of a row) and keeps all their loads of a round in flight.
+  f32x4 acc[PER];
+  bool ok[PER];
+  const f32x4* pp[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + kReduceThreads * u;
+    const int row = e >> 3, col = 32 * nb + (e & 7) * 4;
+    ok[u] = e < V4 && row < D && col < D;
+    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pp[u] = reinterpret_cast<const f32x4*>(partial + bh * chunks * DP * DP + row * DP + col);
+    if (ok[u]) acc[u] = a * *reinterpret_cast<const f32x4*>(s_prev + (bh * D + row) * D + col);
+  }
+  for (int c = 0; c < chunks; c += kUnroll) {
+    f32x4 x[PER][kUnroll];
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+#pragma unroll
+      for (int w = 0; w < kUnroll; ++w)
+        x[u][w] = (ok[u] && c + w < chunks) ? pp[u][(int64_t)(c + w) * kStride] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+#pragma unroll
+      for (int w = 0; w < kUnroll; ++w)
+        if (c + w < chunks) acc[u] += x[u][w];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + kReduceThreads * u;
+    if (e >= V4) continue;
     const int row = e >> 3, c4 = (e & 7) * 4, col = 32 * nb + c4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (row < D && col < D) {
-      const f32x4 sp = *reinterpret_cast<const f32x4*>(s_prev + (bh * D + row) * D + col);
-      acc = a * sp;
-      const f32x4* pp = reinterpret_cast<const f32x4*>(partial + bh * chunks * DP * DP + row * DP + col);
-      constexpr int kStride = DP * DP / 4;  // float4 between consecutive chunks
-      int c = 0;
-      for (; c + 8 <= chunks; c += 8) {
-        f32x4 x[8];
+    if (ok[u]) *reinterpret_cast<f32x4*>(s_new + (bh * D + row) * D + col) = acc[u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = pp[(int64_t)(c + u) * kStride];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += x[u];
-      }
-      for (; c < chunks; ++c) acc += pp[(int64_t)c * kStride];
-      *reinterpret_cast<f32x4*>(s_new + (bh * D + row) * D + col) = acc;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) tile[row][c4 + u] = acc[u];
+    for (int q = 0; q < 4; ++q) tile[row][c4 + q] = acc[u][q];
   }
   __syncthreads();
 
   // -S_new as B fragments for the next write: k-step st, element j <-> key feature
   // 16 st + 8 (j / 4) + 4 (l / 32) + j % 4 (the row order of a C block), lane column = value feature.
-  for (int e = tid; e < KS * 64; e += kThreads) {
+  for (int e = tid; e < KS * 64; e += kReduceThreads) {
     const int st = e >> 6, l = e & 63;
     bf16x8 hi, lo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(-tile[16 * st + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3)][l & 31]); hi[j] = sp_.hi; lo[j] = sp_.lo; }
+    for (int j = 0; j < 8; ++j) {
+      const Bf16Pair sp = split_bf16(-tile[16 * st + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3)][l & 31]);
+      hi[j] = sp.hi;
+      lo[j] = sp.lo;
+    }
     const int64_t fo = ((bh * KS + st) * NB + nb) * 64 + l;
     reinterpret_cast<bf16x8*>(sneg_hi)[fo] = hi;
     reinterpret_cast<bf16x8*>(sneg_lo)[fo] = lo;
@@ -243,14 +319,18 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_reduce_kernel(
 
   // W = phi_q S_new on this column block; stored transposed and split: W^T [j][i].
   const bf16* pqh = pq + (int64_t)h * DP * D;
-  for (int mb = wave; mb < MB; mb += 4) {
+  for (int mb = wave; mb < MB; mb += kReduceThreads / 64) {
     f32x16 w = zero16();
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
       const bf16x8 af = ld_bf16x8(pqh + (32 * mb + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
       bf16x8 bhi, blo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { const Bf16Pair sp_ = split_bf16(tile[16 * st + 8 * (lane >> 5) + j][lane & 31]); bhi[j] = sp_.hi; blo[j] = sp_.lo; }
+      for (int j = 0; j < 8; ++j) {
+        const Bf16Pair sp = split_bf16(tile[16 * st + 8 * (lane >> 5) + j][lane & 31]);
+        bhi[j] = sp.hi;
+        blo[j] = sp.lo;
+      }
       w = mfma32(af, bhi, w);
       w = mfma32(af, blo, w);
     }
@@ -261,7 +341,11 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_reduce_kernel(
       if (i0 < D) {
         bf16x4 hi, lo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { const Bf16Pair sp_ = split_bf16(w[4 * g + e]); hi[e] = sp_.hi; lo[e] = sp_.lo; }
+        for (int e = 0; e < 4; ++e) {
+          const Bf16Pair sp = split_bf16(w[4 * g + e]);
+          hi[e] = sp.hi;
+          lo[e] = sp.lo;
+        }
         const int64_t o = (bh * DP + col) * D + i0;
         *reinterpret_cast<bf16x4*>(wt_hi + o) = hi;
         *reinterpret_cast<bf16x4*>(wt_lo + o) = lo;
@@ -302,7 +386,7 @@ hipError_t launch_partial_d(const CommitPartialArgs& a, hipStream_t stream) {
 template <int D>
 hipError_t launch_reduce_d(const CommitReduceArgs& a, hipStream_t stream) {
   dim3 grid(CommitShape<D>::NB, a.H, a.B);
-  hipLaunchKernelGGL((arl2_commit_reduce_kernel<D>), grid, dim3(kThreads), 0, stream, a.s_prev, a.alpha,
+  hipLaunchKernelGGL((arl2_commit_reduce_kernel<D>), grid, dim3(kReduceThreads), 0, stream, a.s_prev, a.alpha,
                      a.partial, a.chunks, static_cast<const bf16*>(a.pq), a.s_new, static_cast<bf16*>(a.sneg_hi),
                      static_cast<bf16*>(a.sneg_lo), static_cast<bf16*>(a.wt_hi), static_cast<bf16*>(a.wt_lo),
                      a.H);
