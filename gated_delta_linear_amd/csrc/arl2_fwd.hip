@@ -6,25 +6,41 @@
 // associativity; W is formed once per frame by the state-write kernels, so a pass only
 // adds a Q x W product to the attention accumulator.
 //
-// Work decomposition.  One work-group of 8 waves per (stream, head, 128-query tile), two
-// waves per SIMD.  Waves 0-3 and 4-7 form two groups that own the same 128 query rows (32
-// per wave) but opposite halves of the frame's keys; the halves are merged through LDS at
-// the end (max / sum rescaling), so no partial result leaves the chip.  Each group streams
-// its half in 64-key tiles, double-buffered in LDS and staged by all 512 threads.
+// Work decomposition.  One work-group of 4 waves (one per SIMD) per (stream, head,
+// 128-query tile).  Wave w owns 64 query rows (w % 2) and one half of the frame's keys
+// (w / 2); the two halves of a row block are merged through LDS at the end (max / sum
+// rescaling), so no partial result leaves the chip.  A wave holds two 32-row MFMA blocks,
+// so every K or V fragment it reads from LDS feeds two MFMAs: LDS traffic is 64 bytes per
+// clock and CU at the full MFMA rate, half of what 32-row waves would need.  With one wave
+// per SIMD the wave has the whole register file (the output accumulators live in AGPRs).
 //
-// Scores are computed transposed, S^T = K Q^T, so that every lane holds one query row and
-// 32 of the tile's keys: the row max needs one cross-lane exchange (l, l ^ 32), the row sum
-// none until the end.  The output is accumulated transposed too, O^T += V^T P^T, one query
-// row per lane, so rescaling is a per-lane multiply.  V^T is written to LDS while staging:
-// each thread transposes a 4-key x 8-feature block in registers (v_perm) and stores it in
-// the key order of the P^T fragments; rows are padded by 16 bytes so that fragment reads
-// (32 consecutive rows) are conflict-free 16-byte loads.  K and V come in through buffer
-// loads: rows past the end of the frame lie outside the buffer and read as zeros.
+// Pipeline.  A wave walks its keys in units of 32.  Step u overlaps the score MFMAs of unit
+// u+1 (S^T = K Q^T) with the VALU softmax of unit u (phase A), then the O^T += V^T P^T MFMAs
+// of unit u with the row max of unit u+1 (phase B); each phase is a few short stages closed
+// by scheduling barriers, and LDS fragments are read two stages ahead of their MFMAs.  Keys
+// are staged per 64-key iteration (two units, one work-group barrier): K as 32-key
+// half-tiles in a ring of four LDS slots per key half (direct-to-LDS buffer loads), since
+// an iteration's units read the second half of one tile and the first half of the next;
+// V^T as whole 64-key tiles, double-buffered, through registers: each thread transposes
+// 4-key x 8-feature blocks, converting them to fp16 on the way, and stores them in the key
+// order of the P^T fragments, in rows padded by 16 bytes so that fragment reads (32
+// consecutive rows) are conflict-free 16-byte loads.  Rows past the end of the frame lie
+// outside the buffer descriptors and read as zeros.
 //
-// Softmax: exp2 with the scale folded in; the running max is only raised when a tile's max
+// Precision.  The P V product runs in fp16 (same MFMA rate as bf16): P, at most 2^8 (see
+// below), is rounded to nearest fp16 (relative step 2^-11, eight times finer than bf16, whose
+// rounding of P alone puts the output error at the edge of a 2e-2 budget on long streams),
+// and V converts from bf16 to fp16 exactly for |v| <= 65504 (values beyond become infinite,
+// so they show up instead of being clipped).  Q K^T and the Q W term stay bf16 x bf16 with
+// fp32 accumulation.
+//
+// Scores are transposed so that every lane holds one query row per block and 16 of the
+// unit's keys: the row max needs one cross-lane exchange (l, l ^ 32), the row sum none
+// until the end, and rescaling the transposed accumulator is a per-lane multiply.
+// Softmax: exp2 with the scale folded in; the running max is only raised when a unit's max
 // exceeds it by more than 8 (in log2 units) in some lane of the wave, so P stays below 2^8
-// and the rescale of the accumulator is skipped on almost every tile.  Row sums use dot2 on
-// the bf16 P that enters the MFMA.
+// and the rescale of the accumulator is skipped on almost every unit.  Row sums use dot2 on
+// the rounded P that enters the MFMA.
 #include <type_traits>
 
 #include "arl2_device.h"
@@ -34,13 +50,22 @@ namespace arl2 {
 namespace {
 
 constexpr int kQTile = 128;  // query rows per work-group
-constexpr int kKV = 64;      // keys per LDS tile
-constexpr int kThreads = 512;
+constexpr int kKV = 64;      // keys per staging iteration (two units)
+constexpr int kUnit = 32;    // keys per pipeline unit
+constexpr int kThreads = 256;
 constexpr float kRescaleSlack = 8.f;  // log2 headroom before the running max is raised
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+// Lambdas of the kernel are always inlined (large generic lambdas would otherwise become calls
+// with their captures on the stack).
+#define ARL2_INLINE __attribute__((always_inline))
+
+using On = std::true_type;
+using Off = std::false_type;
+template <int N>
+using Ic = std::integral_constant<int, N>;
 
 template <int D>
 struct FwdShape {
@@ -49,53 +74,90 @@ struct FwdShape {
   static constexpr int MB = DP / 32;         // 32-row blocks over output features
   static constexpr int CPR = D / 8;          // 16-byte chunks per token row
   static constexpr int VBLK = 16 * CPR;      // 4-key x 8-feature blocks per V tile
-  static constexpr int VLD = kKV + 8;        // V^T row stride in bf16 (64 keys + 16 bytes of padding)
-  // K tile: one plane of 64 rows x 32 bytes per k-step (features 16 st .. 16 st + 15), so that
-  // every MFMA fragment is one contiguous kilobyte.
-  static constexpr int K_BYTES = KS * kKV * 32;
+  static constexpr int VPT = (VBLK + 127) / 128;  // such blocks per staging thread (128 per key half)
+  static constexpr int VLD = kKV + 8;        // V^T row stride in fp16 (64 keys + 16 bytes of padding)
+  // K half-tile: one plane of 32 rows x 32 bytes per k-step (features 16 st .. 16 st + 15), so
+  // that every MFMA fragment is one contiguous kilobyte.
+  static constexpr int KH_BYTES = KS * kUnit * 32;
   static constexpr int VT_BYTES = DP * VLD * 2;
-  static constexpr int K_INSTR = 2 * KS;     // 1-KB direct-to-LDS loads per K tile
+  static constexpr int NA = KS < 4 ? KS : 4;          // stages of phase A
+  static constexpr int NB = 2 * MB < 4 ? 2 * MB : 4;  // stages of phase B
+  static constexpr int FA = KS / NA;                  // K fragments per A stage
+  static constexpr int FB = 2 * MB / NB;              // V^T fragments per B stage
 };
 
-// Buffer resource over rows [tile * 64, T) of one (stream, head) slice of a [B][T][H][d]
+// Buffer resource over rows [first_row, T) of one (stream, head) slice of a [B][T][H][d]
 // tensor: anything past the frame lies outside num_records, and loads there return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, int T, int64_t rs, int d, int tile) {
-  const int64_t start = (int64_t)tile * kKV * rs;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int T, int64_t rs, int d, int first_row) {
+  const int64_t start = (int64_t)first_row * rs;
   const int64_t left = (int64_t)(T - 1) * rs + d - start;
   const bool any = left > 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(any ? base + start : base), (short)0,
                                            any ? (int)(left * 2) : 0, 0x00020000);
 }
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+// voff: per-lane byte offset; soff: wave-uniform byte offset (kept in a scalar register).
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(x.x, x.y, x.z, x.w);
 }
 
 // 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane (lds wave-uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Pins a value to the architectural VGPRs at this point.  MFMA results land in AGPRs; a
+// score block that the VALU is about to read moves over once, here, so that the AGPRs hold
+// only the blocks still being accumulated.
+__device__ __forceinline__ void to_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
+
+// Marks a value as produced at this point, so that the compiler does not sink its computation
+// into a later stage (stages are laid out so that VALU work overlaps the MFMAs of its stage).
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 // Wait until all of this wave's vector memory operations (including loads into LDS) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most n of this wave's vector memory loads are in flight (n < 16).  Loads
+// complete in issue order, so this waits for every load issued before the last n.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void arl2_fwd_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void arl2_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
     int T, int H, int nq, int n_items, int per_xcd, float scale_log2) {
   using S = FwdShape<D>;
-  constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, CPR = S::CPR, VBLK = S::VBLK,
-                K_BYTES = S::K_BYTES, VT_BYTES = S::VT_BYTES, K_INSTR = S::K_INSTR;
+  constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
+                KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB;
 
-  // LDS: K tiles [group][buffer] then V^T tiles [group][buffer].  After the loop the K part
-  // holds W^T (hi, lo) and the V part the exchange between the two groups.
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * K_BYTES + 4 * VT_BYTES];
-  unsigned char* const kreg_lds = smem;
-  unsigned char* const vreg_lds = smem + 4 * K_BYTES;
-  auto ktile = [&](int g, int buf) { return kreg_lds + (2 * g + buf) * K_BYTES; };
-  auto vtile = [&](int g, int buf) { return reinterpret_cast<bf16*>(vreg_lds + (2 * g + buf) * VT_BYTES); };
+  // LDS: the four K ring slots and the two V^T buffers are separate arrays ([key half][...]
+  // each), addressed with compile-time slot numbers (the steady loop is unrolled by iteration
+  // parity), so that the compiler can tell the LDS accesses of an iteration from the
+  // direct-to-LDS loads in flight into other slots and does not wait for those loads.  After
+  // the loop the K arrays hold W^T (hi, lo) and the V arrays the exchange between the halves.
+  constexpr int KA_BYTES = 2 * KH_BYTES, VA_BYTES = 2 * VT_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char ks0[KA_BYTES], ks1[KA_BYTES], ks2[KA_BYTES], ks3[KA_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char vs0[VA_BYTES], vs1[VA_BYTES];
+  auto karr = [&](auto slot_c) ARL2_INLINE -> unsigned char* {
+    constexpr int sl = decltype(slot_c)::value & 3;
+    if constexpr (sl == 0) return ks0;
+    else if constexpr (sl == 1) return ks1;
+    else if constexpr (sl == 2) return ks2;
+    else return ks3;
+  };
+  auto varr = [&](auto buf_c) ARL2_INLINE -> unsigned char* {
+    if constexpr ((decltype(buf_c)::value & 1) == 0) return vs0;
+    else return vs1;
+  };
 
   // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin, so consecutive items
   // (the query tiles of one head) are given to work-groups on the same XCD and share its L2.
@@ -108,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void arl2_fwd_kernel(
   // descriptors and LDS bases built from them need no per-lane handling
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wq = wave & 3;
+  const int qs = wave & 1, grp = wave >> 1;  // row block of 64 and key half of this wave
   const int64_t rs = (int64_t)H * D;
   const int64_t base = ((int64_t)b * T * H + h) * D;
   const bf16* qb = q + base;
@@ -116,279 +178,433 @@ __global__ __launch_bounds__(kThreads) void arl2_fwd_kernel(
   const bf16* vb = v + base;
 
   const int ntiles = (T + kKV - 1) / kKV;
-  const int nt0 = (ntiles + 1) >> 1;  // group 0: tiles [0, nt0); group 1: [nt0, ntiles)
+  const int nt0 = (ntiles + 1) >> 1;  // key half 0: tiles [0, nt0); key half 1: [nt0, ntiles)
   const int my_first = grp ? nt0 : 0, my_count = grp ? ntiles - nt0 : nt0;
   const int iters = nt0;
+  const int key0 = my_first * kKV;  // first key of this wave's half
+  // end of this wave's keys: every iteration runs all its units, and units past the end (the
+  // second half's last iteration when it has one tile fewer, the unit after each half's last)
+  // are masked to -inf, so they add nothing
+  const int key_end = grp ? T : min(T, nt0 * kKV);
+  (void)my_count;
 
   if (D < DP) {  // padded V^T rows stay zero for the whole kernel
-    for (int i = tid; i < 4 * VT_BYTES / 16; i += kThreads)
-      reinterpret_cast<uint4*>(vreg_lds)[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < VA_BYTES / 16; i += kThreads) {
+      reinterpret_cast<uint4*>(vs0)[i] = make_uint4(0, 0, 0, 0);
+      reinterpret_cast<uint4*>(vs1)[i] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();
   }
 
-  // Staging roles: waves 0-3 stage group 0's tiles, waves 4-7 group 1's.
-  const int sg = wave >> 2, st_t = tid & 255, sw = wave & 3;
-  const int sg_first = sg ? nt0 : 0;
-  // K: direct-to-LDS loads; instruction i (st = i / 2, 32-row block i % 2) puts rows
-  // 32 (i % 2) + lane / 2, features 16 st + 8 (lane % 2) .. + 7 at 16 lane.
+  // Staging: the two waves of a key half stage its keys (wave sw of the pair: 128 threads).
+  const int st_t = tid & 127, sw = qs;
+  // K half-tile u (keys key0 + 32 u ..): KS direct-to-LDS loads, plane st from instruction st;
+  // lane l brings row l / 2, features 16 st + 8 (l % 2) .. + 7, to 16 l within the plane.
   const int k_lane_off = (int)(((lane >> 1) * rs + 8 * (lane & 1)) * 2);
-  auto load_k = [&](int tile, int buf) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kb, T, rs, D, sg_first + tile);
-    unsigned char* dst = ktile(sg, buf);
+  auto load_k_half = [&](int u, unsigned char* slot) ARL2_INLINE {  // slot: the ring slot's array
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, T, rs, D, key0 + kUnit * u);
+    unsigned char* dst = slot + grp * KH_BYTES;
 #pragma unroll
-    for (int c = 0; c < (K_INSTR + 3) / 4; ++c) {
-      const int i = sw + 4 * c;
-      if (i < K_INSTR)
-        dma16(r, dst + (i >> 1) * (kKV * 32) + (i & 1) * 1024,
-              k_lane_off + (int)((i & 1) * 32 * rs * 2) + (i >> 1) * 32);
+    for (int st = 0; st < KS; ++st) dma16(r, dst + st * 1024, k_lane_off, st * 32);
+  };
+  // V: blocks of 4 keys (4 va .. 4 va + 3) x 8 features (8 vbb ..) through registers, with the
+  // 16 lanes of a quarter-wave on the 16 key blocks of one feature block, transposed (and
+  // converted to fp16) on the way into LDS so that the stores of a quarter-wave fill one V^T
+  // row.  Every thread issues the same number of loads (a thread without a block of its own
+  // reloads block 0).
+  int v_off[VPT];  // byte offset of the block's first key row (key kk adds kk rows)
+  int v_dst[VPT];  // V^T element offset of the block's first row and key slot
+  bool v_mine[VPT];
+#pragma unroll
+  for (int r = 0; r < VPT; ++r) {
+    const int blk = st_t + 128 * r;
+    v_mine[r] = blk < VBLK;
+    const int bb = v_mine[r] ? blk : 0;
+    const int va = bb & 15, vbb = bb >> 4;
+    v_off[r] = (int)((4 * va * rs + 8 * vbb) * 2);
+    // keys of block va sit at slot {0, 2, 1, 3}[va % 4] of their 16-key group (the P^T order)
+    const int v_slot = ((va & 1) << 1) | ((va >> 1) & 1);
+    v_dst[r] = (8 * vbb) * VLD + 16 * (va >> 2) + 4 * v_slot;
+  }
+  uint4 vreg[VPT][4];
+  auto load_v = [&](int tile) ARL2_INLINE {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(vb, T, rs, D, key0 + kKV * tile);
+#pragma unroll
+    for (int rr = 0; rr < VPT; ++rr)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) vreg[rr][kk] = buf_load16(r, v_off[rr], (int)(kk * rs * 2));
+  };
+  // store_v_part: block rr, word pairs i in [i0, i1) (rows 2 i, 2 i + 1 of the block's V^T
+  // rows); load_v_part: block rr, keys kk in [k0, k1).
+  auto store_v_part = [&](auto buf_c, int rr, int i0, int i1) ARL2_INLINE {
+    if (v_mine[rr]) {
+      f16* vrow = reinterpret_cast<f16*>(varr(buf_c) + grp * VT_BYTES) + v_dst[rr];
+      const unsigned w[4][4] = {{vreg[rr][0].x, vreg[rr][0].y, vreg[rr][0].z, vreg[rr][0].w},
+                                {vreg[rr][1].x, vreg[rr][1].y, vreg[rr][1].z, vreg[rr][1].w},
+                                {vreg[rr][2].x, vreg[rr][2].y, vreg[rr][2].z, vreg[rr][2].w},
+                                {vreg[rr][3].x, vreg[rr][3].y, vreg[rr][3].z, vreg[rr][3].w}};
+      auto feat = [&](int kk, int i, int odd) ARL2_INLINE {
+        return __uint_as_float(odd ? (w[kk][i] & 0xFFFF0000u) : (w[kk][i] << 16));
+      };
+#pragma unroll
+      for (int i = i0; i < i1; ++i)
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const f16x2 k01 = __builtin_convertvector((f32x2{feat(0, i, odd), feat(1, i, odd)}), f16x2);
+          const f16x2 k23 = __builtin_convertvector((f32x2{feat(2, i, odd), feat(3, i, odd)}), f16x2);
+          *reinterpret_cast<uint2*>(vrow + (2 * i + odd) * VLD) =
+              make_uint2(__builtin_bit_cast(unsigned, k01), __builtin_bit_cast(unsigned, k23));
+        }
     }
   };
-  // V: a block of 4 keys (4 va .. 4 va + 3) x 8 features (8 vbb ..) through registers, with the
-  // 16 lanes of a quarter-wave on 16 key blocks of one feature block, transposed on the way
-  // into LDS so that the stores of a quarter-wave fill one V^T row.
-  const int va = st_t & 15, vbb = st_t >> 4;
-  const bool v_stager = st_t < VBLK;
-  int v_off[4];
+  auto load_v_part = [&](__amdgpu_buffer_rsrc_t r, int rr, int k0, int k1) ARL2_INLINE {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) v_off[kk] = (int)(((4 * va + kk) * rs + 8 * vbb) * 2);
-  uint4 vreg[4];
-  auto load_v = [&](int tile) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vb, T, rs, D, sg_first + tile);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) vreg[kk] = v_stager ? buf_load16(r, v_off[kk]) : make_uint4(0, 0, 0, 0);
+    for (int kk = k0; kk < k1; ++kk) vreg[rr][kk] = buf_load16(r, v_off[rr], (int)(kk * rs * 2));
   };
-  // keys of block va sit at slot {0, 2, 1, 3}[va % 4] of their 16-key group (the P^T order)
-  const int v_slot = ((va & 1) << 1) | ((va >> 1) & 1);
-  const int v_col = 16 * (va >> 2) + 4 * v_slot;  // key position within a V^T row
-  auto store_v = [&](int buf) {
-    if (!v_stager) return;
-    bf16* vrow = vtile(sg, buf) + (8 * vbb) * VLD + v_col;
-    const unsigned w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-    const unsigned w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-    const unsigned w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-    const unsigned w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+  auto store_v = [&](auto buf_c) ARL2_INLINE {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int rr = 0; rr < VPT; ++rr) {
+      if (!v_mine[rr]) continue;
+      f16* vrow = reinterpret_cast<f16*>(varr(buf_c) + grp * VT_BYTES) + v_dst[rr];
+      const unsigned w[4][4] = {{vreg[rr][0].x, vreg[rr][0].y, vreg[rr][0].z, vreg[rr][0].w},
+                                {vreg[rr][1].x, vreg[rr][1].y, vreg[rr][1].z, vreg[rr][1].w},
+                                {vreg[rr][2].x, vreg[rr][2].y, vreg[rr][2].z, vreg[rr][2].w},
+                                {vreg[rr][3].x, vreg[rr][3].y, vreg[rr][3].z, vreg[rr][3].w}};
+      // word i of key kk holds features 2i (low half) and 2i + 1 (high half) as bf16; a bf16 is
+      // the upper half of the fp32 with the same value
+      auto feat = [&](int kk, int i, int odd) ARL2_INLINE {
+        return __uint_as_float(odd ? (w[kk][i] & 0xFFFF0000u) : (w[kk][i] << 16));
+      };
 #pragma unroll
-      for (int odd = 0; odd < 2; ++odd) {
-        const unsigned sel = odd ? 0x07060302u : 0x05040100u;
-        const uint2 val = make_uint2(__builtin_amdgcn_perm(w1[i], w0[i], sel), __builtin_amdgcn_perm(w3[i], w2[i], sel));
-        *reinterpret_cast<uint2*>(vrow + (2 * i + odd) * VLD) = val;
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const f16x2 k01 = __builtin_convertvector((f32x2{feat(0, i, odd), feat(1, i, odd)}), f16x2);
+          const f16x2 k23 = __builtin_convertvector((f32x2{feat(2, i, odd), feat(3, i, odd)}), f16x2);
+          *reinterpret_cast<uint2*>(vrow + (2 * i + odd) * VLD) =
+              make_uint2(__builtin_bit_cast(unsigned, k01), __builtin_bit_cast(unsigned, k23));
+        }
+    }
   };
-  // W^T = (phi_q S)^T, hi then lo, into the K part of LDS (free during the last iteration), in
-  // the same plane layout: plane (hl, st) holds rows 0 .. DP-1 x 32 bytes.
-  constexpr int W_INSTR = 2 * KS * DP / 32;
+  // W^T = (phi_q S)^T, hi then lo, into the K arrays after the loop, as planes of DP rows x 32
+  // bytes: plane (hl, st) holds features 16 st .. 16 st + 15 of every output feature.  Its
+  // kilobyte c sits in K array c / KA_KB at kilobyte c % KA_KB.
+  constexpr int W_INSTR = 2 * KS * DP / 32, KA_KB = KA_BYTES / 1024;
+  auto w_kb = [&](int c) ARL2_INLINE -> unsigned char* {
+    const int a = c / KA_KB;
+    return (a == 0 ? ks0 : a == 1 ? ks1 : a == 2 ? ks2 : ks3) + (c % KA_KB) * 1024;
+  };
   const int64_t wbase = ((int64_t)b * H + h) * DP * D;
   const int w_lane_off = (int)(((lane >> 1) * D + 8 * (lane & 1)) * 2);
-  auto load_w = [&]() {
+  auto load_w = [&]() ARL2_INLINE {
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(wt_hi + wbase), (short)0,
                                                                         DP * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(wt_lo + wbase), (short)0,
                                                                         DP * D * 2, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < (W_INSTR + 7) / 8; ++c) {
-      const int i = wave + 8 * c;  // 1 KB each: plane i / (DP / 32), 32-row block i % (DP / 32)
+    for (int c = 0; c < (W_INSTR + 3) / 4; ++c) {
+      const int i = wave + 4 * c;  // 1 KB each: plane i / (DP / 32), 32-row block i % (DP / 32)
       if (i < W_INSTR) {
         const int plane = i / (DP / 32), rb = i % (DP / 32);
         const int hl = plane / KS, st = plane % KS;
-        dma16(hl ? rl : rh, kreg_lds + i * 1024, w_lane_off + (32 * rb * D + 16 * st) * 2);
+        dma16(hl ? rl : rh, w_kb(i), w_lane_off, (32 * rb * D + 16 * st) * 2);
       }
     }
   };
 
-  // This lane's query row as B fragments of Q^T (k-step st = features 16 st .. 16 st + 15).
-  const int qrow = qt * kQTile + wq * 32 + (lane & 31);
-  bf16x8 qf[KS];
+  // This lane's query rows (one per 32-row block) as B fragments of Q^T (k-step st = features
+  // 16 st .. 16 st + 15).
+  int qrow[2];
+  bf16x8 qf[2][KS];
 #pragma unroll
-  for (int st = 0; st < KS; ++st)
-    qf[st] = qrow < T ? ld_bf16x8(qb + qrow * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+  for (int qq = 0; qq < 2; ++qq) {
+    qrow[qq] = qt * kQTile + qs * 64 + qq * 32 + (lane & 31);
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qf[qq][st] = qrow[qq] < T ? ld_bf16x8(qb + qrow[qq] * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+  }
 
-  f32x16 acc[MB];
+  f32x16 acc[2][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
-  float m_run = -INFINITY;  // running max (raw score units), equal in lanes l and l ^ 32
-  float l_run = 0.f;        // this lane's share of the running sum
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[qq][mb] = zero16();
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max (raw score units), equal in lanes l and l ^ 32
+  float l_run[2] = {0.f, 0.f};              // this lane's share of the running sum
 
   // Fragment offsets of this lane inside a K plane and a V^T tile.
   const int k_frag = (lane & 31) * 32 + (lane >> 5) * 16;
   const int v_frag = (lane & 31) * VLD + 8 * (lane >> 5);
 
-  // Scores of one K tile (S^T, two 32-key blocks) and their per-row max, with keys past the
-  // frame masked (lanes l and l ^ 32 hold the two halves of a row).
-  auto scores = [&](int kbuf, f32x16 (&sc)[2]) {
-    const unsigned char* kt = ktile(grp, kbuf) + k_frag;
+  // Fragments in flight.  K fragment st of a unit = k-step st; V^T fragment f of a unit =
+  // k-step f / MB of the unit (16 keys), feature block f % MB.
+  bf16x8 kfr[KS];
+  f16x8 vfr[2 * MB];
+  const f16x2 ones = {(f16)1.f, (f16)1.f};
+
+  // Softmax chunk c of a unit: row block c / 2, keys of k-step c % 2 (registers 8 (c % 2) ..
+  // + 7 of the score block), into the fp16 P^T fragment pf[c / 2][c % 2] and the row sum (of
+  // the rounded P that enters the MFMA).
+  auto softmax_chunk = [&](const f32x16 (&sa)[2], f16x8 (&pf)[2][2], int c, const float (&mc)[2]) ARL2_INLINE {
+    const int qq = c >> 1, hh = c & 1;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sc[kb2] = zero16();
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-        sc[kb2] = mfma32(*reinterpret_cast<const bf16x8*>(kt + st * (kKV * 32) + kb2 * 1024), qf[st], sc[kb2]);
+    for (int jj = 0; jj < 8; jj += 2) {
+      const f32x2 e = {__builtin_amdgcn_exp2f(fmaf(sa[qq][8 * hh + jj], scale_log2, -mc[qq])),
+                       __builtin_amdgcn_exp2f(fmaf(sa[qq][8 * hh + jj + 1], scale_log2, -mc[qq]))};
+      const f16x2 p2 = __builtin_convertvector(e, f16x2);
+      pf[qq][hh][jj] = p2[0];
+      pf[qq][hh][jj + 1] = p2[1];
+      l_run[qq] = __builtin_amdgcn_fdot2(p2, ones, l_run[qq], false);
     }
+    pin(pf[qq][hh]);
+    pin(l_run[qq]);
   };
-  auto tile_max = [&](int tile, f32x16 (&sc)[2]) {
-    if ((tile + 1) * kKV > T) {  // ragged last tile: keys beyond the frame do not exist
+  // Keys of unit u past the end of this wave's keys do not take part.
+  auto mask_unit = [&](int u, f32x16 (&sc)[2]) ARL2_INLINE {
+    const int k0 = key0 + kUnit * u;
+    if (k0 + kUnit > key_end) {
+      const int lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (tile * kKV + 32 * kb2 + c_row(i, lane) >= T) sc[kb2][i] = -INFINITY;
+          if (k0 + c_row(i, lid) >= key_end) sc[qq][i] = -INFINITY;
     }
-    float mx = sc[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][i]);
-    return fmaxf(mx, other_half(mx, lane));
   };
-
-  // Raise the running max to a tile's max when it exceeds it by more than the slack in some
+  // Raise the running max to a unit's max when it exceeds it by more than the slack in some
   // lane of the wave (the accumulator and sum are rescaled); otherwise keep it, so P <= 2^8.
-  auto rescale_to = [&](float mx) {
-    if (__builtin_amdgcn_ballot_w64((mx - m_run) * scale_log2 > kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      l_run *= corr;
+  auto rescale_to = [&](const float (&mp)[2]) ARL2_INLINE {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int qq = 0; qq < 2; ++qq) {
+      const float mx = fmaxf(mp[qq], other_half(mp[qq], lane));  // lanes l and l ^ 32 hold one row
+      if (__builtin_amdgcn_ballot_w64((mx - m_run[qq]) * scale_log2 > kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run[qq], mx);
+        const float corr = __builtin_amdgcn_exp2f((m_run[qq] - m_new) * scale_log2);
+        m_run[qq] = m_new;
+        l_run[qq] *= corr;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][i] *= corr;
-    }
-  };
-  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-  // P = exp2(S scale - m scale) of one tile as bf16 B fragments, the row sums, and O^T += V^T P^T
-  // with the tile's V^T from LDS buffer vbuf.
-  auto softmax_pv = [&](const f32x16 (&sa)[2], int vbuf) {
-    const float mc = m_run * scale_log2;
-    const bf16* vt = vtile(grp, vbuf) + v_frag;
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
-      bf16x8 pf;  // k-step ks4 = 16 keys: element jj <-> register 8 (ks4 % 2) + jj of block ks4 / 2
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        pf[jj] = (bf16)__builtin_amdgcn_exp2f(fmaf(sa[ks4 >> 1][8 * (ks4 & 1) + jj], scale_log2, -mc));
-#pragma unroll
-      for (int jj = 0; jj < 8; jj += 2)
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[jj], pf[jj + 1]}, ones, l_run, false);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = mfma32(*reinterpret_cast<const bf16x8*>(vt + 32 * mb * VLD + 16 * ks4), pf, acc[mb]);
+          for (int i = 0; i < 16; ++i) acc[qq][mb][i] *= corr;
+      }
     }
   };
 
-  // Prologue: K of the group's first two tiles, V of the first; scores of the first tile.
-  load_k(0, 0);
-  load_k(1, 1);
+  // Step u: phase A = scores of unit u + 1 (into sb) with the softmax of unit u (from sa);
+  // phase B = O^T += V^T P^T for unit u with the row max of unit u + 1.  next_sw / cur_sw
+  // switch the work on unit u + 1 / unit u on or off at compile time (On / Off), so that every
+  // variant is branch-free.  Stage s of the step (A stages, then B stages) reads the fragments
+  // of stage s + 2.
+  // kslot_c / vbuf_c: compile-time ring slot of unit u + 1 and V^T buffer of unit u.
+  // hook(s) issues the staging work of stage s (A stages 0 .. NA - 1, then B stages) first.
+  auto step = [&](int u, const f32x16 (&sa)[2], f32x16 (&sb)[2], auto next_sw, auto cur_sw, auto kslot_c,
+                  auto vbuf_c, auto&& hook) ARL2_INLINE {
+    constexpr bool nx = decltype(next_sw)::value, cu = decltype(cur_sw)::value;
+    const unsigned char* kt = karr(kslot_c) + grp * KH_BYTES + k_frag;
+    const f16* vt = reinterpret_cast<const f16*>(varr(vbuf_c) + grp * VT_BYTES) + v_frag + 32 * (u & 1);
+    auto read_stage = [&](int s) ARL2_INLINE {
+      if (s < NA) {
+        if (nx)
+#pragma unroll
+          for (int f = s * FA; f < (s + 1) * FA; ++f) kfr[f] = *reinterpret_cast<const bf16x8*>(kt + f * 1024);
+      } else if (s < NA + NB) {
+        if (cu)
+#pragma unroll
+          for (int f = (s - NA) * FB; f < (s - NA + 1) * FB; ++f)
+            vfr[f] = *reinterpret_cast<const f16x8*>(vt + 32 * (f % MB) * VLD + 16 * (f / MB));
+      }
+    };
+    // (a half without keys keeps m = -inf; its P must come out 0, not NaN)
+    const float mc[2] = {m_run[0] == -INFINITY ? 0.f : m_run[0] * scale_log2,
+                         m_run[1] == -INFINITY ? 0.f : m_run[1] * scale_log2};
+    f16x8 pf[2][2];
+    read_stage(0);
+    read_stage(1);
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      hook(t);
+      read_stage(t + 2);
+      if (cu)
+#pragma unroll
+        for (int c = t * 4 / NA; c < (t + 1) * 4 / NA; ++c) softmax_chunk(sa, pf, c, mc);
+      if (nx)
+#pragma unroll
+        for (int f = t * FA; f < (t + 1) * FA; ++f)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) sb[qq] = mfma32(kfr[f], qf[qq][f], f ? sb[qq] : zero16());
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float mp[2] = {-INFINITY, -INFINITY};
+    if (nx) {
+      mask_unit(u + 1, sb);
+      to_vgpr(sb[0]);
+      to_vgpr(sb[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      hook(NA + t);
+      read_stage(NA + t + 2);
+      if (nx)
+#pragma unroll
+        for (int c = t * 4 / NB; c < (t + 1) * 4 / NB; ++c) {
+          const int qq = c >> 1, i0 = 8 * (c & 1);
+#pragma unroll
+          for (int i = i0; i < i0 + 8; ++i) mp[qq] = fmaxf(mp[qq], sb[qq][i]);
+          pin(mp[qq]);
+        }
+      if (cu)
+#pragma unroll
+        for (int f = t * FB; f < (t + 1) * FB; ++f)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) acc[qq][f % MB] = mfma32(vfr[f], pf[qq][f / MB], acc[qq][f % MB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (nx) rescale_to(mp);
+  };
+
+  // Prologue: K half-tiles 0, 1, 2 (ring slots 0-2), V tile 0 into LDS and tile 1 into
+  // registers; scores and max of unit 0.  The second barrier keeps the first iteration's
+  // loads into slot 0 behind every wave's read of unit 0.
+  load_k_half(sw, sw ? ks1 : ks0);
+  if (sw == 0) load_k_half(2, ks2);
   load_v(0);
-  store_v(0);
   wait_vmem();
+  store_v(Ic<0>());
+  if (iters > 1) load_v(1);
+  __syncthreads();
+  f32x16 s0[2], s1[2];
+  auto no_staging = [](int) ARL2_INLINE {};
+  step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
   __syncthreads();
 
-  f32x16 s0[2], s1[2];
-  if (my_count > 0) {
-    scores(0, s0);
-    rescale_to(tile_max(my_first, s0));
-  }
-  if (iters == 1) __syncthreads();  // W goes over K tile 0 during the only iteration
-
-  // Steady iteration j (j + 2 < iters, so tiles j and j + 1 exist for both groups): the MFMAs
-  // of tile j+1's scores, tile j's softmax (VALU) and tile j's P V MFMAs form one branch-free
-  // block that the compiler can interleave; the max of tile j+1 and the staging of K_{j+2}
-  // (already in flight) and V_{j+1} follow.
-  auto step_full = [&](int j, f32x16 (&sa)[2], f32x16 (&sb)[2]) {
-    load_k(j + 2, j & 1);
-    load_v(j + 1);
-    scores((j + 1) & 1, sb);
-    softmax_pv(sa, j & 1);
-    // interleave each score MFMA (with its fragment read) with a share of the softmax VALU
-    // work, then each P V MFMA likewise
-#pragma unroll
-    for (int i = 0; i < 2 * KS + 4 * MB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  // Iteration j (parity P = j % 2, a compile-time constant): units 2j and 2j + 1 (tile j of
+  // this key half).  Staging, spread over the stages so that the vector-memory path (shared by
+  // the CU's four waves) drains while the MFMAs run: K half-tile 2j + 3 + (wave of the pair)
+  // into the ring slot that held 2j - 1 or 2j (one plane per A stage of step 2j); V tile j + 1
+  // block by block from registers into the buffer that held tile j - 1, each block's registers
+  // then reloaded with tile j + 2 (block 0 in the B stages of step 2j, block 1 in those of step
+  // 2j + 1).  All K loads precede all V loads, so waiting for all but the V loads before the
+  // barrier leaves the K loads complete and the V loads in flight until their use.  Staging
+  // past the last tile reads zeros (outside the buffer descriptors) into slots and buffers
+  // that nothing reads again.
+  constexpr int SPLIT = NB >= 4 ? 2 : 1;  // B stages per store / per load of a block
+  auto v_stage = [&](auto buf_c, __amdgpu_buffer_rsrc_t vr, int rr, int b) ARL2_INLINE {
+    if (b < SPLIT) {
+      store_v_part(buf_c, rr, 4 * b / SPLIT, 4 * (b + 1) / SPLIT);
+    } else if (b < 2 * SPLIT) {
+      const int bb = b - SPLIT;
+      load_v_part(vr, rr, 4 * bb / SPLIT, 4 * (bb + 1) / SPLIT);
     }
-    rescale_to(tile_max(my_first + j + 1, sb));
-    store_v((j + 1) & 1);
-    wait_vmem();
-    __syncthreads();
   };
-  // The last two iterations: a group may have no tile j or j + 1, and W comes in last.
-  auto step_tail = [&](int j, f32x16 (&sa)[2], f32x16 (&sb)[2]) {
-    if (j + 1 < iters) load_v(j + 1);
-    if (j == iters - 1) load_w();
-    const bool next = j + 1 < my_count;
-    if (next) scores((j + 1) & 1, sb);
-    if (j < my_count) softmax_pv(sa, j & 1);
-    if (next) rescale_to(tile_max(my_first + j + 1, sb));
-    if (j + 1 < iters) store_v((j + 1) & 1);
-    wait_vmem();
+  auto iteration = [&](int j, auto par_c) ARL2_INLINE {
+    constexpr int P = decltype(par_c)::value;
+    unsigned char* kdst = (sw ? karr(Ic<2 * P + 4>()) : karr(Ic<2 * P + 3>())) + grp * KH_BYTES;
+    const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 3 + sw));
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vb, T, rs, D, key0 + kKV * (j + 2));
+    auto hook0 = [&](int st) ARL2_INLINE {
+      if (st < NA) {
+#pragma unroll
+        for (int pl = st * KS / NA; pl < (st + 1) * KS / NA; ++pl) dma16(kr, kdst + pl * 1024, k_lane_off, pl * 32);
+      } else {
+        if (st == NA) asm volatile("" ::: "memory");  // the K loads stay ahead of the V loads
+        v_stage(Ic<P + 1>(), vr, 0, st - NA);
+      }
+    };
+    auto hook1 = [&](int st) ARL2_INLINE {
+      if (VPT > 1 && st >= NA) v_stage(Ic<P + 1>(), vr, VPT - 1, st - NA);
+    };
+    step(2 * j, s0, s1, On(), On(), Ic<2 * P + 1>(), Ic<P>(), hook0);
+    step(2 * j + 1, s1, s0, On(), On(), Ic<2 * P + 2>(), Ic<P>(), hook1);
+    wait_vmem_but<4 * VPT>();
     __syncthreads();
   };
   int j = 0;
-  for (; j + 2 < iters; ++j) {
-    step_full(j, s0, s1);
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) s0[kb2] = s1[kb2];
+  for (; j + 1 < iters; j += 2) {
+    iteration(j, Ic<0>());
+    iteration(j + 1, Ic<1>());
   }
-  for (; j < iters; ++j) {
-    step_tail(j, s0, s1);
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) s0[kb2] = s1[kb2];
-  }
+  if (j < iters) iteration(j, Ic<0>());
 
-  // Epilogue.  W^T is in the K part of LDS.  The two groups exchange, through the V part, the
-  // halves of the accumulator that the other one finalises (with their running max and sum):
-  // group g finalises output feature blocks [g * MBH, (g + 1) * MBH) (for d < 64 group 0
-  // finalises the single block).
+  // Epilogue.  W^T comes into the K arrays while the two waves of a row block exchange,
+  // through the V arrays, the halves of the accumulator that the other one finalises (with
+  // their running max and sum): the wave of key half g finalises output feature blocks
+  // [g * MBH, (g + 1) * MBH) (for d < 64 key half 0 finalises the single block).
+  load_w();
   constexpr int MBH = MB >= 2 ? MB / 2 : 1;
-  constexpr int NXR = MBH * 16 + 2;  // exported rows: accumulator blocks, then max, then sum
-  static_assert((MB >= 2 ? 2 : 1) * NXR * 256 * 4 <= 4 * VT_BYTES, "exchange must fit in the V part");
-  static_assert(W_INSTR * 1024 <= 4 * K_BYTES, "W must fit in the K part");
-  float* xb = reinterpret_cast<float*>(vreg_lds);  // [exporter][NXR][256]
-  const int xl = wq * 64 + lane;
-  const int partner = 1 - grp;
+  constexpr int NXR = 2 * MBH * 16 + 4;  // exported rows: accumulator blocks, then 2 max, 2 sums
+  constexpr int NX = MB >= 2 ? 4 : 2;    // exporting waves
+  constexpr int XS_BYTES = NXR * 64 * 4, XS_PER = VA_BYTES / XS_BYTES;  // exchange slots per V array
+  static_assert(XS_PER >= 1 && (NX + XS_PER - 1) / XS_PER <= 2, "exchange must fit in the V arrays");
+  static_assert(W_INSTR <= 4 * KA_KB, "W must fit in the K arrays");
+  const int partner = wave ^ 2;
   const bool owner = MB >= 2 || grp == 0;
-  const bool partner_owns = MB >= 2 || partner == 0;
+  const bool partner_owns = MB >= 2 || grp == 1;
+  auto xslot = [&](int w) ARL2_INLINE {  // [NXR][64] floats of exporter w
+    const int xs = MB >= 2 ? w : (w & 1);
+    return reinterpret_cast<float*>((xs / XS_PER ? vs1 : vs0) + (xs % XS_PER) * XS_BYTES);
+  };
   if (partner_owns) {
-    float* xo = xb + (MB >= 2 ? grp : 0) * NXR * 256;
-    const int p0 = MB >= 2 ? partner * MBH : 0;
+    float* xo = xslot(wave);
+    const int p0 = MB >= 2 ? (1 - grp) * MBH : 0;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      if (mb >= p0 && mb < p0 + MBH)
+    for (int qq = 0; qq < 2; ++qq) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xo[((mb - p0) * 16 + i) * 256 + xl] = acc[mb][i];
-    xo[(MBH * 16) * 256 + xl] = m_run;
-    xo[(MBH * 16 + 1) * 256 + xl] = l_run;
+      for (int mb = 0; mb < MB; ++mb)
+        if (mb >= p0 && mb < p0 + MBH)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xo[((qq * MBH + mb - p0) * 16 + i) * 64 + lane] = acc[qq][mb][i];
+      xo[(2 * MBH * 16 + qq) * 64 + lane] = m_run[qq];
+      xo[(2 * MBH * 16 + 2 + qq) * 64 + lane] = l_run[qq];
+    }
   }
+  __syncthreads();
+
+  const float* xi = xslot(partner);
+  const int o0 = MB >= 2 ? grp * MBH : 0;
+  if (owner) {
+    float a0[2], a1[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const float m1 = xi[(2 * MBH * 16 + qq) * 64 + lane], l1 = xi[(2 * MBH * 16 + 2 + qq) * 64 + lane];
+      const float m = fmaxf(m_run[qq], m1);
+      const float e0 = __builtin_amdgcn_exp2f((m_run[qq] - m) * scale_log2);
+      const float e1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+      const float lsum = l_run[qq] * e0 + l1 * e1;
+      const float inv = 1.f / (lsum + other_half(lsum, lane));
+      a0[qq] = e0 * inv;
+      a1[qq] = e1 * inv;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb < o0 || mb >= o0 + MBH) continue;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[qq][mb][i] = acc[qq][mb][i] * a0[qq] + xi[((qq * MBH + mb - o0) * 16 + i) * 64 + lane] * a1[qq];
+    }
+  }
+  wait_vmem();  // W^T has landed (every wave waits for its own loads, then the barrier)
   __syncthreads();
   if (!owner) return;
 
-  const float* xi = xb + (MB >= 2 ? partner : 0) * NXR * 256;
-  const float m1 = xi[(MBH * 16) * 256 + xl], l1 = xi[(MBH * 16 + 1) * 256 + xl];
-  const float m = fmaxf(m_run, m1);
-  const float a0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
-  const float a1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
-  const float lsum = l_run * a0 + l1 * a1;
-  const float inv = 1.f / (lsum + other_half(lsum, lane));
-  const int o0 = MB >= 2 ? grp * MBH : 0;
-
-  // Normalise, then add Q W = Q (phi_q S) with W^T split in two bf16 terms (A fragments from LDS).
-  const unsigned char* wfrag = kreg_lds + k_frag;
+  // Add Q W = Q (phi_q S) with W^T split in two bf16 terms (A fragments from LDS).
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     if (mb < o0 || mb >= o0 + MBH) continue;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mb][i] = (acc[mb][i] * a0 + xi[((mb - o0) * 16 + i) * 256 + xl] * a1) * inv;
-#pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll
-      for (int hl = 0; hl < 2; ++hl)
-        acc[mb] = mfma32(*reinterpret_cast<const bf16x8*>(wfrag + ((hl * KS + st) * DP + 32 * mb) * 32), qf[st], acc[mb]);
+      for (int hl = 0; hl < 2; ++hl) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(w_kb((hl * KS + st) * (DP / 32) + mb) + k_frag);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) acc[qq][mb] = mfma32(a, qf[qq][st], acc[qq][mb]);
+      }
   }
 
-  if (qrow < T) {
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    if (qrow[qq] >= T) continue;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb < o0 || mb >= o0 + MBH) continue;
@@ -396,16 +612,16 @@ __global__ __launch_bounds__(kThreads) void arl2_fwd_kernel(
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * mb + 8 * g + 4 * (lane >> 5);
         if (d < D) {
-          const int64_t o = base + qrow * rs + d;
+          const int64_t o = base + qrow[qq] * rs + d;
           if (OUT_BF16) {
             bf16x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (bf16)acc[mb][4 * g + e];
+            for (int e = 0; e < 4; ++e) w[e] = (bf16)acc[qq][mb][4 * g + e];
             *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o) = w;
           } else {
             f32x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = acc[mb][4 * g + e];
+            for (int e = 0; e < 4; ++e) w[e] = acc[qq][mb][4 * g + e];
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = w;
           }
         }
