@@ -317,7 +317,9 @@ __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
     reinterpret_cast<bf16x8*>(sneg_lo)[fo] = lo;
   }
 
-  // W = phi_q S_new on this column block; stored transposed and split: W^T [j][i].
+  // W = phi_q S_new on this column block; stored transposed and split, W^T[j][i], as the pass
+  // kernel stages it: k-step planes [i / 16][j][i % 16], so that every kilobyte it loads is
+  // contiguous.
   const bf16* pqh = pq + (int64_t)h * DP * D;
   for (int mb = wave; mb < MB; mb += kReduceThreads / 64) {
     f32x16 w = zero16();
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
           hi[e] = sp.hi;
           lo[e] = sp.lo;
         }
-        const int64_t o = (bh * DP + col) * D + i0;
+        const int64_t o = bh * DP * D + ((int64_t)(i0 >> 4) * DP + col) * 16 + (i0 & 15);
         *reinterpret_cast<bf16x4*>(wt_hi + o) = hi;
         *reinterpret_cast<bf16x4*>(wt_lo + o) = lo;
       }

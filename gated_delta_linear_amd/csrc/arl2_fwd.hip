@@ -76,9 +76,14 @@ struct FwdShape {
   static constexpr int VBLK = 16 * CPR;      // 4-key x 8-feature blocks per V tile
   static constexpr int VPT = (VBLK + 127) / 128;  // such blocks per staging thread (128 per key half)
   static constexpr int VLD = kKV + 8;        // V^T row stride in fp16 (64 keys + 16 bytes of padding)
-  // K half-tile: one plane of 32 rows x 32 bytes per k-step (features 16 st .. 16 st + 15), so
-  // that every MFMA fragment is one contiguous kilobyte.
+  // K half-tile: 32 rows of 2D bytes, row-major, with the 16-byte granules of row r permuted
+  // (granule g holds feature chunk g ^ (r mod CPR)).  Every direct-to-LDS load then brings
+  // RPI whole rows (contiguous in memory), and the 32 rows of an MFMA fragment read land on
+  // distinct banks.
   static constexpr int KH_BYTES = KS * kUnit * 32;
+  static constexpr int RB = 2 * D;                  // bytes per row
+  static constexpr int RPI = 1024 / RB;             // rows per 1-KB load
+  static constexpr int NKV = CPR * CPR / 64 > 1 ? CPR * CPR / 64 : 1;  // distinct lane offsets of the loads
   static constexpr int VT_BYTES = DP * VLD * 2;
   static constexpr int NA = KS < 4 ? KS : 4;          // stages of phase A
   static constexpr int NB = 2 * MB < 4 ? 2 * MB : 4;  // stages of phase B
@@ -198,15 +203,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // Staging: the two waves of a key half stage its keys (wave sw of the pair: 128 threads).
   const int st_t = tid & 127, sw = qs;
-  // K half-tile u (keys key0 + 32 u ..): KS direct-to-LDS loads, plane st from instruction st;
-  // lane l brings row l / 2, features 16 st + 8 (l % 2) .. + 7, to 16 l within the plane.
-  const int k_lane_off = (int)(((lane >> 1) * rs + 8 * (lane & 1)) * 2);
+  // K half-tile u (keys key0 + 32 u ..): KS direct-to-LDS loads; load i brings rows RPI i ..
+  // RPI i + RPI - 1, lane l the granule l % CPR of row RPI i + l / CPR, i.e. feature chunk
+  // (l % CPR) ^ (row % CPR).  The lane offset repeats every NKV loads.
+  constexpr int RB = S::RB, RPI = S::RPI, NKV = S::NKV, CPR = S::CPR;
+  int k_vo[NKV];
+#pragma unroll
+  for (int q = 0; q < NKV; ++q) {
+    const int row = RPI * q + lane / CPR;
+    k_vo[q] = (int)((lane / CPR) * rs * 2) + 16 * ((lane % CPR) ^ (row % CPR));
+  }
+  auto dma_k = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int i) ARL2_INLINE {
+    dma16(r, dst + i * 1024, k_vo[i % NKV], (int)(RPI * i * rs * 2));
+  };
   auto load_k_half = [&](int u, unsigned char* slot) ARL2_INLINE {  // slot: the ring slot's array
     const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, T, rs, D, key0 + kUnit * u);
     unsigned char* dst = slot + grp * KH_BYTES;
 #pragma unroll
-    for (int st = 0; st < KS; ++st) dma16(r, dst + st * 1024, k_lane_off, st * 32);
+    for (int i = 0; i < KS; ++i) dma_k(r, dst, i);
   };
+  // K fragment of k-step st (row lane % 32, feature chunk 2 st + lane / 32) within a half-tile.
+  int k_fo[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    const int row = lane & 31;
+    k_fo[st] = row * RB + 16 * ((2 * st + (lane >> 5)) ^ (row % CPR));
+  }
   // V: blocks of 4 keys (4 va .. 4 va + 3) x 8 features (8 vbb ..) through registers, with the
   // 16 lanes of a quarter-wave on the 16 key blocks of one feature block, transposed (and
   // converted to fp16) on the way into LDS so that the stores of a quarter-wave fill one V^T
@@ -295,7 +317,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     return (a == 0 ? ks0 : a == 1 ? ks1 : a == 2 ? ks2 : ks3) + (c % KA_KB) * 1024;
   };
   const int64_t wbase = ((int64_t)b * H + h) * DP * D;
-  const int w_lane_off = (int)(((lane >> 1) * D + 8 * (lane & 1)) * 2);
   auto load_w = [&]() ARL2_INLINE {
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(wt_hi + wbase), (short)0,
                                                                         DP * D * 2, 0x00020000);
@@ -303,11 +324,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                                                         DP * D * 2, 0x00020000);
 #pragma unroll
     for (int c = 0; c < (W_INSTR + 3) / 4; ++c) {
-      const int i = wave + 4 * c;  // 1 KB each: plane i / (DP / 32), 32-row block i % (DP / 32)
+      const int i = wave + 4 * c;  // kilobyte i: plane i / (DP / 32), 32-row block i % (DP / 32)
       if (i < W_INSTR) {
-        const int plane = i / (DP / 32), rb = i % (DP / 32);
-        const int hl = plane / KS, st = plane % KS;
-        dma16(hl ? rl : rh, w_kb(i), w_lane_off, (32 * rb * D + 16 * st) * 2);
+        const int hl = i / (W_INSTR / 2), kb_in = i % (W_INSTR / 2);
+        dma16(hl ? rl : rh, w_kb(i), 16 * lane, kb_in * 1024);
       }
     }
   };
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   float l_run[2] = {0.f, 0.f};              // this lane's share of the running sum
 
   // Fragment offsets of this lane inside a K plane and a V^T tile.
-  const int k_frag = (lane & 31) * 32 + (lane >> 5) * 16;
+  const int k_frag = (lane & 31) * 32 + (lane >> 5) * 16;  // W^T planes: 32-byte rows
   const int v_frag = (lane & 31) * VLD + 8 * (lane >> 5);
 
   // Fragments in flight.  K fragment st of a unit = k-step st; V^T fragment f of a unit =
@@ -400,13 +420,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   auto step = [&](int u, const f32x16 (&sa)[2], f32x16 (&sb)[2], auto next_sw, auto cur_sw, auto kslot_c,
                   auto vbuf_c, auto&& hook) ARL2_INLINE {
     constexpr bool nx = decltype(next_sw)::value, cu = decltype(cur_sw)::value;
-    const unsigned char* kt = karr(kslot_c) + grp * KH_BYTES + k_frag;
+    const unsigned char* kt = karr(kslot_c) + grp * KH_BYTES;
     const f16* vt = reinterpret_cast<const f16*>(varr(vbuf_c) + grp * VT_BYTES) + v_frag + 32 * (u & 1);
     auto read_stage = [&](int s) ARL2_INLINE {
       if (s < NA) {
         if (nx)
 #pragma unroll
-          for (int f = s * FA; f < (s + 1) * FA; ++f) kfr[f] = *reinterpret_cast<const bf16x8*>(kt + f * 1024);
+          for (int f = s * FA; f < (s + 1) * FA; ++f) kfr[f] = *reinterpret_cast<const bf16x8*>(kt + k_fo[f]);
       } else if (s < NA + NB) {
         if (cu)
 #pragma unroll
@@ -504,7 +524,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     auto hook0 = [&](int st) ARL2_INLINE {
       if (st < NA) {
 #pragma unroll
-        for (int pl = st * KS / NA; pl < (st + 1) * KS / NA; ++pl) dma16(kr, kdst + pl * 1024, k_lane_off, pl * 32);
+        for (int pl = st * KS / NA; pl < (st + 1) * KS / NA; ++pl) dma_k(kr, kdst, pl);
       } else {
         if (st == NA) asm volatile("" ::: "memory");  // the K loads stay ahead of the V loads
         v_stage(Ic<P + 1>(), vr, 0, st - NA);

@@ -56,7 +56,7 @@ struct arl2_layer {
   float* partial = nullptr;          // [B][H][chunks][dp][dp]
   void* sneg_hi = nullptr;           // -S as B fragments, bf16 [B][H][d/16][dp/32][64][8]
   void* sneg_lo = nullptr;
-  void* wt_hi = nullptr;             // (phi_q S)^T, bf16 [B][H][dp][d]
+  void* wt_hi = nullptr;             // (phi_q S)^T, bf16 [B][H][d/16][dp][16] (k-step planes)
   void* wt_lo = nullptr;
   void* pq = nullptr;                // maps' working layouts, bf16 [H][dp][d]
   void* pkt = nullptr;

@@ -14,7 +14,8 @@ constexpr int kCommitChunk = 128;
 inline int commit_chunks(int T) { return (T + kCommitChunk - 1) / kCommitChunk; }
 
 // Per-pass output: out = softmax(Q K^T * scale) V + Q (phi_q S).  wt_hi / wt_lo hold
-// (phi_q S)^T split into two bf16 terms, layout [B][H][dp][d].
+// (phi_q S)^T split into two bf16 terms, layout [B][H][d / 16][dp][16]: W^T[j][i] at
+// [i / 16][j][i % 16] (k-step planes of the pass kernel's MFMA fragments).
 struct FwdArgs {
   const void* q;
   const void* k;
