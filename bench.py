@@ -311,20 +311,27 @@ def series(args):
     layer.close()
 
 
+COPY_BYTES = 2**30  # calibration copy: 1 GiB each way, four times the 256 MB last-level cache
+
+
 def pmc_target(args):
-    """A short, fixed run for counter passes: a plain copy of known size (the calibration of
-    FETCH_SIZE / WRITE_SIZE), then a few frames of the layer."""
+    """A short, fixed run for counter passes: a plain device-to-device copy of known size (the
+    calibration of FETCH_SIZE / WRITE_SIZE; before each copy another 1 GiB buffer is written,
+    so the source comes from HBM, not the last-level cache), then a few frames of the layer."""
     import torch
 
     from synth import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    n = 256 * 2**20 // 4
+    n = COPY_BYTES // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    evict = torch.empty_like(src)
     for _ in range(3):
+        evict.fill_(2.0)
         dst.copy_(src)
     torch.cuda.synchronize()
+    del evict
     layer = make_layer(w, torch)
     ring = stage_ring(w, torch)
     out = layer.new_output()
@@ -337,7 +344,7 @@ def pmc_target(args):
 def summarize_pmc(args):
     """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into HBM bytes
     per launch of the pass kernel, each scaled by the counter's reading for the plain copy
-    (256 MiB read + 256 MiB written).  Writes the JSON bench.py reads and a text summary."""
+    (1 GiB read + 1 GiB written).  Writes the JSON bench.py reads."""
     import csv
 
     def per_kernel(counter):
@@ -352,11 +359,12 @@ def summarize_pmc(args):
     res = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = per_kernel(counter)
-        copy = [v for k, v in rows if "elementwise" in k.lower() or "copy" in k.lower()]
+        # the runtime's device-to-device copy kernel; the calibration copies are its three largest
+        copy = sorted((v for k, v in rows if "copyBuffer" in k), reverse=True)[:3]
         fwd = [v for k, v in rows if FWD_KERNEL in k]
-        if not copy or not fwd:
+        if len(copy) < 3 or not fwd:
             sys.exit(f"{counter}: copy kernel or {FWD_KERNEL} not found in {args.summarize_pmc}")
-        expect_kib = 256 * 1024.0
+        expect_kib = COPY_BYTES / 1024.0
         factor = float(np.median(copy)) / expect_kib
         res[counter] = {"copy_kib_median": float(np.median(copy)), "scale": factor,
                         "fwd_kib_mean": float(np.mean(fwd)), "fwd_bytes": float(np.mean(fwd)) / factor * 1024,
