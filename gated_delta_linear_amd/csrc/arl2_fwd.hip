@@ -139,7 +139,7 @@ template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void arl2_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
-    int T, int H, int nq, int n_items, int per_xcd, float scale_log2) {
+    int T, int H, int nq, int n_bh, float scale_log2) {
   using S = FwdShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
                 KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB;
@@ -164,8 +164,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     else return vs1;
   };
 
-  // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin, so consecutive items
-  // (the query tiles of one head) are given to work-groups on the same XCD and share its L2.
+  // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin (work-group i runs on XCD
+  // i % 8), so each XCD gets a contiguous run of items (the query tiles of one head, then the
+  // next head's): a head's K and V come into one or two L2 caches, and every XCD gets the same
+  // number of work-groups.  (Dealing whole heads to XCDs saves the second L2 fill but leaves
+  // the XCDs unevenly loaded, which costs more.)
+  const int n_items = nq * n_bh, per_xcd = (n_items + 7) / 8;
   const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (item >= n_items) return;
   const int qt = item % nq, bh = item / nq;
@@ -653,9 +657,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const int nq = (a.T + kQTile - 1) / kQTile;
-  const int n_items = nq * a.H * a.B;
-  const int per_xcd = (n_items + 7) / 8;
-  dim3 grid(per_xcd * 8);
+  const int n_bh = a.H * a.B;
+  dim3 grid(8 * ((nq * n_bh + 7) / 8));
   const bf16* q = static_cast<const bf16*>(a.q);
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);
@@ -663,10 +666,10 @@ hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const bf16* wl = static_cast<const bf16*>(a.wt_lo);
   if (a.out_bf16)
     hipLaunchKernelGGL((arl2_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T,
-                       a.H, nq, n_items, per_xcd, a.scale_log2);
+                       a.H, nq, n_bh, a.scale_log2);
   else
     hipLaunchKernelGGL((arl2_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T,
-                       a.H, nq, n_items, per_xcd, a.scale_log2);
+                       a.H, nq, n_bh, a.scale_log2);
   return hipGetLastError();
 }
 

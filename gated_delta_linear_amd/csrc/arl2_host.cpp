@@ -193,6 +193,10 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   const int64_t slice_bytes = ((int64_t)c.tokens_per_frame + 256) * c.heads * c.head_dim * 2;
   if (slice_bytes >= (int64_t(1) << 31))
     return fail(ARL2_E_UNSUPPORTED, "one stream's frame (T x H x d bf16) must stay below 2 GiB");
+  // the pass kernel runs ceil(T / 128) x B x H work-groups (rounded up to 8) in one grid dimension
+  const int64_t pass_wgs = (((int64_t)c.tokens_per_frame + 127) / 128) * c.batch * c.heads + 7;
+  if (pass_wgs > (int64_t(1) << 24))
+    return fail(ARL2_E_UNSUPPORTED, "B x H x T too large for one launch (%lld work-groups)", (long long)pass_wgs);
   arl2_status st;
   if ((st = check_ptr(phi_q, "phi_q")) || (st = check_ptr(phi_k, "phi_k")) || (st = check_ptr(phi_v, "phi_v")))
     return st;

@@ -78,7 +78,8 @@ typedef struct {
   int32_t heads;            /* H, 1 <= H <= 65535 */
   int32_t head_dim;         /* d: 16, 64 or 128 */
   int32_t tokens_per_frame; /* T, 1 <= T <= ARL2_MAX_TOKENS (a chunk of frames counts as one frame);
-                               (T + 256) * H * d * 2 bytes must stay below 2 GiB */
+                               (T + 256) * H * d * 2 bytes must stay below 2 GiB, and
+                               ceil(T / 128) * B * H below 2^24 (ARL2_E_UNSUPPORTED) */
   int32_t io_dtype;         /* dtype of q, k, v and phi: ARL2_BF16 (the only one supported) */
   int32_t out_dtype;        /* ARL2_F32 (recommended) or ARL2_BF16 (round to nearest even) */
   float softmax_scale;      /* 0 selects 1/sqrt(d) */

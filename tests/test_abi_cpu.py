@@ -77,6 +77,10 @@ FAKE = 0x10000
     (dict(softmax_scale=-1.0), A.ARL2_E_INVALID_ARG),
     (dict(softmax_scale=float("nan")), A.ARL2_E_INVALID_ARG),
     (dict(knorm_eps=float("inf")), A.ARL2_E_INVALID_ARG),
+    # a stream's frame slice reaches 2 GiB
+    (dict(heads=8192, tokens_per_frame=1024), A.ARL2_E_UNSUPPORTED),
+    # the pass kernel's grid: ceil(T / 128) x B x H work-groups beyond 2^24
+    (dict(batch=65535, heads=64, tokens_per_frame=1024, head_dim=16), A.ARL2_E_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config(lib, kw, status):
     h = ctypes.c_void_p(123)
