@@ -337,16 +337,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
 
   // This lane's query rows (one per 32-row block) as B fragments of Q^T (k-step st = features
-  // 16 st .. 16 st + 15).
-  int qrow[2];
+  // 16 st .. 16 st + 15), read from LDS in the prologue.
   bf16x8 qf[2][KS];
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    qrow[qq] = qt * kQTile + qs * 64 + qq * 32 + (lane & 31);
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qf[qq][st] = qrow[qq] < T ? ld_bf16x8(qb + qrow[qq] * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
-  }
 
   f32x16 acc[2][MB];
 #pragma unroll
@@ -486,19 +478,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (nx) rescale_to(mp);
   };
 
-  // Prologue: K half-tiles 0, 1, 2 (ring slots 0-2), V tile 0 into LDS and tile 1 into
-  // registers; scores and max of unit 0.  The second barrier keeps the first iteration's
-  // loads into slot 0 behind every wave's read of unit 0.
+  // Prologue.  The work-group's query tile comes into V^T buffer 1 (unused until the first
+  // iteration stores into it) with the swizzled row-major loads of K, and K half-tiles 0-2 into
+  // ring slots 0-2; V tile 0 comes into registers.  The first barrier waits for the loads into
+  // LDS only; each wave then takes its Q fragments from LDS and computes the scores and max of
+  // unit 0, while V tile 0 arrives, goes to V^T buffer 0, and tile 1 comes into registers.
+  // The second barrier publishes V tile 0 and keeps the first iteration's loads into slot 0
+  // (and stores into buffer 1) behind every wave's reads.
+  {
+    const __amdgpu_buffer_rsrc_t qr = rows_rsrc(qb, T, rs, D, qt * kQTile);
+    constexpr int QI = kQTile / RPI;  // 1-KB loads of the query tile
+#pragma unroll
+    for (int c = 0; c < (QI + 3) / 4; ++c)
+      if (wave + 4 * c < QI) dma_k(qr, vs1, wave + 4 * c);
+  }
   load_k_half(sw, sw ? ks1 : ks0);
   if (sw == 0) load_k_half(2, ks2);
+  asm volatile("" ::: "memory");  // the V loads stay behind the loads into LDS
+  __builtin_amdgcn_sched_barrier(0);
   load_v(0);
-  wait_vmem();
-  store_v(Ic<0>());
-  if (iters > 1) load_v(1);
+  wait_vmem_but<4 * VPT>();
   __syncthreads();
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qf[qq][st] = *reinterpret_cast<const bf16x8*>(vs1 + (qs * 64 + qq * 32) * RB + k_fo[st]);
   f32x16 s0[2], s1[2];
   auto no_staging = [](int) ARL2_INLINE {};
   step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
+  store_v(Ic<0>());
+  if (iters > 1) load_v(1);
+  if (D < DP) {  // the query tile overlapped padded V^T rows of buffer 1, which stay zero
+    __syncthreads();
+    for (int i = tid; i < VA_BYTES / 16; i += kThreads) reinterpret_cast<uint4*>(vs1)[i] = make_uint4(0, 0, 0, 0);
+  }
   __syncthreads();
 
   // Iteration j (parity P = j % 2, a compile-time constant): units 2j and 2j + 1 (tile j of
@@ -555,41 +569,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // [g * MBH, (g + 1) * MBH) (for d < 64 key half 0 finalises the single block).
   load_w();
   constexpr int MBH = MB >= 2 ? MB / 2 : 1;
-  constexpr int NXR = 2 * MBH * 16 + 4;  // exported rows: accumulator blocks, then 2 max, 2 sums
-  constexpr int NX = MB >= 2 ? 4 : 2;    // exporting waves
-  constexpr int XS_BYTES = NXR * 64 * 4, XS_PER = VA_BYTES / XS_BYTES;  // exchange slots per V array
+  constexpr int NXV = 2 * MBH * 4 + 1;  // exported 16-byte rows: accumulator quads, then (m0, m1, l0, l1)
+  constexpr int NX = MB >= 2 ? 4 : 2;   // exporting waves
+  constexpr int XS_BYTES = NXV * 64 * 16, XS_PER = VA_BYTES / XS_BYTES;  // exchange slots per V array
   static_assert(XS_PER >= 1 && (NX + XS_PER - 1) / XS_PER <= 2, "exchange must fit in the V arrays");
   static_assert(W_INSTR <= 4 * KA_KB, "W must fit in the K arrays");
   const int partner = wave ^ 2;
   const bool owner = MB >= 2 || grp == 0;
   const bool partner_owns = MB >= 2 || grp == 1;
-  auto xslot = [&](int w) ARL2_INLINE {  // [NXR][64] floats of exporter w
+  auto xslot = [&](int w) ARL2_INLINE {  // [NXV][64] f32x4 of exporter w
     const int xs = MB >= 2 ? w : (w & 1);
-    return reinterpret_cast<float*>((xs / XS_PER ? vs1 : vs0) + (xs % XS_PER) * XS_BYTES);
+    return reinterpret_cast<f32x4*>((xs / XS_PER ? vs1 : vs0) + (xs % XS_PER) * XS_BYTES);
   };
   if (partner_owns) {
-    float* xo = xslot(wave);
+    f32x4* xo = xslot(wave);
     const int p0 = MB >= 2 ? (1 - grp) * MBH : 0;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         if (mb >= p0 && mb < p0 + MBH)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) xo[((qq * MBH + mb - p0) * 16 + i) * 64 + lane] = acc[qq][mb][i];
-      xo[(2 * MBH * 16 + qq) * 64 + lane] = m_run[qq];
-      xo[(2 * MBH * 16 + 2 + qq) * 64 + lane] = l_run[qq];
-    }
+          for (int g = 0; g < 4; ++g)
+            xo[((qq * MBH + mb - p0) * 4 + g) * 64 + lane] =
+                f32x4{acc[qq][mb][4 * g], acc[qq][mb][4 * g + 1], acc[qq][mb][4 * g + 2], acc[qq][mb][4 * g + 3]};
+    xo[(NXV - 1) * 64 + lane] = f32x4{m_run[0], m_run[1], l_run[0], l_run[1]};
   }
   __syncthreads();
 
-  const float* xi = xslot(partner);
+  const f32x4* xi = xslot(partner);
   const int o0 = MB >= 2 ? grp * MBH : 0;
   if (owner) {
     float a0[2], a1[2];
+    const f32x4 ml = xi[(NXV - 1) * 64 + lane];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
-      const float m1 = xi[(2 * MBH * 16 + qq) * 64 + lane], l1 = xi[(2 * MBH * 16 + 2 + qq) * 64 + lane];
+      const float m1 = ml[qq], l1 = ml[2 + qq];
       const float m = fmaxf(m_run[qq], m1);
       const float e0 = __builtin_amdgcn_exp2f((m_run[qq] - m) * scale_log2);
       const float e1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
@@ -604,8 +619,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc[qq][mb][i] = acc[qq][mb][i] * a0[qq] + xi[((qq * MBH + mb - o0) * 16 + i) * 64 + lane] * a1[qq];
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = xi[((qq * MBH + mb - o0) * 4 + g) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[qq][mb][4 * g + e] = acc[qq][mb][4 * g + e] * a0[qq] + x[e] * a1[qq];
+        }
     }
   }
   wait_vmem();  // W^T has landed (every wave waits for its own loads, then the barrier)
@@ -626,29 +644,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
   }
 
+  // Output.  The wave's 64 rows x OWN_D finished features go through LDS (the V arrays, free
+  // since the barrier) into row-major order, 16-byte chunks of row r at granule
+  // chunk ^ (r % OC), so that each store instruction writes whole row segments.
+  constexpr int OWN_D = D < 32 * MBH ? D : 32 * MBH;  // features this wave finalises
+  constexpr int OC = OWN_D / 4, ORB = 16 * OC, RPS = 64 / OC;  // chunks per row, row bytes, rows per store
+  static_assert(2 * 64 * ORB <= VA_BYTES, "output staging must fit in the V arrays");
+  unsigned char* ost = (wave >> 1 ? vs1 : vs0) + (wave & 1) * 64 * ORB;
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    if (qrow[qq] >= T) continue;
+  for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb < o0 || mb >= o0 + MBH) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * mb + 8 * g + 4 * (lane >> 5);
-        if (d < D) {
-          const int64_t o = base + qrow[qq] * rs + d;
-          if (OUT_BF16) {
-            bf16x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (bf16)acc[qq][mb][4 * g + e];
-            *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o) = w;
-          } else {
-            f32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = acc[qq][mb][4 * g + e];
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = w;
-          }
+        const int ld = 32 * (mb - o0) + 8 * g + 4 * (lane >> 5);
+        if (ld < OWN_D) {
+          const int r = qq * 32 + (lane & 31), c = ld >> 2;
+          *reinterpret_cast<f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC))) =
+              f32x4{acc[qq][mb][4 * g], acc[qq][mb][4 * g + 1], acc[qq][mb][4 * g + 2], acc[qq][mb][4 * g + 3]};
         }
+      }
+    }
+  const int row0 = qt * kQTile + qs * 64;
+#pragma unroll
+  for (int i = 0; i < OC; ++i) {
+    const int r = RPS * i + lane / OC, c = lane % OC;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC)));
+    if (row0 + r < T) {
+      const int64_t o = base + (int64_t)(row0 + r) * rs + 32 * o0 + 4 * c;
+      if (OUT_BF16) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)x[e];
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = x;
       }
     }
   }
