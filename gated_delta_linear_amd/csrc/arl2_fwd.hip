@@ -6,13 +6,15 @@
 // associativity; W is formed once per frame by the state-write kernels, so a pass only
 // adds a Q x W product to the attention accumulator.
 //
-// Work decomposition.  One work-group of 4 waves (one per SIMD) per (stream, head,
-// 128-query tile).  Wave w owns 64 query rows (w % 2) and one half of the frame's keys
-// (w / 2); the two halves of a row block are merged through LDS at the end (max / sum
-// rescaling), so no partial result leaves the chip.  A wave holds two 32-row MFMA blocks,
-// so every K or V fragment it reads from LDS feeds two MFMAs: LDS traffic is 64 bytes per
-// clock and CU at the full MFMA rate, half of what 32-row waves would need.  With one wave
-// per SIMD the wave has the whole register file (the output accumulators live in AGPRs).
+// Work decomposition.  One work-group of 8 waves, two per SIMD, per (stream, head, 128-query
+// tile).  Wave w owns the 32 query rows w % 4 of the tile and one half of the frame's keys
+// (w / 4); the two halves of a row block are merged through LDS at the end (max / sum
+// rescaling), so no partial result leaves the chip.  The two waves on a SIMD work on
+// different key halves with no ordering between them inside an iteration, so the matrix
+// cores run one wave's MFMAs while the vector ALU runs the other's softmax: the overlap
+// that one wave cannot get from its own in-order instruction stream.  Every K or V fragment
+// a wave reads from LDS feeds one MFMA; at the full MFMA rate the CU reads 128 bytes per
+// clock, half of what gfx950's LDS delivers.  The four waves of a key half share its staging.
 //
 // Pipeline.  A wave walks its keys in units of 32.  Step u overlaps the score MFMAs of unit
 // u+1 (S^T = K Q^T) with the VALU softmax of unit u (phase A), then the O^T += V^T P^T MFMAs
@@ -34,13 +36,14 @@
 // so they show up instead of being clipped).  Q K^T and the Q W term stay bf16 x bf16 with
 // fp32 accumulation.
 //
-// Scores are transposed so that every lane holds one query row per block and 16 of the
-// unit's keys: the row max needs one cross-lane exchange (l, l ^ 32), the row sum none
-// until the end, and rescaling the transposed accumulator is a per-lane multiply.
-// Softmax: exp2 with the scale folded in; the running max is only raised when a unit's max
-// exceeds it by more than 8 (in log2 units) in some lane of the wave, so P stays below 2^8
-// and the rescale of the accumulator is skipped on almost every unit.  Row sums use dot2 on
-// the rounded P that enters the MFMA.
+// Scores are transposed so that every lane holds one query row and 16 of the unit's keys:
+// the row max needs one cross-lane exchange (l, l ^ 32), the row sum none until the end,
+// and rescaling the transposed accumulator is a per-lane multiply.  Softmax: exp2 with the
+// scale folded in; the running max is only raised when a unit's max exceeds it by more than
+// 8 (in log2 units) in some lane of the wave, so P stays below 2^8 and the rescale of the
+// accumulator is skipped on almost every unit.  Row sums add the rounded P that enters the
+// MFMA in fp16 pairs within a unit (at most 16 terms of at most 2^8, relative rounding 2^-11
+// per add) and in fp32 across units.
 #include <type_traits>
 
 #include "arl2_device.h"
@@ -52,8 +55,10 @@ namespace {
 constexpr int kQTile = 128;  // query rows per work-group
 constexpr int kKV = 64;      // keys per staging iteration (two units)
 constexpr int kUnit = 32;    // keys per pipeline unit
-constexpr int kThreads = 256;
-constexpr float kRescaleSlack = 8.f;  // log2 headroom before the running max is raised
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHalfThreads = kThreads / 2;  // staging threads of one key half (its four waves)
+constexpr float kRescaleSlack = 8.f;        // log2 headroom before the running max is raised
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -74,7 +79,7 @@ struct FwdShape {
   static constexpr int MB = DP / 32;         // 32-row blocks over output features
   static constexpr int CPR = D / 8;          // 16-byte chunks per token row
   static constexpr int VBLK = 16 * CPR;      // 4-key x 8-feature blocks per V tile
-  static constexpr int VPT = (VBLK + 127) / 128;  // such blocks per staging thread (128 per key half)
+  static constexpr int VPT = (VBLK + kHalfThreads - 1) / kHalfThreads;  // such blocks per staging thread
   static constexpr int VLD = kKV + 8;        // V^T row stride in fp16 (64 keys + 16 bytes of padding)
   // K half-tile: 32 rows of 2D bytes, row-major, with the 16-byte granules of row r permuted
   // (granule g holds feature chunk g ^ (r mod CPR)).  Every direct-to-LDS load then brings
@@ -89,6 +94,7 @@ struct FwdShape {
   static constexpr int NB = 2 * MB < 4 ? 2 * MB : 4;  // stages of phase B
   static constexpr int FA = KS / NA;                  // K fragments per A stage
   static constexpr int FB = 2 * MB / NB;              // V^T fragments per B stage
+  static constexpr int KPW = (2 * KS + 3) / 4;        // K half-tile loads per wave per iteration
 };
 
 // Buffer resource over rows [first_row, T) of one (stream, head) slice of a [B][T][H][d]
@@ -112,9 +118,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-// Pins a value to the architectural VGPRs at this point.  MFMA results land in AGPRs; a
-// score block that the VALU is about to read moves over once, here, so that the AGPRs hold
-// only the blocks still being accumulated.
+// Pins a value to the architectural VGPRs at this point.  MFMA results may land in AGPRs; a
+// score block that the VALU is about to read moves over once, here.
 __device__ __forceinline__ void to_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // Marks a value as produced at this point, so that the compiler does not sink its computation
@@ -136,13 +141,14 @@ __device__ __forceinline__ void wait_vmem_but() {
 }
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void arl2_fwd_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
     int T, int H, int nq, int n_bh, float scale_log2) {
   using S = FwdShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
-                KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB;
+                KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB,
+                KPW = S::KPW;
 
   // LDS: the four K ring slots and the two V^T buffers are separate arrays ([key half][...]
   // each), addressed with compile-time slot numbers (the steady loop is unrolled by iteration
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // descriptors and LDS bases built from them need no per-lane handling
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qs = wave & 1, grp = wave >> 1;  // row block of 64 and key half of this wave
+  const int rb = wave & 3, grp = wave >> 2;  // 32-row block and key half of this wave
   const int64_t rs = (int64_t)H * D;
   const int64_t base = ((int64_t)b * T * H + h) * D;
   const bf16* qb = q + base;
@@ -188,14 +194,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   const int ntiles = (T + kKV - 1) / kKV;
   const int nt0 = (ntiles + 1) >> 1;  // key half 0: tiles [0, nt0); key half 1: [nt0, ntiles)
-  const int my_first = grp ? nt0 : 0, my_count = grp ? ntiles - nt0 : nt0;
   const int iters = nt0;
-  const int key0 = my_first * kKV;  // first key of this wave's half
+  const int key0 = (grp ? nt0 : 0) * kKV;  // first key of this wave's half
   // end of this wave's keys: every iteration runs all its units, and units past the end (the
   // second half's last iteration when it has one tile fewer, the unit after each half's last)
   // are masked to -inf, so they add nothing
   const int key_end = grp ? T : min(T, nt0 * kKV);
-  (void)my_count;
 
   if (D < DP) {  // padded V^T rows stay zero for the whole kernel
     for (int i = tid; i < VA_BYTES / 16; i += kThreads) {
@@ -205,8 +209,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __syncthreads();
   }
 
-  // Staging: the two waves of a key half stage its keys (wave sw of the pair: 128 threads).
-  const int st_t = tid & 127, sw = qs;
+  // Staging: the four waves of a key half stage its keys (wave sw of the four: 256 threads).
+  const int st_t = tid & (kHalfThreads - 1), sw = rb;
   // K half-tile u (keys key0 + 32 u ..): KS direct-to-LDS loads; load i brings rows RPI i ..
   // RPI i + RPI - 1, lane l the granule l % CPR of row RPI i + l / CPR, i.e. feature chunk
   // (l % CPR) ^ (row % CPR).  The lane offset repeats every NKV loads.
@@ -219,12 +223,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   auto dma_k = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int i) ARL2_INLINE {
     dma16(r, dst + i * 1024, k_vo[i % NKV], (int)(RPI * i * rs * 2));
-  };
-  auto load_k_half = [&](int u, unsigned char* slot) ARL2_INLINE {  // slot: the ring slot's array
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, T, rs, D, key0 + kUnit * u);
-    unsigned char* dst = slot + grp * KH_BYTES;
-#pragma unroll
-    for (int i = 0; i < KS; ++i) dma_k(r, dst, i);
   };
   // K fragment of k-step st (row lane % 32, feature chunk 2 st + lane / 32) within a half-tile.
   int k_fo[KS];
@@ -243,7 +241,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   bool v_mine[VPT];
 #pragma unroll
   for (int r = 0; r < VPT; ++r) {
-    const int blk = st_t + 128 * r;
+    const int blk = st_t + kHalfThreads * r;
     v_mine[r] = blk < VBLK;
     const int bb = v_mine[r] ? blk : 0;
     const int va = bb & 15, vbb = bb >> 4;
@@ -269,6 +267,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                 {vreg[rr][1].x, vreg[rr][1].y, vreg[rr][1].z, vreg[rr][1].w},
                                 {vreg[rr][2].x, vreg[rr][2].y, vreg[rr][2].z, vreg[rr][2].w},
                                 {vreg[rr][3].x, vreg[rr][3].y, vreg[rr][3].z, vreg[rr][3].w}};
+      // word i of key kk holds features 2i (low half) and 2i + 1 (high half) as bf16; a bf16 is
+      // the upper half of the fp32 with the same value
       auto feat = [&](int kk, int i, int odd) ARL2_INLINE {
         return __uint_as_float(odd ? (w[kk][i] & 0xFFFF0000u) : (w[kk][i] << 16));
       };
@@ -289,28 +289,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   };
   auto store_v = [&](auto buf_c) ARL2_INLINE {
 #pragma unroll
-    for (int rr = 0; rr < VPT; ++rr) {
-      if (!v_mine[rr]) continue;
-      f16* vrow = reinterpret_cast<f16*>(varr(buf_c) + grp * VT_BYTES) + v_dst[rr];
-      const unsigned w[4][4] = {{vreg[rr][0].x, vreg[rr][0].y, vreg[rr][0].z, vreg[rr][0].w},
-                                {vreg[rr][1].x, vreg[rr][1].y, vreg[rr][1].z, vreg[rr][1].w},
-                                {vreg[rr][2].x, vreg[rr][2].y, vreg[rr][2].z, vreg[rr][2].w},
-                                {vreg[rr][3].x, vreg[rr][3].y, vreg[rr][3].z, vreg[rr][3].w}};
-      // word i of key kk holds features 2i (low half) and 2i + 1 (high half) as bf16; a bf16 is
-      // the upper half of the fp32 with the same value
-      auto feat = [&](int kk, int i, int odd) ARL2_INLINE {
-        return __uint_as_float(odd ? (w[kk][i] & 0xFFFF0000u) : (w[kk][i] << 16));
-      };
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int odd = 0; odd < 2; ++odd) {
-          const f16x2 k01 = __builtin_convertvector((f32x2{feat(0, i, odd), feat(1, i, odd)}), f16x2);
-          const f16x2 k23 = __builtin_convertvector((f32x2{feat(2, i, odd), feat(3, i, odd)}), f16x2);
-          *reinterpret_cast<uint2*>(vrow + (2 * i + odd) * VLD) =
-              make_uint2(__builtin_bit_cast(unsigned, k01), __builtin_bit_cast(unsigned, k23));
-        }
-    }
+    for (int rr = 0; rr < VPT; ++rr) store_v_part(buf_c, rr, 0, 4);
   };
   // W^T = (phi_q S)^T, hi then lo, into the K arrays after the loop, as planes of DP rows x 32
   // bytes: plane (hl, st) holds features 16 st .. 16 st + 15 of every output feature.  Its
@@ -327,8 +306,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(wt_lo + wbase), (short)0,
                                                                         DP * D * 2, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < (W_INSTR + 3) / 4; ++c) {
-      const int i = wave + 4 * c;  // kilobyte i: plane i / (DP / 32), 32-row block i % (DP / 32)
+    for (int c = 0; c < (W_INSTR + kWaves - 1) / kWaves; ++c) {
+      const int i = wave + kWaves * c;  // kilobyte i: plane i / (DP / 32), 32-row block i % (DP / 32)
       if (i < W_INSTR) {
         const int hl = i / (W_INSTR / 2), kb_in = i % (W_INSTR / 2);
         dma16(hl ? rl : rh, w_kb(i), 16 * lane, kb_in * 1024);
@@ -336,17 +315,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  // This lane's query rows (one per 32-row block) as B fragments of Q^T (k-step st = features
-  // 16 st .. 16 st + 15), read from LDS in the prologue.
-  bf16x8 qf[2][KS];
+  // This lane's query row as B fragments of Q^T (k-step st = features 16 st .. 16 st + 15),
+  // read from LDS in the prologue.
+  bf16x8 qf[KS];
 
-  f32x16 acc[2][MB];
+  f32x16 acc[MB];
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[qq][mb] = zero16();
-  float m_run[2] = {-INFINITY, -INFINITY};  // running max (raw score units), equal in lanes l and l ^ 32
-  float l_run[2] = {0.f, 0.f};              // this lane's share of the running sum
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
+  float m_run = -INFINITY;  // running max (raw score units), equal in lanes l and l ^ 32
+  float l_run = 0.f;        // this lane's share of the running sum
 
   // Fragment offsets of this lane inside a K plane and a V^T tile.
   const int k_frag = (lane & 31) * 32 + (lane >> 5) * 16;  // W^T planes: 32-byte rows
@@ -356,53 +333,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // k-step f / MB of the unit (16 keys), feature block f % MB.
   bf16x8 kfr[KS];
   f16x8 vfr[2 * MB];
-  const f16x2 ones = {(f16)1.f, (f16)1.f};
 
-  // Softmax chunk c of a unit: row block c / 2, keys of k-step c % 2 (registers 8 (c % 2) ..
-  // + 7 of the score block), into the fp16 P^T fragment pf[c / 2][c % 2] and the row sum (of
-  // the rounded P that enters the MFMA).
-  auto softmax_chunk = [&](const f32x16 (&sa)[2], f16x8 (&pf)[2][2], int c, const float (&mc)[2]) ARL2_INLINE {
-    const int qq = c >> 1, hh = c & 1;
+  // Softmax of score registers [v0, v1) of a unit (v1 - v0 a multiple of 4) into the fp16 P^T
+  // fragments pf[k-step] (register i of the score block is register i % 8 of fragment i / 8)
+  // and the unit's row sum lsum (fp16 pairs of the rounded P that enters the MFMA).
+  auto softmax_part = [&](const f32x16& sa, f16x8 (&pf)[2], int v0, int v1, float mc, f16x2& lsum) ARL2_INLINE {
 #pragma unroll
-    for (int jj = 0; jj < 8; jj += 2) {
-      const f32x2 e = {__builtin_amdgcn_exp2f(fmaf(sa[qq][8 * hh + jj], scale_log2, -mc[qq])),
-                       __builtin_amdgcn_exp2f(fmaf(sa[qq][8 * hh + jj + 1], scale_log2, -mc[qq]))};
-      const f16x2 p2 = __builtin_convertvector(e, f16x2);
-      pf[qq][hh][jj] = p2[0];
-      pf[qq][hh][jj + 1] = p2[1];
-      l_run[qq] = __builtin_amdgcn_fdot2(p2, ones, l_run[qq], false);
+    for (int jj = v0; jj < v1; jj += 4) {
+      f16x2 p[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = jj + 2 * e;
+        const f32x2 x = {__builtin_amdgcn_exp2f(fmaf(sa[i], scale_log2, -mc)),
+                         __builtin_amdgcn_exp2f(fmaf(sa[i + 1], scale_log2, -mc))};
+        p[e] = __builtin_convertvector(x, f16x2);
+        pf[i >> 3][i & 7] = p[e][0];
+        pf[i >> 3][(i & 7) + 1] = p[e][1];
+      }
+      lsum += p[0] + p[1];
     }
-    pin(pf[qq][hh]);
-    pin(l_run[qq]);
+    pin(pf[v0 >> 3]);
+    pin(lsum);
   };
   // Keys of unit u past the end of this wave's keys do not take part.
-  auto mask_unit = [&](int u, f32x16 (&sc)[2]) ARL2_INLINE {
+  auto mask_unit = [&](int u, f32x16& sc) ARL2_INLINE {
     const int k0 = key0 + kUnit * u;
     if (k0 + kUnit > key_end) {
       const int lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + c_row(i, lid) >= key_end) sc[qq][i] = -INFINITY;
+      for (int i = 0; i < 16; ++i)
+        if (k0 + c_row(i, lid) >= key_end) sc[i] = -INFINITY;
     }
   };
   // Raise the running max to a unit's max when it exceeds it by more than the slack in some
   // lane of the wave (the accumulator and sum are rescaled); otherwise keep it, so P <= 2^8.
-  auto rescale_to = [&](const float (&mp)[2]) ARL2_INLINE {
+  auto rescale_to = [&](float mp) ARL2_INLINE {
+    const float mx = fmaxf(mp, other_half(mp, lane));  // lanes l and l ^ 32 hold one row
+    if (__builtin_amdgcn_ballot_w64((mx - m_run) * scale_log2 > kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      m_run = m_new;
+      l_run *= corr;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const float mx = fmaxf(mp[qq], other_half(mp[qq], lane));  // lanes l and l ^ 32 hold one row
-      if (__builtin_amdgcn_ballot_w64((mx - m_run[qq]) * scale_log2 > kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run[qq], mx);
-        const float corr = __builtin_amdgcn_exp2f((m_run[qq] - m_new) * scale_log2);
-        m_run[qq] = m_new;
-        l_run[qq] *= corr;
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[qq][mb][i] *= corr;
-      }
+        for (int i = 0; i < 16; ++i) acc[mb][i] *= corr;
     }
   };
 
@@ -413,8 +388,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // of stage s + 2.
   // kslot_c / vbuf_c: compile-time ring slot of unit u + 1 and V^T buffer of unit u.
   // hook(s) issues the staging work of stage s (A stages 0 .. NA - 1, then B stages) first.
-  auto step = [&](int u, const f32x16 (&sa)[2], f32x16 (&sb)[2], auto next_sw, auto cur_sw, auto kslot_c,
-                  auto vbuf_c, auto&& hook) ARL2_INLINE {
+  auto step = [&](int u, const f32x16& sa, f32x16& sb, auto next_sw, auto cur_sw, auto kslot_c, auto vbuf_c,
+                  auto&& hook) ARL2_INLINE {
     constexpr bool nx = decltype(next_sw)::value, cu = decltype(cur_sw)::value;
     const unsigned char* kt = karr(kslot_c) + grp * KH_BYTES;
     const f16* vt = reinterpret_cast<const f16*>(varr(vbuf_c) + grp * VT_BYTES) + v_frag + 32 * (u & 1);
@@ -431,80 +406,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     };
     // (a half without keys keeps m = -inf; its P must come out 0, not NaN)
-    const float mc[2] = {m_run[0] == -INFINITY ? 0.f : m_run[0] * scale_log2,
-                         m_run[1] == -INFINITY ? 0.f : m_run[1] * scale_log2};
-    f16x8 pf[2][2];
+    const float mc = m_run == -INFINITY ? 0.f : m_run * scale_log2;
+    f16x8 pf[2];
+    f16x2 lsum = {(f16)0.f, (f16)0.f};
     read_stage(0);
     read_stage(1);
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
       hook(t);
       read_stage(t + 2);
-      if (cu)
-#pragma unroll
-        for (int c = t * 4 / NA; c < (t + 1) * 4 / NA; ++c) softmax_chunk(sa, pf, c, mc);
+      if (cu) softmax_part(sa, pf, t * 16 / NA, (t + 1) * 16 / NA, mc, lsum);
       if (nx)
 #pragma unroll
-        for (int f = t * FA; f < (t + 1) * FA; ++f)
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) sb[qq] = mfma32(kfr[f], qf[qq][f], f ? sb[qq] : zero16());
+        for (int f = t * FA; f < (t + 1) * FA; ++f) sb = mfma32(kfr[f], qf[f], f ? sb : zero16());
       __builtin_amdgcn_sched_barrier(0);
     }
-    float mp[2] = {-INFINITY, -INFINITY};
+    if (cu) l_run += (float)lsum[0] + (float)lsum[1];
+    float mp = -INFINITY;
     if (nx) {
       mask_unit(u + 1, sb);
-      to_vgpr(sb[0]);
-      to_vgpr(sb[1]);
+      to_vgpr(sb);
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       hook(NA + t);
       read_stage(NA + t + 2);
-      if (nx)
+      if (nx) {
 #pragma unroll
-        for (int c = t * 4 / NB; c < (t + 1) * 4 / NB; ++c) {
-          const int qq = c >> 1, i0 = 8 * (c & 1);
-#pragma unroll
-          for (int i = i0; i < i0 + 8; ++i) mp[qq] = fmaxf(mp[qq], sb[qq][i]);
-          pin(mp[qq]);
-        }
+        for (int i = t * 16 / NB; i < (t + 1) * 16 / NB; ++i) mp = fmaxf(mp, sb[i]);
+        pin(mp);
+      }
       if (cu)
 #pragma unroll
-        for (int f = t * FB; f < (t + 1) * FB; ++f)
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) acc[qq][f % MB] = mfma32(vfr[f], pf[qq][f / MB], acc[qq][f % MB]);
+        for (int f = t * FB; f < (t + 1) * FB; ++f) acc[f % MB] = mfma32(vfr[f], pf[f / MB], acc[f % MB]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (nx) rescale_to(mp);
   };
 
   // Prologue.  The work-group's query tile comes into V^T buffer 1 (unused until the first
-  // iteration stores into it) with the swizzled row-major loads of K, and K half-tiles 0-2 into
-  // ring slots 0-2; V tile 0 comes into registers.  The first barrier waits for the loads into
-  // LDS only; each wave then takes its Q fragments from LDS and computes the scores and max of
-  // unit 0, while V tile 0 arrives, goes to V^T buffer 0, and tile 1 comes into registers.
-  // The second barrier publishes V tile 0 and keeps the first iteration's loads into slot 0
-  // (and stores into buffer 1) behind every wave's reads.
+  // iteration stores into it) with the swizzled row-major loads of K, and each key half's K
+  // half-tiles 0-2 into its ring slots 0-2; V tile 0 comes into registers.  The first barrier
+  // waits for the loads into LDS only; each wave then takes its Q fragments from LDS and
+  // computes the scores and max of unit 0, while V tile 0 arrives, goes to V^T buffer 0, and
+  // tile 1 comes into registers.  The second barrier publishes V tile 0 and keeps the first
+  // iteration's loads into slot 0 (and stores into buffer 1) behind every wave's reads.
   {
     const __amdgpu_buffer_rsrc_t qr = rows_rsrc(qb, T, rs, D, qt * kQTile);
     constexpr int QI = kQTile / RPI;  // 1-KB loads of the query tile
 #pragma unroll
-    for (int c = 0; c < (QI + 3) / 4; ++c)
-      if (wave + 4 * c < QI) dma_k(qr, vs1, wave + 4 * c);
+    for (int c = 0; c < (QI + kWaves - 1) / kWaves; ++c)
+      if (wave + kWaves * c < QI) dma_k(qr, vs1, wave + kWaves * c);
+    constexpr int NKI = 3 * KS;  // loads of this key half's K half-tiles 0-2
+#pragma unroll
+    for (int m = 0; m < (NKI + 3) / 4; ++m) {
+      const int i = sw + 4 * m;
+      if (i < NKI) {
+        const int hh = i / KS;
+        const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, T, rs, D, key0 + kUnit * hh);
+        dma_k(r, (hh == 0 ? ks0 : hh == 1 ? ks1 : ks2) + grp * KH_BYTES, i % KS);
+      }
+    }
   }
-  load_k_half(sw, sw ? ks1 : ks0);
-  if (sw == 0) load_k_half(2, ks2);
   asm volatile("" ::: "memory");  // the V loads stay behind the loads into LDS
   __builtin_amdgcn_sched_barrier(0);
   load_v(0);
   wait_vmem_but<4 * VPT>();
   __syncthreads();
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qf[qq][st] = *reinterpret_cast<const bf16x8*>(vs1 + (qs * 64 + qq * 32) * RB + k_fo[st]);
-  f32x16 s0[2], s1[2];
+  for (int st = 0; st < KS; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(vs1 + rb * 32 * RB + k_fo[st]);
+  f32x16 s0, s1;
   auto no_staging = [](int) ARL2_INLINE {};
   step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
   store_v(Ic<0>());
@@ -516,40 +487,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __syncthreads();
 
   // Iteration j (parity P = j % 2, a compile-time constant): units 2j and 2j + 1 (tile j of
-  // this key half).  Staging, spread over the stages so that the vector-memory path (shared by
-  // the CU's four waves) drains while the MFMAs run: K half-tile 2j + 3 + (wave of the pair)
-  // into the ring slot that held 2j - 1 or 2j (one plane per A stage of step 2j); V tile j + 1
-  // block by block from registers into the buffer that held tile j - 1, each block's registers
-  // then reloaded with tile j + 2 (block 0 in the B stages of step 2j, block 1 in those of step
-  // 2j + 1).  All K loads precede all V loads, so waiting for all but the V loads before the
-  // barrier leaves the K loads complete and the V loads in flight until their use.  Staging
-  // past the last tile reads zeros (outside the buffer descriptors) into slots and buffers
-  // that nothing reads again.
-  constexpr int SPLIT = NB >= 4 ? 2 : 1;  // B stages per store / per load of a block
-  auto v_stage = [&](auto buf_c, __amdgpu_buffer_rsrc_t vr, int rr, int b) ARL2_INLINE {
-    if (b < SPLIT) {
-      store_v_part(buf_c, rr, 4 * b / SPLIT, 4 * (b + 1) / SPLIT);
-    } else if (b < 2 * SPLIT) {
-      const int bb = b - SPLIT;
-      load_v_part(vr, rr, 4 * bb / SPLIT, 4 * (bb + 1) / SPLIT);
-    }
-  };
+  // this key half).  Staging, spread over the stages so that the vector-memory path drains
+  // while the MFMAs run: K half-tiles 2j + 3 and 2j + 4 into the ring slots that held 2j - 1
+  // and 2j (the 2 KS loads dealt over the four waves of the half, in the A stages of step
+  // 2j); V tile j + 1 from registers into the buffer that held tile j - 1 (B stages of step
+  // 2j), then the registers reloaded with tile j + 2 (B stages of step 2j + 1).  All K loads
+  // precede the V loads, so waiting for all but the V loads before the barrier leaves the K
+  // loads complete and the V loads in flight until their use.  Staging past the last tile
+  // reads zeros (outside the buffer descriptors) into slots and buffers that nothing reads
+  // again.
   auto iteration = [&](int j, auto par_c) ARL2_INLINE {
     constexpr int P = decltype(par_c)::value;
-    unsigned char* kdst = (sw ? karr(Ic<2 * P + 4>()) : karr(Ic<2 * P + 3>())) + grp * KH_BYTES;
-    const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 3 + sw));
+    unsigned char* kd0 = karr(Ic<2 * P + 3>()) + grp * KH_BYTES;
+    unsigned char* kd1 = karr(Ic<2 * P + 4>()) + grp * KH_BYTES;
+    const __amdgpu_buffer_rsrc_t kr0 = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 3));
+    const __amdgpu_buffer_rsrc_t kr1 = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 4));
     const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vb, T, rs, D, key0 + kKV * (j + 2));
     auto hook0 = [&](int st) ARL2_INLINE {
       if (st < NA) {
 #pragma unroll
-        for (int pl = st * KS / NA; pl < (st + 1) * KS / NA; ++pl) dma_k(kr, kdst, pl);
+        for (int m = st * KPW / NA; m < (st + 1) * KPW / NA; ++m) {
+          const int i = sw + 4 * m;
+          if (i < KS) dma_k(kr0, kd0, i);
+          else if (i < 2 * KS) dma_k(kr1, kd1, i - KS);
+        }
       } else {
-        if (st == NA) asm volatile("" ::: "memory");  // the K loads stay ahead of the V loads
-        v_stage(Ic<P + 1>(), vr, 0, st - NA);
+        const int bs = st - NA;
+#pragma unroll
+        for (int rr = 0; rr < VPT; ++rr) store_v_part(Ic<P + 1>(), rr, 4 * bs / NB, 4 * (bs + 1) / NB);
       }
     };
     auto hook1 = [&](int st) ARL2_INLINE {
-      if (VPT > 1 && st >= NA) v_stage(Ic<P + 1>(), vr, VPT - 1, st - NA);
+      if (st >= NA) {
+        if (st == NA) asm volatile("" ::: "memory");  // the V loads stay behind the K loads
+        const int bs = st - NA;
+#pragma unroll
+        for (int rr = 0; rr < VPT; ++rr) load_v_part(vr, rr, 4 * bs / NB, 4 * (bs + 1) / NB);
+      }
     };
     step(2 * j, s0, s1, On(), On(), Ic<2 * P + 1>(), Ic<P>(), hook0);
     step(2 * j + 1, s1, s0, On(), On(), Ic<2 * P + 2>(), Ic<P>(), hook1);
@@ -569,61 +543,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // [g * MBH, (g + 1) * MBH) (for d < 64 key half 0 finalises the single block).
   load_w();
   constexpr int MBH = MB >= 2 ? MB / 2 : 1;
-  constexpr int NXV = 2 * MBH * 4 + 1;  // exported 16-byte rows: accumulator quads, then (m0, m1, l0, l1)
-  constexpr int NX = MB >= 2 ? 4 : 2;   // exporting waves
+  constexpr int NXV = MBH * 4 + 1;     // exported 16-byte rows: accumulator quads, then (m, l)
+  constexpr int NX = MB >= 2 ? 8 : 4;  // exporting waves
   constexpr int XS_BYTES = NXV * 64 * 16, XS_PER = VA_BYTES / XS_BYTES;  // exchange slots per V array
-  static_assert(XS_PER >= 1 && (NX + XS_PER - 1) / XS_PER <= 2, "exchange must fit in the V arrays");
+  // (for d < 128 the exchange takes an array of its own; LDS is plentiful there)
+  constexpr bool XFIT = XS_PER >= 1 && (NX + XS_PER - 1) / XS_PER <= 2;
+  __shared__ __attribute__((aligned(16))) unsigned char xs_own[XFIT ? 16 : NX * XS_BYTES];
   static_assert(W_INSTR <= 4 * KA_KB, "W must fit in the K arrays");
-  const int partner = wave ^ 2;
+  const int partner = wave ^ 4;
   const bool owner = MB >= 2 || grp == 0;
   const bool partner_owns = MB >= 2 || grp == 1;
   auto xslot = [&](int w) ARL2_INLINE {  // [NXV][64] f32x4 of exporter w
-    const int xs = MB >= 2 ? w : (w & 1);
-    return reinterpret_cast<f32x4*>((xs / XS_PER ? vs1 : vs0) + (xs % XS_PER) * XS_BYTES);
+    const int xs = MB >= 2 ? w : (w & 3);
+    if constexpr (XFIT) return reinterpret_cast<f32x4*>((xs / XS_PER ? vs1 : vs0) + (xs % XS_PER) * XS_BYTES);
+    else return reinterpret_cast<f32x4*>(xs_own + xs * XS_BYTES);
   };
   if (partner_owns) {
     f32x4* xo = xslot(wave);
     const int p0 = MB >= 2 ? (1 - grp) * MBH : 0;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb >= p0 && mb < p0 + MBH)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        if (mb >= p0 && mb < p0 + MBH)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            xo[((qq * MBH + mb - p0) * 4 + g) * 64 + lane] =
-                f32x4{acc[qq][mb][4 * g], acc[qq][mb][4 * g + 1], acc[qq][mb][4 * g + 2], acc[qq][mb][4 * g + 3]};
-    xo[(NXV - 1) * 64 + lane] = f32x4{m_run[0], m_run[1], l_run[0], l_run[1]};
+        for (int g = 0; g < 4; ++g)
+          xo[((mb - p0) * 4 + g) * 64 + lane] =
+              f32x4{acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
+    xo[(NXV - 1) * 64 + lane] = f32x4{m_run, l_run, 0.f, 0.f};
   }
   __syncthreads();
 
   const f32x4* xi = xslot(partner);
   const int o0 = MB >= 2 ? grp * MBH : 0;
   if (owner) {
-    float a0[2], a1[2];
     const f32x4 ml = xi[(NXV - 1) * 64 + lane];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const float m1 = ml[qq], l1 = ml[2 + qq];
-      const float m = fmaxf(m_run[qq], m1);
-      const float e0 = __builtin_amdgcn_exp2f((m_run[qq] - m) * scale_log2);
-      const float e1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
-      const float lsum = l_run[qq] * e0 + l1 * e1;
-      const float inv = 1.f / (lsum + other_half(lsum, lane));
-      a0[qq] = e0 * inv;
-      a1[qq] = e1 * inv;
-    }
+    const float m1 = ml[0], l1 = ml[1];
+    const float m = fmaxf(m_run, m1);
+    const float e0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
+    const float e1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+    const float lsum = l_run * e0 + l1 * e1;
+    const float inv = 1.f / (lsum + other_half(lsum, lane));
+    const float a0 = e0 * inv, a1 = e1 * inv;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb < o0 || mb >= o0 + MBH) continue;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = xi[((mb - o0) * 4 + g) * 64 + lane];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = xi[((qq * MBH + mb - o0) * 4 + g) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[qq][mb][4 * g + e] = acc[qq][mb][4 * g + e] * a0[qq] + x[e] * a1[qq];
-        }
+        for (int e = 0; e < 4; ++e) acc[mb][4 * g + e] = acc[mb][4 * g + e] * a0 + x[e] * a1;
+      }
     }
   }
   wait_vmem();  // W^T has landed (every wave waits for its own loads, then the barrier)
@@ -639,36 +607,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(w_kb((hl * KS + st) * (DP / 32) + mb) + k_frag);
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) acc[qq][mb] = mfma32(a, qf[qq][st], acc[qq][mb]);
+        acc[mb] = mfma32(a, qf[st], acc[mb]);
       }
   }
 
-  // Output.  The wave's 64 rows x OWN_D finished features go through LDS (the V arrays, free
+  // Output.  The wave's 32 rows x OWN_D finished features go through LDS (the V arrays, free
   // since the barrier) into row-major order, 16-byte chunks of row r at granule
   // chunk ^ (r % OC), so that each store instruction writes whole row segments.
   constexpr int OWN_D = D < 32 * MBH ? D : 32 * MBH;  // features this wave finalises
   constexpr int OC = OWN_D / 4, ORB = 16 * OC, RPS = 64 / OC;  // chunks per row, row bytes, rows per store
-  static_assert(2 * 64 * ORB <= VA_BYTES, "output staging must fit in the V arrays");
-  unsigned char* ost = (wave >> 1 ? vs1 : vs0) + (wave & 1) * 64 * ORB;
+  static_assert(4 * 32 * ORB <= VA_BYTES, "output staging must fit in the V arrays");
+  unsigned char* ost = (wave >> 2 ? vs1 : vs0) + (wave & 3) * 32 * ORB;
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb < o0 || mb >= o0 + MBH) continue;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb < o0 || mb >= o0 + MBH) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ld = 32 * (mb - o0) + 8 * g + 4 * (lane >> 5);
-        if (ld < OWN_D) {
-          const int r = qq * 32 + (lane & 31), c = ld >> 2;
-          *reinterpret_cast<f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC))) =
-              f32x4{acc[qq][mb][4 * g], acc[qq][mb][4 * g + 1], acc[qq][mb][4 * g + 2], acc[qq][mb][4 * g + 3]};
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int ld = 32 * (mb - o0) + 8 * g + 4 * (lane >> 5);
+      if (ld < OWN_D) {
+        const int r = lane & 31, c = ld >> 2;
+        *reinterpret_cast<f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC))) =
+            f32x4{acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
       }
     }
-  const int row0 = qt * kQTile + qs * 64;
+  }
+  const int row0 = qt * kQTile + rb * 32;
 #pragma unroll
-  for (int i = 0; i < OC; ++i) {
+  for (int i = 0; i < 32 / RPS; ++i) {
     const int r = RPS * i + lane / OC, c = lane % OC;
     const f32x4 x = *reinterpret_cast<const f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC)));
     if (row0 + r < T) {
