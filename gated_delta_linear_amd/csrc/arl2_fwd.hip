@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // direct-to-LDS loads in flight into other slots and does not wait for those loads.  After
   // the loop the K arrays hold W^T (hi, lo) and the V arrays the exchange between the halves.
   constexpr int KA_BYTES = 2 * KH_BYTES, VA_BYTES = 2 * VT_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char ks0[KA_BYTES], ks1[KA_BYTES], ks2[KA_BYTES], ks3[KA_BYTES];
+  __shared__ __attribute__((aligned(64))) unsigned char ks0[KA_BYTES], ks1[KA_BYTES], ks2[KA_BYTES], ks3[KA_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char vs0[VA_BYTES], vs1[VA_BYTES];
   auto karr = [&](auto slot_c) ARL2_INLINE -> unsigned char* {
     constexpr int sl = decltype(slot_c)::value & 3;
@@ -224,12 +224,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto dma_k = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int i) ARL2_INLINE {
     dma16(r, dst + i * 1024, k_vo[i % NKV], (int)(RPI * i * rs * 2));
   };
-  // K fragment of k-step st (row lane % 32, feature chunk 2 st + lane / 32) within a half-tile.
+  // K fragment of k-step st (row lane % 32, feature chunk 2 st + lane / 32) within this key
+  // half's part of a ring slot.
   int k_fo[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     const int row = lane & 31;
-    k_fo[st] = row * RB + 16 * ((2 * st + (lane >> 5)) ^ (row % CPR));
+    k_fo[st] = grp * KH_BYTES + row * RB + 16 * ((2 * st + (lane >> 5)) ^ (row % CPR));
   }
   // V: blocks of 4 keys (4 va .. 4 va + 3) x 8 features (8 vbb ..) through registers, with the
   // 16 lanes of a quarter-wave on the 16 key blocks of one feature block, transposed (and
@@ -325,19 +326,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   float m_run = -INFINITY;  // running max (raw score units), equal in lanes l and l ^ 32
   float l_run = 0.f;        // this lane's share of the running sum
 
-  // Fragment offsets of this lane inside a K plane and a V^T tile.
-  const int k_frag = (lane & 31) * 32 + (lane >> 5) * 16;  // W^T planes: 32-byte rows
-  const int v_frag = (lane & 31) * VLD + 8 * (lane >> 5);
+  // Fragment offsets of this lane inside a W^T plane (32-byte rows) and, in bytes, inside this
+  // key half's part of a V^T buffer.
+  const int k_frag = (lane & 31) * 32 + (lane >> 5) * 16;
+  const int v_frag = grp * VT_BYTES + 2 * ((lane & 31) * VLD + 8 * (lane >> 5));
 
   // Fragments in flight.  K fragment st of a unit = k-step st; V^T fragment f of a unit =
   // k-step f / MB of the unit (16 keys), feature block f % MB.
   bf16x8 kfr[KS];
   f16x8 vfr[2 * MB];
 
-  // Softmax of score registers [v0, v1) of a unit (v1 - v0 a multiple of 4) into the fp16 P^T
-  // fragments pf[k-step] (register i of the score block is register i % 8 of fragment i / 8)
-  // and the unit's row sum lsum (fp16 pairs of the rounded P that enters the MFMA).
-  auto softmax_part = [&](const f32x16& sa, f16x8 (&pf)[2], int v0, int v1, float mc, f16x2& lsum) ARL2_INLINE {
+  // Softmax of score registers [v0, v1) of a unit (v1 - v0 a multiple of 4) into fp16 pairs:
+  // registers i, i + 1 of the score block become word (i / 2) % 4 of pw[i / 8], the P^T
+  // fragment of k-step i / 8; and the unit's row sum lsum (fp16 pairs of the rounded P that
+  // enters the MFMA).  A fragment is pinned once complete.
+  auto softmax_part = [&](const f32x16& sa, u32x4 (&pw)[2], int v0, int v1, float mc, f16x2& lsum) ARL2_INLINE {
 #pragma unroll
     for (int jj = v0; jj < v1; jj += 4) {
       f16x2 p[2];
@@ -347,12 +350,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const f32x2 x = {__builtin_amdgcn_exp2f(fmaf(sa[i], scale_log2, -mc)),
                          __builtin_amdgcn_exp2f(fmaf(sa[i + 1], scale_log2, -mc))};
         p[e] = __builtin_convertvector(x, f16x2);
-        pf[i >> 3][i & 7] = p[e][0];
-        pf[i >> 3][(i & 7) + 1] = p[e][1];
+        pw[i >> 3][(i >> 1) & 3] = __builtin_bit_cast(unsigned, p[e]);
       }
       lsum += p[0] + p[1];
     }
-    pin(pf[v0 >> 3]);
+    if (v1 % 8 == 0) pin(pw[(v1 - 1) >> 3]);
     pin(lsum);
   };
   // Keys of unit u past the end of this wave's keys do not take part.
@@ -391,8 +393,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto step = [&](int u, const f32x16& sa, f32x16& sb, auto next_sw, auto cur_sw, auto kslot_c, auto vbuf_c,
                   auto&& hook) ARL2_INLINE {
     constexpr bool nx = decltype(next_sw)::value, cu = decltype(cur_sw)::value;
-    const unsigned char* kt = karr(kslot_c) + grp * KH_BYTES;
-    const f16* vt = reinterpret_cast<const f16*>(varr(vbuf_c) + grp * VT_BYTES) + v_frag + 32 * (u & 1);
+    const unsigned char* kt = karr(kslot_c);
+    const unsigned char* vt = varr(vbuf_c) + v_frag + 64 * (u & 1);
     auto read_stage = [&](int s) ARL2_INLINE {
       if (s < NA) {
         if (nx)
@@ -402,12 +404,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (cu)
 #pragma unroll
           for (int f = (s - NA) * FB; f < (s - NA + 1) * FB; ++f)
-            vfr[f] = *reinterpret_cast<const f16x8*>(vt + 32 * (f % MB) * VLD + 16 * (f / MB));
+            vfr[f] = *reinterpret_cast<const f16x8*>(vt + 64 * (f % MB) * VLD + 32 * (f / MB));
       }
     };
     // (a half without keys keeps m = -inf; its P must come out 0, not NaN)
     const float mc = m_run == -INFINITY ? 0.f : m_run * scale_log2;
-    f16x8 pf[2];
+    u32x4 pw[2];
     f16x2 lsum = {(f16)0.f, (f16)0.f};
     read_stage(0);
     read_stage(1);
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int t = 0; t < NA; ++t) {
       hook(t);
       read_stage(t + 2);
-      if (cu) softmax_part(sa, pf, t * 16 / NA, (t + 1) * 16 / NA, mc, lsum);
+      if (cu) softmax_part(sa, pw, t * 16 / NA, (t + 1) * 16 / NA, mc, lsum);
       if (nx)
 #pragma unroll
         for (int f = t * FA; f < (t + 1) * FA; ++f) sb = mfma32(kfr[f], qf[f], f ? sb : zero16());
@@ -438,7 +440,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       if (cu)
 #pragma unroll
-        for (int f = t * FB; f < (t + 1) * FB; ++f) acc[f % MB] = mfma32(vfr[f], pf[f / MB], acc[f % MB]);
+        for (int f = t * FB; f < (t + 1) * FB; ++f)
+          acc[f % MB] = mfma32(vfr[f], __builtin_bit_cast(f16x8, pw[f / MB]), acc[f % MB]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (nx) rescale_to(mp);
@@ -474,8 +477,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   wait_vmem_but<4 * VPT>();
   __syncthreads();
 #pragma unroll
-  for (int st = 0; st < KS; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(vs1 + rb * 32 * RB + k_fo[st]);
-  f32x16 s0, s1;
+  for (int st = 0; st < KS; ++st)
+    qf[st] = *reinterpret_cast<const bf16x8*>(vs1 + rb * 32 * RB + k_fo[st] - grp * KH_BYTES);
+  f32x16 s0, s1 = zero16();  // (s1 is not read by the first step)
   auto no_staging = [](int) ARL2_INLINE {};
   step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
   store_v(Ic<0>());
