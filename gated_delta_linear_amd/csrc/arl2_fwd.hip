@@ -192,14 +192,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bf16* kb = k + base;
   const bf16* vb = v + base;
 
-  const int ntiles = (T + kKV - 1) / kKV;
-  const int nt0 = (ntiles + 1) >> 1;  // key half 0: tiles [0, nt0); key half 1: [nt0, ntiles)
-  const int iters = nt0;
-  const int key0 = (grp ? nt0 : 0) * kKV;  // first key of this wave's half
-  // end of this wave's keys: every iteration runs all its units, and units past the end (the
-  // second half's last iteration when it has one tile fewer, the unit after each half's last)
-  // are masked to -inf, so they add nothing
-  const int key_end = grp ? T : min(T, nt0 * kKV);
+  // The halves split the frame's keys at 32-key units: half 0 takes the first u0 = ceil(U / 2)
+  // of the U units, half 1 the rest.  Every wave runs u0 pipeline steps (one per unit; the
+  // work-group barriers keep the halves together), in iters full iterations of two units and,
+  // for odd u0, a last single step.  Units past the end of a wave's keys (half 1's last when U
+  // is odd, the one after each half's last) are masked to -inf, so they add nothing.
+  const int units = (T + kUnit - 1) / kUnit;
+  const int u0 = (units + 1) >> 1;
+  const int steps = u0, iters = steps >> 1;
+  const int key0 = grp ? u0 * kUnit : 0;  // first key of this wave's half
+  const int key_end = grp ? T : min(T, u0 * kUnit);
 
   if (D < DP) {  // padded V^T rows stay zero for the whole kernel
     for (int i = tid; i < VA_BYTES / 16; i += kThreads) {
@@ -324,7 +326,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = zero16();
   float m_run = -INFINITY;  // running max (raw score units), equal in lanes l and l ^ 32
+  float mc = 0.f;           // m_run * scale_log2 (0 while m_run = -inf: a half without keys gets P = 0, not NaN)
+  float thr = -INFINITY;    // raw score above which the running max is raised
   float l_run = 0.f;        // this lane's share of the running sum
+  const float slack_raw = kRescaleSlack / scale_log2;
 
   // Fragment offsets of this lane inside a W^T plane (32-byte rows) and, in bytes, inside this
   // key half's part of a V^T buffer.
@@ -369,12 +374,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   // Raise the running max to a unit's max when it exceeds it by more than the slack in some
   // lane of the wave (the accumulator and sum are rescaled); otherwise keep it, so P <= 2^8.
+  // mp is this lane's max over its 16 keys of the unit; the row max (lanes l and l ^ 32) is
+  // only needed when raising.
   auto rescale_to = [&](float mp) ARL2_INLINE {
-    const float mx = fmaxf(mp, other_half(mp, lane));  // lanes l and l ^ 32 hold one row
-    if (__builtin_amdgcn_ballot_w64((mx - m_run) * scale_log2 > kRescaleSlack) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mp > thr) != 0) {
+      const float mx = fmaxf(mp, other_half(mp, lane));
       const float m_new = fmaxf(m_run, mx);
       const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
       m_run = m_new;
+      mc = m_new * scale_log2;
+      thr = m_new + slack_raw;
       l_run *= corr;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -407,8 +416,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             vfr[f] = *reinterpret_cast<const f16x8*>(vt + 64 * (f % MB) * VLD + 32 * (f / MB));
       }
     };
-    // (a half without keys keeps m = -inf; its P must come out 0, not NaN)
-    const float mc = m_run == -INFINITY ? 0.f : m_run * scale_log2;
     u32x4 pw[2];
     f16x2 lsum = {(f16)0.f, (f16)0.f};
     read_stage(0);
@@ -483,7 +490,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto no_staging = [](int) ARL2_INLINE {};
   step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
   store_v(Ic<0>());
-  if (iters > 1) load_v(1);
+  if (steps > 2) load_v(1);
   if (D < DP) {  // the query tile overlapped padded V^T rows of buffer 1, which stay zero
     __syncthreads();
     for (int i = tid; i < VA_BYTES / 16; i += kThreads) reinterpret_cast<uint4*>(vs1)[i] = make_uint4(0, 0, 0, 0);
@@ -539,7 +546,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     iteration(j, Ic<0>());
     iteration(j + 1, Ic<1>());
   }
-  if (j < iters) iteration(j, Ic<0>());
+  if (j < iters) {
+    iteration(j, Ic<0>());
+    ++j;
+  }
+  if (steps & 1) {  // the last unit, 2j: its scores are in s0 and its V^T tile j in buffer j % 2
+    if (j & 1) step(2 * j, s0, s1, Off(), On(), Ic<0>(), Ic<1>(), no_staging);
+    else step(2 * j, s0, s1, Off(), On(), Ic<0>(), Ic<0>(), no_staging);
+    __syncthreads();  // every wave is done with the V arrays before the exchange writes them
+  }
 
   // Epilogue.  W^T comes into the K arrays while the two waves of a row block exchange,
   // through the V arrays, the halves of the accumulator that the other one finalises (with
