@@ -481,7 +481,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   asm volatile("" ::: "memory");  // the V loads stay behind the loads into LDS
   __builtin_amdgcn_sched_barrier(0);
   load_v(0);
-  wait_vmem_but<4 * VPT>();
+  // The first barrier needs the query tile and K half-tile 0 only.  When every wave issued the
+  // same loads (the query tile dealt evenly over the 8 waves, half-tile 0 first and evenly over
+  // the 4 waves of a half), the loads of half-tiles 1-2 and of V stay in flight; otherwise only
+  // those of V.
+  {
+    constexpr int QI = kQTile / RPI, NKI = 3 * KS;
+    constexpr bool EVEN = QI % kWaves == 0 && KS % 4 == 0;
+    wait_vmem_but<(EVEN ? (NKI - KS) / 4 : 0) + 4 * VPT>();
+  }
   __syncthreads();
 #pragma unroll
   for (int st = 0; st < KS; ++st)
@@ -491,6 +499,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
   store_v(Ic<0>());
   if (steps > 2) load_v(1);
+  wait_vmem_but<4 * VPT>();  // half-tiles 1-2 have landed (V tile 1 may still be in flight)
   if (D < DP) {  // the query tile overlapped padded V^T rows of buffer 1, which stay zero
     __syncthreads();
     for (int i = tid; i < VA_BYTES / 16; i += kThreads) reinterpret_cast<uint4*>(vs1)[i] = make_uint4(0, 0, 0, 0);
@@ -550,6 +559,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     iteration(j, Ic<0>());
     ++j;
   }
+  // W^T (for the epilogue) comes into the K arrays, which the last single step does not read.
+  load_w();
   if (steps & 1) {  // the last unit, 2j: its scores are in s0 and its V^T tile j in buffer j % 2
     if (j & 1) step(2 * j, s0, s1, Off(), On(), Ic<0>(), Ic<1>(), no_staging);
     else step(2 * j, s0, s1, Off(), On(), Ic<0>(), Ic<0>(), no_staging);
@@ -560,7 +571,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // through the V arrays, the halves of the accumulator that the other one finalises (with
   // their running max and sum): the wave of key half g finalises output feature blocks
   // [g * MBH, (g + 1) * MBH) (for d < 64 key half 0 finalises the single block).
-  load_w();
   constexpr int MBH = MB >= 2 ? MB / 2 : 1;
   constexpr int NXV = MBH * 4 + 1;     // exported 16-byte rows: accumulator quads, then (m, l)
   constexpr int NX = MB >= 2 ? 8 : 4;  // exporting waves
