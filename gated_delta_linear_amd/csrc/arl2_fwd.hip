@@ -461,39 +461,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // computes the scores and max of unit 0, while V tile 0 arrives, goes to V^T buffer 0, and
   // tile 1 comes into registers.  The second barrier publishes V tile 0 and keeps the first
   // iteration's loads into slot 0 (and stores into buffer 1) behind every wave's reads.
+  // Only the query tile and K half-tile 0 are waited for before unit 0's scores; half-tiles
+  // 1-2 and V tile 0 are issued after the first barrier, so that the vector-memory path
+  // drains them while those MFMAs run.
   {
     const __amdgpu_buffer_rsrc_t qr = rows_rsrc(qb, T, rs, D, qt * kQTile);
     constexpr int QI = kQTile / RPI;  // 1-KB loads of the query tile
 #pragma unroll
     for (int c = 0; c < (QI + kWaves - 1) / kWaves; ++c)
       if (wave + kWaves * c < QI) dma_k(qr, vs1, wave + kWaves * c);
-    constexpr int NKI = 3 * KS;  // loads of this key half's K half-tiles 0-2
+    const __amdgpu_buffer_rsrc_t r0 = rows_rsrc(kb, T, rs, D, key0);
+#pragma unroll
+    for (int m = 0; m < (KS + 3) / 4; ++m)
+      if (sw + 4 * m < KS) dma_k(r0, ks0 + grp * KH_BYTES, sw + 4 * m);
+  }
+  wait_vmem();
+  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    qf[st] = *reinterpret_cast<const bf16x8*>(vs1 + rb * 32 * RB + k_fo[st] - grp * KH_BYTES);
+  {
+    constexpr int NKI = 2 * KS;  // loads of this key half's K half-tiles 1-2
 #pragma unroll
     for (int m = 0; m < (NKI + 3) / 4; ++m) {
       const int i = sw + 4 * m;
       if (i < NKI) {
-        const int hh = i / KS;
+        const int hh = 1 + i / KS;
         const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, T, rs, D, key0 + kUnit * hh);
-        dma_k(r, (hh == 0 ? ks0 : hh == 1 ? ks1 : ks2) + grp * KH_BYTES, i % KS);
+        dma_k(r, (hh == 1 ? ks1 : ks2) + grp * KH_BYTES, i % KS);
       }
     }
   }
   asm volatile("" ::: "memory");  // the V loads stay behind the loads into LDS
   __builtin_amdgcn_sched_barrier(0);
   load_v(0);
-  // The first barrier needs the query tile and K half-tile 0 only.  When every wave issued the
-  // same loads (the query tile dealt evenly over the 8 waves, half-tile 0 first and evenly over
-  // the 4 waves of a half), the loads of half-tiles 1-2 and of V stay in flight; otherwise only
-  // those of V.
-  {
-    constexpr int QI = kQTile / RPI, NKI = 3 * KS;
-    constexpr bool EVEN = QI % kWaves == 0 && KS % 4 == 0;
-    wait_vmem_but<(EVEN ? (NKI - KS) / 4 : 0) + 4 * VPT>();
-  }
-  __syncthreads();
-#pragma unroll
-  for (int st = 0; st < KS; ++st)
-    qf[st] = *reinterpret_cast<const bf16x8*>(vs1 + rb * 32 * RB + k_fo[st] - grp * KH_BYTES);
   f32x16 s0, s1 = zero16();  // (s1 is not read by the first step)
   auto no_staging = [](int) ARL2_INLINE {};
   step(-1, s1, s0, On(), Off(), Ic<0>(), Ic<1>(), no_staging);
