@@ -66,11 +66,6 @@ struct arl2_layer {
   hipStream_t last_stream = nullptr;
   bool have_last_stream = false;
   hipEvent_t handoff = nullptr;
-  // The state write's per-chunk kernel runs on this stream, concurrently with the clean pass's
-  // output kernel (both only read the frame's inputs); fork / join go through two events.
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr;
-  hipEvent_t join = nullptr;
 };
 
 namespace {
@@ -255,16 +250,10 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
     (void)hipStreamSynchronize(stream);
     (void)hipFree(L->slab);
     if (L->handoff) (void)hipEventDestroy(L->handoff);
-    if (L->fork) (void)hipEventDestroy(L->fork);
-    if (L->join) (void)hipEventDestroy(L->join);
-    if (L->side) (void)hipStreamDestroy(L->side);
     delete L;
     return fail(ARL2_E_HIP, "%s: %s", what, hipGetErrorString(err));
   };
   if ((e = hipEventCreateWithFlags(&L->handoff, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
-  if ((e = hipEventCreateWithFlags(&L->fork, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
-  if ((e = hipEventCreateWithFlags(&L->join, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
-  if ((e = hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking)) != hipSuccess) return bail(e, "hipStreamCreate");
   // S_0 = 0 and everything derived from it is 0 as well.
   if ((e = hipMemsetAsync(L->slab, 0, L->bytes - 3 * map_bytes, stream)) != hipSuccess) return bail(e, "hipMemsetAsync");
   arl2::PrepMapsArgs pm{phi_q, phi_k, phi_v, L->pq, L->pkt, L->pvt, c.heads};
@@ -311,20 +300,12 @@ arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const
   pa.H = L->cfg.heads;
   pa.T = L->cfg.tokens_per_frame;
   pa.knorm_eps = L->eps;
-  if (out) {
-    // fork: the per-chunk kernel on the side stream overlaps the output kernel on `stream`
-    hipError_t e = hipEventRecord(L->fork, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(L->side, L->fork, 0);
-    if (e != hipSuccess) return hip_fail(L, e, "fork to the side stream");
-    if ((st = after_launch(L, arl2::launch_commit_partial(L->d, pa, L->side), L->side, "state write kernel launch")))
-      return st;
-    if ((st = launch_pass(L, q, k, v, out, stream))) return st;
-    e = hipEventRecord(L->join, L->side);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, L->join, 0);
-    if (e != hipSuccess) return hip_fail(L, e, "join from the side stream");
-  } else if ((st = after_launch(L, arl2::launch_commit_partial(L->d, pa, stream), stream, "state write kernel launch"))) {
+  // The clean pass's output first, then the write, in stream order: run beside the output kernel
+  // the state write's per-chunk kernel slowed it by more than it saved (both load the memory
+  // system at their start, and the per-chunk work-groups took CUs the output kernel needed).
+  if (out && (st = launch_pass(L, q, k, v, out, stream))) return st;
+  if ((st = after_launch(L, arl2::launch_commit_partial(L->d, pa, stream), stream, "state write kernel launch")))
     return st;
-  }
   if ((st = launch_reduce(L, L->s[L->cur], alpha, L->chunks, L->cur ^ 1, stream))) return st;
   L->cur ^= 1;
   L->frame += 1;
@@ -335,12 +316,8 @@ arl2_status arl2_destroy(arl2_layer* L) {
   if (!L) return ARL2_OK;
   hipError_t e = hipSuccess;
   if (L->have_last_stream) e = hipStreamSynchronize(L->last_stream);
-  if (e == hipSuccess && L->side) e = hipStreamSynchronize(L->side);
   hipError_t e2 = L->slab ? hipFree(L->slab) : hipSuccess;
   if (L->handoff) (void)hipEventDestroy(L->handoff);
-  if (L->fork) (void)hipEventDestroy(L->fork);
-  if (L->join) (void)hipEventDestroy(L->join);
-  if (L->side) (void)hipStreamDestroy(L->side);
   delete L;
   if (e != hipSuccess) return fail(ARL2_E_HIP, "destroy: synchronise: %s", hipGetErrorString(e));
   if (e2 != hipSuccess) return fail(ARL2_E_HIP, "destroy: hipFree: %s", hipGetErrorString(e2));
