@@ -58,6 +58,14 @@ struct PartialSmem {
   float inv_norm[kCommitChunk];
 };
 
+// Wait until at most N of this wave's vector memory loads are in flight (N < 64; loads complete
+// in issue order).  The count's low 4 bits and high 2 bits sit apart in the instruction.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane (lds wave-uniform).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
@@ -90,34 +98,41 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
 
   // This lane's token for the A/B fragments of K and V (row-major, 8 features per lane).
   const int tok = t0 + 32 * wave + (lane & 31);
-  const bool tok_ok = tok < T;
   const int64_t sb = ((int64_t)b * H + h) * (KS * NB * 64);  // fragment index base
 
-  // Shared operands into LDS: 4 * MB * KS fragments of 1 KB, spread over the 4 waves.
-  {
-    const __amdgpu_buffer_rsrc_t rk = rsrc(pkt + (int64_t)h * DP * D, DP * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(pvt + (int64_t)h * DP * D, DP * D * 2);
-    const __amdgpu_buffer_rsrc_t rh = rsrc(sneg_hi + sb * 8, KS * NB * 1024);
-    const __amdgpu_buffer_rsrc_t rl = rsrc(sneg_lo + sb * 8, KS * NB * 1024);
-    const int map_lane = ((lane & 31) * D + 8 * (lane >> 5)) * 2;  // row l % 32, features 8 (l / 32) ..
-    for (int f = wave; f < MB * KS; f += 4) {
-      const int mb = f / KS, st = f % KS;
-      dma16(rk, &sm.op.pk[mb][st][0], map_lane + (32 * mb * D + 16 * st) * 2);
-      dma16(rv, &sm.op.pv[mb][st][0], map_lane + (32 * mb * D + 16 * st) * 2);
-      dma16(rh, &sm.op.shi[0][0][0] + 64 * f, f * 1024 + lane * 16);
-      dma16(rl, &sm.op.slo[0][0][0] + 64 * f, f * 1024 + lane * 16);
-    }
-  }
-
-  // All global loads of the wave are issued before the first wait: this lane's token row of
-  // K and of V (8 features per lane and k-step).
+  // Loads in the order the products need them, each group waited for just before its first
+  // use (when the operand fragments deal evenly over the 4 waves; otherwise all at once):
+  // phi_k^T fragments and this lane's row of K; phi_v^T and the row of V; -S hi / lo.
+  // Operands go straight into LDS (4 * MB * KS fragments of 1 KB); K and V come through
+  // buffer loads, so rows past the frame read as zeros and every wave issues the same loads.
+  constexpr int NFRAG = MB * KS;
+  constexpr bool EVEN = NFRAG % 4 == 0;
+  constexpr int NF = NFRAG / 4;  // fragments per wave and operand when EVEN
+  const __amdgpu_buffer_rsrc_t rk = rsrc(pkt + (int64_t)h * DP * D, DP * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(pvt + (int64_t)h * DP * D, DP * D * 2);
+  const __amdgpu_buffer_rsrc_t rh = rsrc(sneg_hi + sb * 8, KS * NB * 1024);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(sneg_lo + sb * 8, KS * NB * 1024);
+  const int slice_bytes = (int)(((int64_t)(T - 1) * rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rkin = rsrc(k + base, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rvin = rsrc(v + base, slice_bytes);
+  const int map_lane = ((lane & 31) * D + 8 * (lane >> 5)) * 2;  // row l % 32, features 8 (l / 32) ..
+  const int row_lane = (int)(tok * rs * 2) + 16 * (lane >> 5);      // this lane's token row, 8 features
   bf16x8 kf[KS], vf[KS];
+  for (int f = wave; f < NFRAG; f += 4)
+    dma16(rk, &sm.op.pk[f / KS][f % KS][0], map_lane + (32 * (f / KS) * D + 16 * (f % KS)) * 2);
 #pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    kf[st] = tok_ok ? ld_bf16x8(k + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
-    vf[st] = tok_ok ? ld_bf16x8(v + base + tok * rs + 16 * st + 8 * (lane >> 5)) : zero_bf16x8();
+  for (int st = 0; st < KS; ++st)
+    kf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rkin, row_lane + 32 * st, 0, 0));
+  for (int f = wave; f < NFRAG; f += 4)
+    dma16(rv, &sm.op.pv[f / KS][f % KS][0], map_lane + (32 * (f / KS) * D + 16 * (f % KS)) * 2);
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    vf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rvin, row_lane + 32 * st, 0, 0));
+  for (int f = wave; f < NFRAG; f += 4) {
+    dma16(rh, &sm.op.shi[0][0][0] + 64 * f, f * 1024 + lane * 16);
+    dma16(rl, &sm.op.slo[0][0][0] + 64 * f, f * 1024 + lane * 16);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads into LDS are done
+  wait_vmcnt<EVEN ? 3 * NF + KS : 0>();  // phi_k^T (every wave's share, after the barrier) and K
   __syncthreads();
 
   // K'^T = phi_k^T K^T: rows = key features, lane column = token.
@@ -143,11 +158,19 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
     for (int i = 0; i < 16; ++i) kt[mb][i] *= inv;
   if (lane < 32) sm.inv_norm[32 * wave + lane] = inv;
 
-  // R = V' - K' S: first K' (-S) with split operands, then V phi_v accumulated on top.
+  // R = V' - K' S: first V phi_v, then K' (-S) with split operands accumulated on top.
   // A fragment of K' for k-step st: register 8 (st % 2) + j of block st / 2.
   f32x16 r[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) r[nb] = zero16();
+  wait_vmcnt<EVEN ? 2 * NF : 0>();  // phi_v^T and V
+  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) r[nb] = mfma32(vf[st], sm.op.pv[nb][st][lane], r[nb]);
+  wait_vmcnt<0>();  // -S hi / lo
+  __syncthreads();
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     bf16x8 khi, klo;
@@ -165,10 +188,6 @@ __global__ __launch_bounds__(kThreads) void arl2_commit_partial_kernel(
       r[nb] = mfma32(klo, shi, r[nb]);
     }
   }
-#pragma unroll
-  for (int st = 0; st < KS; ++st)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) r[nb] = mfma32(vf[st], sm.op.pv[nb][st][lane], r[nb]);
 
   // K' = K phi_k (rows = tokens, lane column = key feature): the operands of K'^T in swapped
   // MFMA slots; it is the A operand of the token contraction below.
