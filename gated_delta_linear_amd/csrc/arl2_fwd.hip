@@ -524,27 +524,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const __amdgpu_buffer_rsrc_t kr0 = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 3));
     const __amdgpu_buffer_rsrc_t kr1 = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 4));
     const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vb, T, rs, D, key0 + kKV * (j + 2));
-    auto hook0 = [&](int st) ARL2_INLINE {
-      if (st < NA) {
+    // The K loads are dealt over both phases of step 2j (half each, on every other stage) and the
+    // V loads over both phases of step 2j + 1, so that the vector-memory path has work in every
+    // phase instead of bursts in two.
+    auto k_loads = [&](int m0, int m1) ARL2_INLINE {
 #pragma unroll
-        for (int m = st * KPW / NA; m < (st + 1) * KPW / NA; ++m) {
-          const int i = sw + 4 * m;
-          if (i < KS) dma_k(kr0, kd0, i);
-          else if (i < 2 * KS) dma_k(kr1, kd1, i - KS);
-        }
-      } else {
-        const int bs = st - NA;
-#pragma unroll
-        for (int rr = 0; rr < VPT; ++rr) store_v_part(Ic<P + 1>(), rr, 4 * bs / NB, 4 * (bs + 1) / NB);
+      for (int m = m0; m < m1; ++m) {
+        const int i = sw + 4 * m;
+        if (i < KS) dma_k(kr0, kd0, i);
+        else if (i < 2 * KS) dma_k(kr1, kd1, i - KS);
       }
     };
-    auto hook1 = [&](int st) ARL2_INLINE {
-      if (st >= NA) {
-        if (st == NA) asm volatile("" ::: "memory");  // the V loads stay behind the K loads
-        const int bs = st - NA;
+    // share [s * n / (2 ns), (s + 1) * n / (2 ns)) of n items for stage s of ns in half h of the step
+    auto share = [](int h, int s, int ns, int n, int& i0, int& i1) ARL2_INLINE {
+      i0 = (h * ns + s) * n / (2 * ns);
+      i1 = (h * ns + s + 1) * n / (2 * ns);
+    };
+    auto hook0 = [&](int st) ARL2_INLINE {
+      const bool pa = st < NA;
+      const int s = pa ? st : st - NA, ns = pa ? NA : NB;
+      int m0, m1;
+      share(pa ? 0 : 1, s, ns, KPW, m0, m1);
+      k_loads(m0, m1);
+      if (!pa)
 #pragma unroll
-        for (int rr = 0; rr < VPT; ++rr) load_v_part(vr, rr, 4 * bs / NB, 4 * (bs + 1) / NB);
-      }
+        for (int rr = 0; rr < VPT; ++rr) store_v_part(Ic<P + 1>(), rr, 4 * s / NB, 4 * (s + 1) / NB);
+    };
+    auto hook1 = [&](int st) ARL2_INLINE {
+      const bool pa = st < NA;
+      const int s = pa ? st : st - NA, ns = pa ? NA : NB;
+      if (st == 0) asm volatile("" ::: "memory");  // the V loads stay behind the K loads
+      int k0, k1;
+      share(pa ? 0 : 1, s, ns, 4, k0, k1);
+#pragma unroll
+      for (int rr = 0; rr < VPT; ++rr) load_v_part(vr, rr, k0, k1);
     };
     step(2 * j, s0, s1, On(), On(), Ic<2 * P + 1>(), Ic<P>(), hook0);
     step(2 * j + 1, s1, s0, On(), On(), Ic<2 * P + 2>(), Ic<P>(), hook1);
