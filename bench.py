@@ -34,8 +34,8 @@ if ROOT not in sys.path:
 METRIC = "frame-tokens/sec per ARL2 layer at 1560 tok/frame, H=12, d=128; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FWD_KERNEL = "arl2_fwd_kernel"
-KERNEL_SOURCES = ["gated_delta_linear_amd/csrc/arl2_fwd.hip", "gated_delta_linear_amd/csrc/arl2_device.h",
-                  "gated_delta_linear_amd/csrc/arl2_kernels.h"]
+KERNEL_SOURCES = ["gated_delta_linear_amd/csrc/arl2_fwd.hip", "gated_delta_linear_amd/csrc/arl2_write_partial.h",
+                  "gated_delta_linear_amd/csrc/arl2_device.h", "gated_delta_linear_amd/csrc/arl2_kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "arl2_fwd_dit480p_traffic.json")
 RING = 8
 
@@ -90,7 +90,8 @@ def make_layer(w, torch):
 
 def run_frames(layer, ring, w, n, out, stream, first=0):
     """Enqueue n frames of the protocol, frame i using ring slot (first + i) % RING: the
-    denoising passes, then the clean pass (output with S_{N-1}, then the state write)."""
+    denoising passes, then the clean pass (output with S_{N-1} and the state write's per-chunk
+    sums in one launch, then the write's reduce)."""
     for i in range(n):
         passes, beta, alpha = ring[(first + i) % RING]
         for p, (q, k, v) in enumerate(passes):
@@ -127,33 +128,41 @@ def time_region(stream, torch, enqueue):
 
 
 def pass_launch_us(layer, ring, w, out, stream, torch, n=40):
-    """Average duration of the pass kernel: HIP events around each denoising-pass launch."""
-    evs = []
+    """Average duration of the pass kernel: HIP events around n back-to-back denoising-pass
+    launches on the layer's stream (an event pair around every launch would add its own queue
+    overhead to each)."""
+    for i in range(4):
+        q, k, v = ring[i % RING][0][i % w.denoise_steps]
+        layer.denoise_step(q, k, v, out=out, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
     for i in range(n):
         q, k, v = ring[i % RING][0][i % w.denoise_steps]
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
         layer.denoise_step(q, k, v, out=out, stream=stream)
-        b.record(stream)
-        evs.append((a, b))
+    b.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    return a.elapsed_time(b) * 1e3 / n
 
 
-def write_launch_us(layer, ring, w, stream, torch, n=16):
-    """Average duration of the state write (its two kernels): events around commit_frame
-    without an output."""
-    evs = []
-    for i in range(n):
+def commit_launch_us(layer, ring, w, out, stream, torch, n=16):
+    """Average duration of commit_frame over n back-to-back calls: with the output (the clean
+    pass's launch, which also runs the state write's per-chunk work-groups, then the reduce), or
+    with out=None (the state write alone)."""
+    def one(i):
         passes, beta, alpha = ring[i % RING]
         q, k, v = passes[-1]
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        layer.commit_frame(q, k, v, beta, alpha, want_output=False, stream=stream)
-        b.record(stream)
-        evs.append((a, b))
+        if out is None:
+            layer.commit_frame(q, k, v, beta, alpha, want_output=False, stream=stream)
+        else:
+            layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
+    one(0)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        one(i)
+    b.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    return a.elapsed_time(b) * 1e3 / n
 
 
 def load_traffic():
@@ -228,7 +237,8 @@ def bench(args):
 
         # kernel timing: events around each launch, outside the two timed regions above
         pass_us = pass_launch_us(layer, ring, w, out, stream, torch)
-        write_us = write_launch_us(layer, ring, w, stream, torch)
+        write_us = commit_launch_us(layer, ring, w, None, stream, torch)
+        clean_us = commit_launch_us(layer, ring, w, out, stream, torch)
         torch.cuda.synchronize()
         device_bytes = layer.device_bytes
         layer.close()
@@ -266,7 +276,7 @@ def bench(args):
             "flops_per_launch": pass_flops(w), "avg_launch_us": pass_us,
         },
         "breakdown": {
-            "pass_us": pass_us, "state_write_us": write_us,
+            "pass_us": pass_us, "clean_pass_with_write_us": clean_us, "state_write_alone_us": write_us,
             "frame_us_graph": graph_ms / args.steps * 1e3, "frame_us_eager": eager_ms / args.steps * 1e3,
             "host_wall_s_graph": graph_wall, "host_wall_s_eager": eager_wall,
             "frame_mfma_frac": frame_flops(w) / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -317,7 +327,8 @@ COPY_BYTES = 2**30  # calibration copy: 1 GiB each way, four times the 256 MB la
 def pmc_target(args):
     """A short, fixed run for counter passes: a plain device-to-device copy of known size (the
     calibration of FETCH_SIZE / WRITE_SIZE; before each copy another 1 GiB buffer is written,
-    so the source comes from HBM, not the last-level cache), then a few frames of the layer."""
+    so the source comes from HBM, not the last-level cache), then the denoising passes of two
+    frames (launches of the pass kernel without the state write's work-groups)."""
     import torch
 
     from synth import WORKLOADS
@@ -335,10 +346,15 @@ def pmc_target(args):
     layer = make_layer(w, torch)
     ring = stage_ring(w, torch)
     out = layer.new_output()
-    run_frames(layer, ring, w, 2, out, torch.cuda.current_stream())
+    stream = torch.cuda.current_stream()
+    for f in range(2):
+        for p in range(w.denoise_steps):
+            q, k, v = ring[f][0][p]
+            layer.denoise_step(q, k, v, out=out, stream=stream)
     torch.cuda.synchronize()
     layer.close()
-    print(json.dumps({"copy_bytes_each_way": n * 4, "frames": 2, "kernel_source_hash": kernel_source_hash()}))
+    print(json.dumps({"copy_bytes_each_way": n * 4, "denoise_passes": 2 * w.denoise_steps,
+                      "kernel_source_hash": kernel_source_hash()}))
 
 
 def summarize_pmc(args):

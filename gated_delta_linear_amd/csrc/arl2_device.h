@@ -9,6 +9,13 @@
 // as the k-indices of two consecutive k-steps: k-step h, element j <-> row
 // 16 h + 8 (j / 4) + 4 (l / 32) + j % 4.  Any operand paired with such a fragment uses the
 // same row order; this is a permutation of the contraction index and leaves sums unchanged.
+//
+// v_mfma_f32_16x16x32_bf16 (the state write's per-token products):
+//   A (16 x 32): lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
+//   B (32 x 16): lane l holds B[8 * (l / 16) + j][l % 16]
+//   C (16 x 16): lane l, register i holds C[4 * (l / 16) + i][l % 16]
+// Two C blocks stacked over rows (rows 0-15, then 16-31) serve as one 32-deep operand of a
+// contraction over those rows: element j of lane l <-> row 16 (j / 4) + 4 (l / 16) + j % 4.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,15 +26,11 @@ namespace arl2 {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -35,6 +38,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -60,16 +67,6 @@ __device__ __forceinline__ int c_row(int i, int lane) { return 8 * (i >> 2) + 4 
 __device__ __forceinline__ float other_half(float x, int lane) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
-}
-
-// Two transposing LDS reads (ds_read_b64_tr_b16): within each group of 16 lanes, source
-// lane s supplies the address of 4 consecutive 16-bit values; lane i receives element i % 4
-// from source lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
-__device__ __forceinline__ bf16x8 lds_tr_pair(const bf16* p0, const bf16* p1) {
-  s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-  s16x8 r = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, r);
 }
 
 // An fp32 value as bf16 hi + bf16 lo, hi + lo = x to about 16 mantissa bits.

@@ -48,6 +48,7 @@
 
 #include "arl2_device.h"
 #include "arl2_kernels.h"
+#include "arl2_write_partial.h"
 
 namespace arl2 {
 namespace {
@@ -144,7 +145,7 @@ template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
-    int T, int H, int nq, int n_bh, float scale_log2) {
+    int T, int H, int nq, int n_bh, float scale_log2, int n_pass_blocks, const WritePartialArgs wa, int n_write) {
   using S = FwdShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
                 KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB,
@@ -169,6 +170,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr ((decltype(buf_c)::value & 1) == 0) return vs0;
     else return vs1;
   };
+
+  // The exchange between the key halves in the epilogue (for d < 128 an array of its own; LDS
+  // is plentiful there).
+  constexpr int MBH = MB >= 2 ? MB / 2 : 1;
+  constexpr int NXV = MBH * 4 + 1;     // exported 16-byte rows: accumulator quads, then (m, l)
+  constexpr int NX = MB >= 2 ? 8 : 4;  // exporting waves
+  constexpr int XS_BYTES = NXV * 64 * 16, XS_PER = VA_BYTES / XS_BYTES;  // exchange slots per V array
+  constexpr bool XFIT = XS_PER >= 1 && (NX + XS_PER - 1) / XS_PER <= 2;
+  __shared__ __attribute__((aligned(16))) unsigned char xs_own[XFIT ? 16 : NX * XS_BYTES];
+
+  // Work-groups past the pass's: the state write's per-chunk partial sums of the clean pass's
+  // launch, in the same LDS arrays (region A: the K arrays, or the exchange array where the
+  // K arrays are too small; region B: the V arrays).
+  if ((int)blockIdx.x >= n_pass_blocks) {
+    using WS = WriteShape<D>;
+    constexpr int KA_KB = KA_BYTES / 1024, VA_KB = VA_BYTES / 1024;
+    constexpr bool A_IN_K = 4 * KA_KB >= WS::A_SLOTS;
+    static_assert(A_IN_K || (int)sizeof(xs_own) >= WS::A_SLOTS * 1024, "state-write region A must fit");
+    static_assert(2 * VA_KB >= WS::B_SLOTS, "state-write region B must fit");
+    auto slot_a = [&](int i) ARL2_INLINE -> unsigned char* {
+      if constexpr (A_IN_K) {
+        const int a = i / KA_KB;
+        return (a == 0 ? ks0 : a == 1 ? ks1 : a == 2 ? ks2 : ks3) + (i % KA_KB) * 1024;
+      } else {
+        return xs_own + i * 1024;
+      }
+    };
+    auto slot_b = [&](int i) ARL2_INLINE -> unsigned char* { return i < VA_KB ? vs0 + i * 1024 : vs1 + (i - VA_KB) * 1024; };
+    // XCD-aware like the pass's items below: each XCD gets a contiguous run of chunks.
+    const int wp = (int)blockIdx.x - n_pass_blocks, per = (n_write + 7) / 8;
+    const int witem = (wp & 7) * per + (wp >> 3);
+    if (witem < n_write) write_partial<D>(wa, T, H, witem, slot_a, slot_b);
+    return;
+  }
 
   // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin (work-group i runs on XCD
   // i % 8), so each XCD gets a contiguous run of items (the query tiles of one head, then the
@@ -585,13 +620,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // through the V arrays, the halves of the accumulator that the other one finalises (with
   // their running max and sum): the wave of key half g finalises output feature blocks
   // [g * MBH, (g + 1) * MBH) (for d < 64 key half 0 finalises the single block).
-  constexpr int MBH = MB >= 2 ? MB / 2 : 1;
-  constexpr int NXV = MBH * 4 + 1;     // exported 16-byte rows: accumulator quads, then (m, l)
-  constexpr int NX = MB >= 2 ? 8 : 4;  // exporting waves
-  constexpr int XS_BYTES = NXV * 64 * 16, XS_PER = VA_BYTES / XS_BYTES;  // exchange slots per V array
-  // (for d < 128 the exchange takes an array of its own; LDS is plentiful there)
-  constexpr bool XFIT = XS_PER >= 1 && (NX + XS_PER - 1) / XS_PER <= 2;
-  __shared__ __attribute__((aligned(16))) unsigned char xs_own[XFIT ? 16 : NX * XS_BYTES];
   static_assert(W_INSTR <= 4 * KA_KB, "W must fit in the K arrays");
   const int partner = wave ^ 4;
   const bool owner = MB >= 2 || grp == 0;
@@ -694,10 +722,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 template <int D>
-hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_d(const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream) {
   const int nq = (a.T + kQTile - 1) / kQTile;
   const int n_bh = a.H * a.B;
-  dim3 grid(8 * ((nq * n_bh + 7) / 8));
+  const int n_pass_blocks = a.out ? 8 * ((nq * n_bh + 7) / 8) : 0;
+  const int n_write = w ? commit_chunks(a.T) * n_bh : 0;
+  if (n_pass_blocks + n_write == 0) return hipSuccess;
+  const WritePartialArgs wa = w ? *w : WritePartialArgs{};
+  dim3 grid(n_pass_blocks + 8 * ((n_write + 7) / 8));
   const bf16* q = static_cast<const bf16*>(a.q);
   const bf16* k = static_cast<const bf16*>(a.k);
   const bf16* v = static_cast<const bf16*>(a.v);
@@ -705,20 +737,20 @@ hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const bf16* wl = static_cast<const bf16*>(a.wt_lo);
   if (a.out_bf16)
     hipLaunchKernelGGL((arl2_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T,
-                       a.H, nq, n_bh, a.scale_log2);
+                       a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write);
   else
     hipLaunchKernelGGL((arl2_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T,
-                       a.H, nq, n_bh, a.scale_log2);
+                       a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd(int d, const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd(int d, const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream) {
   switch (d) {
-    case 16: return launch_fwd_d<16>(a, stream);
-    case 64: return launch_fwd_d<64>(a, stream);
-    case 128: return launch_fwd_d<128>(a, stream);
+    case 16: return launch_fwd_d<16>(a, w, stream);
+    case 64: return launch_fwd_d<64>(a, w, stream);
+    case 128: return launch_fwd_d<128>(a, w, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,7 +54,7 @@ struct arl2_layer {
   float* s[2] = {nullptr, nullptr};  // S, fp32 [B][H][d][d], ping-pong
   int cur = 0;                       // index of S_{N-1} (the state every pass reads)
   float* partial = nullptr;          // [B][H][chunks][dp][dp]
-  void* sneg_hi = nullptr;           // -S as B fragments, bf16 [B][H][d/16][dp/32][64][8]
+  void* sneg_hi = nullptr;           // -S as B fragments, bf16 [B][H][dp/32][dp/16][64][8]
   void* sneg_lo = nullptr;
   void* wt_hi = nullptr;             // (phi_q S)^T, bf16 [B][H][d/16][dp][16] (k-step planes)
   void* wt_lo = nullptr;
@@ -109,8 +109,10 @@ arl2_status check_ptr(const void* p, const char* name) {
   return ARL2_OK;
 }
 
+// The pass kernel's launch: the pass (when out is not null) and the state write's per-chunk
+// partial sums (when w is not null).
 arl2_status launch_pass(arl2_layer* L, const void* q, const void* k, const void* v, void* out,
-                        hipStream_t stream) {
+                        const arl2::WritePartialArgs* w, hipStream_t stream) {
   arl2::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -123,7 +125,8 @@ arl2_status launch_pass(arl2_layer* L, const void* q, const void* k, const void*
   a.T = L->cfg.tokens_per_frame;
   a.scale_log2 = L->scale_log2;
   a.out_bf16 = L->cfg.out_dtype == ARL2_BF16;
-  return after_launch(L, arl2::launch_fwd(L->d, a, stream), stream, "pass kernel launch");
+  return after_launch(L, arl2::launch_fwd(L->d, a, w, stream), stream,
+                      w ? "clean pass and state write launch" : "pass kernel launch");
 }
 
 // Derive S_N = alpha S_prev + partials (chunks may be 0) into s[dst], plus its derived forms.
@@ -188,8 +191,9 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   const int64_t slice_bytes = ((int64_t)c.tokens_per_frame + 256) * c.heads * c.head_dim * 2;
   if (slice_bytes >= (int64_t(1) << 31))
     return fail(ARL2_E_UNSUPPORTED, "one stream's frame (T x H x d bf16) must stay below 2 GiB");
-  // the pass kernel runs ceil(T / 128) x B x H work-groups (rounded up to 8) in one grid dimension
-  const int64_t pass_wgs = (((int64_t)c.tokens_per_frame + 127) / 128) * c.batch * c.heads + 7;
+  // the clean pass's launch runs ceil(T / 128) x B x H work-groups for the pass and as many for
+  // the state write (each rounded up to 8) in one grid dimension
+  const int64_t pass_wgs = 2 * ((((int64_t)c.tokens_per_frame + 127) / 128) * c.batch * c.heads + 7);
   if (pass_wgs > (int64_t(1) << 24))
     return fail(ARL2_E_UNSUPPORTED, "B x H x T too large for one launch (%lld work-groups)", (long long)pass_wgs);
   arl2_status st;
@@ -223,10 +227,11 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   const size_t BH = (size_t)c.batch * c.heads, d = L->d, dp = L->dp;
   const size_t s_bytes = align_up(BH * d * d * sizeof(float));
   const size_t part_bytes = align_up(BH * L->chunks * dp * dp * sizeof(float));
-  const size_t frag_bytes = align_up(BH * d * dp * 2);   // [B][H][d/16][dp/32][64][8] bf16
+  const size_t frag_bytes = align_up(BH * dp * dp * 2);  // [B][H][dp/32][dp/16][64][8] bf16
   const size_t wt_bytes = align_up(BH * dp * d * 2);
-  const size_t map_bytes = align_up((size_t)c.heads * dp * d * 2);
-  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + 3 * map_bytes;
+  const size_t pq_bytes = align_up((size_t)c.heads * dp * d * 2);
+  const size_t map_bytes = align_up((size_t)c.heads * dp * dp * 2);
+  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + pq_bytes + 2 * map_bytes;
   if ((e = hipMalloc(&L->slab, L->bytes)) != hipSuccess) {
     (void)hipGetLastError();
     const size_t want = L->bytes;
@@ -241,7 +246,7 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   L->sneg_lo = p; p += frag_bytes;
   L->wt_hi = p; p += wt_bytes;
   L->wt_lo = p; p += wt_bytes;
-  L->pq = p; p += map_bytes;
+  L->pq = p; p += pq_bytes;
   L->pkt = p; p += map_bytes;
   L->pvt = p; p += map_bytes;
 
@@ -255,7 +260,8 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   };
   if ((e = hipEventCreateWithFlags(&L->handoff, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
   // S_0 = 0 and everything derived from it is 0 as well.
-  if ((e = hipMemsetAsync(L->slab, 0, L->bytes - 3 * map_bytes, stream)) != hipSuccess) return bail(e, "hipMemsetAsync");
+  if ((e = hipMemsetAsync(L->slab, 0, L->bytes - pq_bytes - 2 * map_bytes, stream)) != hipSuccess)
+    return bail(e, "hipMemsetAsync");
   arl2::PrepMapsArgs pm{phi_q, phi_k, phi_v, L->pq, L->pkt, L->pvt, c.heads};
   if ((e = arl2::launch_prep_maps(L->d, pm, stream)) != hipSuccess) return bail(e, "map preparation launch");
   if (debug_sync() && (e = hipStreamSynchronize(stream)) != hipSuccess) return bail(e, "map preparation");
@@ -272,7 +278,7 @@ arl2_status arl2_denoise_step(arl2_layer* L, const void* q, const void* k, const
     return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if ((st = use_stream(L, stream))) return st;
-  return launch_pass(L, q, k, v, out, stream);
+  return launch_pass(L, q, k, v, out, nullptr, stream);
 }
 
 arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
@@ -287,25 +293,22 @@ arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if ((st = use_stream(L, stream))) return st;
 
-  arl2::CommitPartialArgs pa;
-  pa.k = k;
-  pa.v = v;
-  pa.beta = beta;
-  pa.pkt = L->pkt;
-  pa.pvt = L->pvt;
-  pa.sneg_hi = L->sneg_hi;
-  pa.sneg_lo = L->sneg_lo;
-  pa.partial = L->partial;
-  pa.B = L->cfg.batch;
-  pa.H = L->cfg.heads;
-  pa.T = L->cfg.tokens_per_frame;
-  pa.knorm_eps = L->eps;
-  // The clean pass's output first, then the write, in stream order: run beside the output kernel
-  // the state write's per-chunk kernel slowed it by more than it saved (both load the memory
-  // system at their start, and the per-chunk work-groups took CUs the output kernel needed).
-  if (out && (st = launch_pass(L, q, k, v, out, stream))) return st;
-  if ((st = after_launch(L, arl2::launch_commit_partial(L->d, pa, stream), stream, "state write kernel launch")))
-    return st;
+  // One launch: the clean pass's output (when wanted) and the state write's per-chunk partial
+  // sums, the latter in work-groups that the dispatcher places after the pass's, on the CUs
+  // the pass leaves idle (as a second kernel, beside the pass on another stream or after it,
+  // the write either took CUs the pass needed or added its whole time to the frame).  Then the
+  // reduce, in stream order.
+  arl2::WritePartialArgs w;
+  w.k = k;
+  w.v = v;
+  w.beta = beta;
+  w.pkt = L->pkt;
+  w.pvt = L->pvt;
+  w.sneg_hi = L->sneg_hi;
+  w.sneg_lo = L->sneg_lo;
+  w.partial = L->partial;
+  w.knorm_eps = L->eps;
+  if ((st = launch_pass(L, q, k, v, out, &w, stream))) return st;
   if ((st = launch_reduce(L, L->s[L->cur], alpha, L->chunks, L->cur ^ 1, stream))) return st;
   L->cur ^= 1;
   L->frame += 1;

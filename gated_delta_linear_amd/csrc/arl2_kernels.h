@@ -11,11 +11,28 @@ namespace arl2 {
 inline int padded_dim(int d) { return d < 32 ? 32 : d; }
 // Tokens per work-group of the state-write kernel, and the number of such chunks.
 constexpr int kCommitChunk = 128;
-inline int commit_chunks(int T) { return (T + kCommitChunk - 1) / kCommitChunk; }
+__host__ __device__ inline int commit_chunks(int T) { return (T + kCommitChunk - 1) / kCommitChunk; }
 
-// Per-pass output: out = softmax(Q K^T * scale) V + Q (phi_q S).  wt_hi / wt_lo hold
-// (phi_q S)^T split into two bf16 terms, layout [B][H][d / 16][dp][16]: W^T[j][i] at
-// [i / 16][j][i % 16] (k-step planes of the pass kernel's MFMA fragments).
+// Per-chunk partial sums of the state write, P_c = K'_c^T diag(beta_c) (V'_c - K'_c S), written
+// to partial [B][H][chunks][dp/16][dp/16][4][64] (16 x 16 blocks, each in the C-register order
+// of the 16x16 MFMA: block (r, c), register i, lane l = P[16 r + 4 (l / 16) + i][16 c + l % 16]).
+struct WritePartialArgs {
+  const void* k;
+  const void* v;
+  const float* beta;    // [B][T][H]
+  const void* pkt;      // phi_k^T, [H][dp][dp] (zero beyond d)
+  const void* pvt;      // phi_v^T, [H][dp][dp]
+  const void* sneg_hi;  // -S_{N-1} as 16x16x32 B fragments, [B][H][dp/32][dp/16][64][8]
+  const void* sneg_lo;
+  float* partial;
+  float knorm_eps;
+};
+
+// One launch of the pass kernel, with either part optional: the pass (out = softmax(Q K^T *
+// scale) V + Q (phi_q S), when a.out is not null) and the state write's per-chunk partial sums
+// (when w is not null), the latter as extra work-groups after the pass's in dispatch order.
+// wt_hi / wt_lo hold (phi_q S)^T split into two bf16 terms, layout [B][H][d / 16][dp][16]:
+// W^T[j][i] at [i / 16][j][i % 16] (k-step planes of the pass kernel's MFMA fragments).
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -27,31 +44,15 @@ struct FwdArgs {
   float scale_log2;  // softmax scale * log2(e)
   bool out_bf16;
 };
-hipError_t launch_fwd(int d, const FwdArgs& a, hipStream_t stream);
-
-// Per-chunk partial sums of the state write, P_c = K'_c^T diag(beta_c) (V'_c - K'_c S),
-// written to partial [B][H][chunks][dp][dp].
-struct CommitPartialArgs {
-  const void* k;
-  const void* v;
-  const float* beta;
-  const void* pkt;      // phi_k^T, [H][dp][d]
-  const void* pvt;      // phi_v^T, [H][dp][d]
-  const void* sneg_hi;  // -S_{N-1} as MFMA B fragments, [B][H][d/16][dp/32][64][8]
-  const void* sneg_lo;
-  float* partial;
-  int B, H, T;
-  float knorm_eps;
-};
-hipError_t launch_commit_partial(int d, const CommitPartialArgs& a, hipStream_t stream);
+hipError_t launch_fwd(int d, const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream);
 
 // S_new = alpha S_prev + sum over chunks of the partials (fixed order), then the derived
-// forms of S_new: -S_new as B fragments (hi/lo) and (phi_q S_new)^T (hi/lo).
+// forms of S_new: -S_new as 16x16x32 B fragments (hi/lo) and (phi_q S_new)^T (hi/lo).
 // alpha == nullptr means alpha = 1; chunks == 0 means no partials (used to load a state).
 struct CommitReduceArgs {
   const float* s_prev;  // [B][H][d][d]
   const float* alpha;   // [B][H] or nullptr
-  const float* partial; // [B][H][chunks][dp][dp]
+  const float* partial; // [B][H][chunks][dp/16][dp/16][4][64]
   int chunks;
   const void* pq;       // phi_q, [H][dp][d] (rows >= d zero)
   float* s_new;         // [B][H][d][d]
@@ -64,7 +65,7 @@ struct CommitReduceArgs {
 hipError_t launch_commit_reduce(int d, const CommitReduceArgs& a, hipStream_t stream);
 
 // Working layouts of the maps from the caller's phi_q, phi_k, phi_v (bf16 [H][d][d]):
-// pq = phi_q padded to [H][dp][d]; pkt = phi_k^T and pvt = phi_v^T padded to [H][dp][d].
+// pq = phi_q padded to [H][dp][d]; pkt = phi_k^T and pvt = phi_v^T padded to [H][dp][dp].
 struct PrepMapsArgs {
   const void* phi_q;
   const void* phi_k;
