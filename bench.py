@@ -16,6 +16,7 @@ layer's stream, against the bf16 MFMA peak, and the CPU oracle's rate on a bound
 
   python bench.py [--steps K] [--warmup W] [--graph] [--workload dit480p|chunked|long_stream]
   python bench.py --series            per-frame GPU time over the whole stream
+  python bench.py --compare-softmax   the retained softmax layer vs the ARL2 layer as its cache grows
   python bench.py --pmc-target        a short run for rocprofv3 counter passes (kernels + a copy)
   python bench.py --summarize-pmc DIR rocprofv3 counter CSVs -> profiles/ traffic summary
 """
@@ -325,6 +326,77 @@ def series(args):
     layer.close()
 
 
+def compare_softmax(args):
+    """The retained softmax layer (block-causal attention over its growing K/V cache) against
+    the ARL2 layer at the same shape: time per frame (4 denoising passes + clean pass, both
+    enqueued launch by launch) and device memory, with N = 0, 20 and 230 frames already cached
+    (frames 1, 21 and 231 of a stream), after the same GPU warm-up as the main bench.  Also
+    the attention kernel's MFMA rate at the longest cache."""
+    import torch
+
+    from gated_delta_linear_amd import SoftmaxLayer
+    from synth import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()  # default priority
+    timed = 4  # frames timed at each cache length
+    res = {"metric": "per-layer frame time and memory, retained softmax layer vs ARL2 layer", "workload":
+           f"{w.name}: {w.batch} x {w.heads} heads x {w.tokens} tokens/frame, d={w.head_dim}, "
+           f"{w.denoise_steps} denoising passes + clean pass per frame", "points": []}
+    with torch.cuda.stream(stream):
+        ring = stage_ring(w, torch)
+        layer = make_layer(w, torch)
+        out = layer.new_output()
+        run_frames(layer, ring, w, args.warmup, out, stream)
+        arl2_ms, _ = time_region(stream, torch, lambda: run_frames(layer, ring, w, 100, out, stream))
+        arl2_us = arl2_ms / 100 * 1e3
+        arl2_bytes = layer.device_bytes
+        layer.close()
+        res["arl2"] = {"frame_us": arl2_us, "device_bytes": arl2_bytes}
+        for n_cached in (0, 20, 230):
+            sm = SoftmaxLayer(w.batch, w.heads, w.head_dim, w.tokens, n_cached + timed)
+            for f in range(n_cached):  # fill the cache: clean passes without output
+                q, k, v = ring[f % RING][0][-1]
+                sm.commit_frame(q, k, v, want_output=False, stream=stream)
+
+            def frames():
+                for f in range(timed):
+                    passes = ring[(n_cached + f) % RING][0]
+                    for p, (q, k, v) in enumerate(passes):
+                        if p < w.denoise_steps:
+                            sm.denoise_step(q, k, v, out=out, stream=stream)
+                        else:
+                            sm.commit_frame(q, k, v, out=out, stream=stream)
+            ms, _ = time_region(stream, torch, frames)
+            frame_us = ms / timed * 1e3
+            # frame n_cached + f attends over (n_cached + f + 1) frames of keys; report the mean
+            point = {"frames_cached": n_cached, "frame_index_first_timed": n_cached + 1,
+                     "frame_us": frame_us, "vs_arl2_time": frame_us / arl2_us,
+                     "cache_bytes_after": (n_cached + timed) * 2 * w.batch * w.tokens * w.heads * w.head_dim * 2,
+                     "vs_arl2_memory": (n_cached + timed) * 2 * w.batch * w.tokens * w.heads * w.head_dim * 2 / arl2_bytes}
+            if n_cached == 230:
+                sm.reset()
+                for f in range(n_cached):
+                    q, k, v = ring[f % RING][0][-1]
+                    sm.commit_frame(q, k, v, want_output=False, stream=stream)
+                q, k, v = ring[0][0][0]
+                n = 10
+
+                def passes():
+                    for _ in range(n):
+                        sm.denoise_step(q, k, v, out=out, stream=stream)
+                pass_ms, _ = time_region(stream, torch, passes)
+                keys = (n_cached + 1) * w.tokens
+                flops = 4.0 * w.batch * w.heads * w.tokens * keys * w.head_dim
+                point["attention_pass_us"] = pass_ms / n * 1e3
+                point["attention_tflops"] = flops / (pass_ms / n * 1e-3) / 1e12
+                point["attention_mfma_frac"] = point["attention_tflops"] / PEAK_BF16_TFLOPS
+            res["points"].append(point)
+            sm.close()
+    print(json.dumps(res), flush=True)
+
+
 COPY_BYTES = 2**30  # calibration copy: 1 GiB each way, four times the 256 MB last-level cache
 
 
@@ -408,6 +480,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="report the HIP-graph replay rate as the value")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work (min one frame)")
     ap.add_argument("--series", action="store_true")
+    ap.add_argument("--compare-softmax", action="store_true",
+                    help="the retained softmax layer against the ARL2 layer as the K/V cache grows")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     args = ap.parse_args()
@@ -420,6 +494,8 @@ def main():
         pmc_target(args)
     elif args.series:
         series(args)
+    elif args.compare_softmax:
+        compare_softmax(args)
     else:
         bench(args)
 

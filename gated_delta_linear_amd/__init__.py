@@ -1,7 +1,8 @@
-"""ARL2 hybrid attention layer (forward hot path) for AMD Instinct MI355X (gfx950).
+"""ARL2 hybrid attention layer (forward hot path) for AMD Instinct MI355X (gfx950), and the
+retained softmax attention layer with its K/V cache that an ARL2 model keeps beside it.
 
-The computation lives in libarl2.so (HIP kernels behind the C interface of include/arl2.h);
-this package only binds it.
+The computation lives in libarl2.so (HIP kernels behind the C interfaces of include/arl2.h
+and include/arl2_softmax.h); this package only binds it.
 """
 from .arl2 import (  # noqa: F401
     ARL2_BF16,
@@ -10,6 +11,8 @@ from .arl2 import (  # noqa: F401
     Arl2Error,
     Arl2Layer,
     LIB_PATH,
+    SoftmaxConfig,
+    SoftmaxLayer,
     load_library,
     status_string,
 )

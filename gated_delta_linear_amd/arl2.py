@@ -40,6 +40,17 @@ SIGNATURES = {
     "arl2_last_error": (c_char_p, []),
 }
 
+# every function declared in include/arl2_softmax.h (the retained softmax layers)
+SOFTMAX_SIGNATURES = {
+    "arl2_softmax_layer_create": (c_int, [c_void_p, c_void_p, POINTER(c_void_p)]),
+    "arl2_softmax_pass": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_softmax_commit": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_softmax_reset": (c_int, [c_void_p]),
+    "arl2_softmax_destroy": (c_int, [c_void_p]),
+    "arl2_softmax_frame_index": (c_int64, [c_void_p]),
+    "arl2_softmax_device_bytes": (c_size_t, [c_void_p]),
+}
+
 
 class Arl2Config(Structure):
     _fields_ = [
@@ -51,6 +62,18 @@ class Arl2Config(Structure):
         ("out_dtype", c_int32),
         ("softmax_scale", c_float),
         ("knorm_eps", c_float),
+    ]
+
+
+class SoftmaxConfig(Structure):
+    _fields_ = [
+        ("batch", c_int32),
+        ("heads", c_int32),
+        ("head_dim", c_int32),
+        ("tokens_per_frame", c_int32),
+        ("max_frames", c_int32),
+        ("out_dtype", c_int32),
+        ("softmax_scale", c_float),
     ]
 
 
@@ -72,7 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_linear_amd.build` "
                            "(the ARL2 layer has no fallback implementation)")
     lib = ctypes.CDLL(path)
-    for name, (res, args) in SIGNATURES.items():
+    for name, (res, args) in {**SIGNATURES, **SOFTMAX_SIGNATURES}.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
@@ -204,6 +227,88 @@ class Arl2Layer:
         if getattr(self, "_handle", None):
             h, self._handle = self._handle, c_void_p()
             _check(self._lib.arl2_destroy(h), "arl2_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+class SoftmaxLayer:
+    """One retained softmax attention layer with its K/V cache on the current GPU (see
+    include/arl2_softmax.h): frame N's passes attend over the cached clean K/V of frames
+    0..N-1 and their own k, v; commit() caches k, v as frame N.  q, k, v are bf16 [B, T, H, d]."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, tokens: int, max_frames: int,
+                 out_dtype: torch.dtype = torch.float32, softmax_scale: float = 0.0, device=None, stream=None):
+        self._lib = load_library()
+        self._handle = c_void_p()
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+        self.batch, self.heads, self.head_dim, self.tokens = int(batch), int(heads), int(head_dim), int(tokens)
+        self.max_frames = int(max_frames)
+        self.out_dtype = out_dtype
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        cfg = SoftmaxConfig(self.batch, self.heads, self.head_dim, self.tokens, self.max_frames,
+                            ARL2_F32 if out_dtype == torch.float32 else ARL2_BF16, float(softmax_scale))
+        with torch.cuda.device(self.device):
+            st = self._lib.arl2_softmax_layer_create(byref(cfg), _stream_handle(stream), byref(self._handle))
+        _check(st, "arl2_softmax_layer_create")
+
+    @property
+    def frame_shape(self) -> tuple:
+        return (self.batch, self.tokens, self.heads, self.head_dim)
+
+    def _ptr(self):
+        if not self._handle:
+            raise Arl2Error(ARL2_E_PROTOCOL, "layer has been closed")
+        return self._handle
+
+    def new_output(self) -> torch.Tensor:
+        return torch.empty(self.frame_shape, dtype=self.out_dtype, device=self.device)
+
+    def denoise_step(self, q, k, v, out=None, stream=None) -> torch.Tensor:
+        out = self.new_output() if out is None else out
+        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        _check(self._lib.arl2_softmax_pass(self._ptr(), *args, po, _stream_handle(stream)), "arl2_softmax_pass")
+        return out
+
+    def commit_frame(self, q, k, v, out=None, want_output: bool = True, stream=None):
+        pk = _dev_tensor(k, "k", torch.bfloat16, self.frame_shape)
+        pv = _dev_tensor(v, "v", torch.bfloat16, self.frame_shape)
+        if want_output or out is not None:
+            out = self.new_output() if out is None else out
+            pq = _dev_tensor(q, "q", torch.bfloat16, self.frame_shape)
+            po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        else:
+            pq, po = None, None
+        _check(self._lib.arl2_softmax_commit(self._ptr(), pq, pk, pv, po, _stream_handle(stream)),
+               "arl2_softmax_commit")
+        return out
+
+    def reset(self) -> None:
+        _check(self._lib.arl2_softmax_reset(self._ptr()), "arl2_softmax_reset")
+
+    @property
+    def frame_index(self) -> int:
+        return int(self._lib.arl2_softmax_frame_index(self._ptr()))
+
+    @property
+    def device_bytes(self) -> int:
+        return int(self._lib.arl2_softmax_device_bytes(self._ptr()))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            h, self._handle = self._handle, c_void_p()
+            _check(self._lib.arl2_softmax_destroy(h), "arl2_softmax_destroy")
 
     def __del__(self):
         try:

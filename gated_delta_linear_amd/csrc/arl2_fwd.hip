@@ -141,11 +141,15 @@ __device__ __forceinline__ void wait_vmem_but() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-template <int D, bool OUT_BF16>
+// INTER: the ARL2 pass (the Q W term; state-write work-groups after n_pass_blocks).  Without it,
+// plain softmax attention of the T queries over keys [0, Tk) of k / v (whose stream slices are
+// kv_rows rows apart): the retained softmax layers' attention over their K/V cache.
+template <int D, bool OUT_BF16, bool INTER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
-    int T, int H, int nq, int n_bh, float scale_log2, int n_pass_blocks, const WritePartialArgs wa, int n_write) {
+    int T, int Tk, int kv_rows, int H, int nq, int n_bh, float scale_log2, int n_pass_blocks,
+    const WritePartialArgs wa, int n_write) {
   using S = FwdShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
                 KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB,
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Work-groups past the pass's: the state write's per-chunk partial sums of the clean pass's
   // launch, in the same LDS arrays (region A: the K arrays, or the exchange array where the
   // K arrays are too small; region B: the V arrays).
-  if ((int)blockIdx.x >= n_pass_blocks) {
+  if (INTER && (int)blockIdx.x >= n_pass_blocks) {
     using WS = WriteShape<D>;
     constexpr int KA_KB = KA_BYTES / 1024, VA_KB = VA_BYTES / 1024;
     constexpr bool A_IN_K = 4 * KA_KB >= WS::A_SLOTS;
@@ -222,21 +226,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave & 3, grp = wave >> 2;  // 32-row block and key half of this wave
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * T * H + h) * D;
+  const int64_t base = ((int64_t)b * T * H + h) * D;  // this (stream, head)'s queries and output
+  const int64_t kv_base = ((int64_t)b * kv_rows * H + h) * D;
   const bf16* qb = q + base;
-  const bf16* kb = k + base;
-  const bf16* vb = v + base;
+  const bf16* kb = k + kv_base;
+  const bf16* vb = v + kv_base;
 
-  // The halves split the frame's keys at 32-key units: half 0 takes the first u0 = ceil(U / 2)
+  // The halves split the keys (the frame's, or a cache's) at 32-key units: half 0 takes the first u0 = ceil(U / 2)
   // of the U units, half 1 the rest.  Every wave runs u0 pipeline steps (one per unit; the
   // work-group barriers keep the halves together), in iters full iterations of two units and,
   // for odd u0, a last single step.  Units past the end of a wave's keys (half 1's last when U
   // is odd, the one after each half's last) are masked to -inf, so they add nothing.
-  const int units = (T + kUnit - 1) / kUnit;
+  const int units = (Tk + kUnit - 1) / kUnit;
   const int u0 = (units + 1) >> 1;
   const int steps = u0, iters = steps >> 1;
   const int key0 = grp ? u0 * kUnit : 0;  // first key of this wave's half
-  const int key_end = grp ? T : min(T, u0 * kUnit);
+  const int key_end = grp ? Tk : min(Tk, u0 * kUnit);
 
   if (D < DP) {  // padded V^T rows stay zero for the whole kernel
     for (int i = tid; i < VA_BYTES / 16; i += kThreads) {
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   uint4 vreg[VPT][4];
   auto load_v = [&](int tile) ARL2_INLINE {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(vb, T, rs, D, key0 + kKV * tile);
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(vb, Tk, rs, D, key0 + kKV * tile);
 #pragma unroll
     for (int rr = 0; rr < VPT; ++rr)
 #pragma unroll
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int c = 0; c < (QI + kWaves - 1) / kWaves; ++c)
       if (wave + kWaves * c < QI) dma_k(qr, vs1, wave + kWaves * c);
-    const __amdgpu_buffer_rsrc_t r0 = rows_rsrc(kb, T, rs, D, key0);
+    const __amdgpu_buffer_rsrc_t r0 = rows_rsrc(kb, Tk, rs, D, key0);
 #pragma unroll
     for (int m = 0; m < (KS + 3) / 4; ++m)
       if (sw + 4 * m < KS) dma_k(r0, ks0 + grp * KH_BYTES, sw + 4 * m);
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int i = sw + 4 * m;
       if (i < NKI) {
         const int hh = 1 + i / KS;
-        const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, T, rs, D, key0 + kUnit * hh);
+        const __amdgpu_buffer_rsrc_t r = rows_rsrc(kb, Tk, rs, D, key0 + kUnit * hh);
         dma_k(r, (hh == 1 ? ks1 : ks2) + grp * KH_BYTES, i % KS);
       }
     }
@@ -556,9 +561,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int P = decltype(par_c)::value;
     unsigned char* kd0 = karr(Ic<2 * P + 3>()) + grp * KH_BYTES;
     unsigned char* kd1 = karr(Ic<2 * P + 4>()) + grp * KH_BYTES;
-    const __amdgpu_buffer_rsrc_t kr0 = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 3));
-    const __amdgpu_buffer_rsrc_t kr1 = rows_rsrc(kb, T, rs, D, key0 + kUnit * (2 * j + 4));
-    const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vb, T, rs, D, key0 + kKV * (j + 2));
+    const __amdgpu_buffer_rsrc_t kr0 = rows_rsrc(kb, Tk, rs, D, key0 + kUnit * (2 * j + 3));
+    const __amdgpu_buffer_rsrc_t kr1 = rows_rsrc(kb, Tk, rs, D, key0 + kUnit * (2 * j + 4));
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vb, Tk, rs, D, key0 + kKV * (j + 2));
     // The K loads are dealt over both phases of step 2j (half each, on every other stage) and the
     // V loads over both phases of step 2j + 1, so that the vector-memory path has work in every
     // phase instead of bursts in two.
@@ -609,7 +614,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     ++j;
   }
   // W^T (for the epilogue) comes into the K arrays, which the last single step does not read.
-  load_w();
+  if constexpr (INTER) load_w();
   if (steps & 1) {  // the last unit, 2j: its scores are in s0 and its V^T tile j in buffer j % 2
     if (j & 1) step(2 * j, s0, s1, Off(), On(), Ic<0>(), Ic<1>(), no_staging);
     else step(2 * j, s0, s1, Off(), On(), Ic<0>(), Ic<0>(), no_staging);
@@ -672,7 +677,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Add Q W = Q (phi_q S) with W^T split in two bf16 terms (A fragments from LDS).
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    if (mb < o0 || mb >= o0 + MBH) continue;
+    if (!INTER || mb < o0 || mb >= o0 + MBH) continue;
 #pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll
@@ -725,8 +730,10 @@ template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream) {
   const int nq = (a.T + kQTile - 1) / kQTile;
   const int n_bh = a.H * a.B;
+  const bool inter = a.Tk < 0;  // the ARL2 pass: keys are the frame's own
+  const int Tk = inter ? a.T : a.Tk, kv_rows = inter ? a.T : a.kv_rows;
   const int n_pass_blocks = a.out ? 8 * ((nq * n_bh + 7) / 8) : 0;
-  const int n_write = w ? commit_chunks(a.T) * n_bh : 0;
+  const int n_write = inter && w ? commit_chunks(a.T) * n_bh : 0;
   if (n_pass_blocks + n_write == 0) return hipSuccess;
   const WritePartialArgs wa = w ? *w : WritePartialArgs{};
   dim3 grid(n_pass_blocks + 8 * ((n_write + 7) / 8));
@@ -735,12 +742,17 @@ hipError_t launch_fwd_d(const FwdArgs& a, const WritePartialArgs* w, hipStream_t
   const bf16* v = static_cast<const bf16*>(a.v);
   const bf16* wh = static_cast<const bf16*>(a.wt_hi);
   const bf16* wl = static_cast<const bf16*>(a.wt_lo);
-  if (a.out_bf16)
-    hipLaunchKernelGGL((arl2_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T,
-                       a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write);
-  else
-    hipLaunchKernelGGL((arl2_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T,
-                       a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write);
+#define ARL2_LAUNCH_FWD(OB, IN)                                                                              \
+  hipLaunchKernelGGL((arl2_fwd_kernel<D, OB, IN>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T, Tk, \
+                     kv_rows, a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write)
+  if (inter) {
+    if (a.out_bf16) ARL2_LAUNCH_FWD(true, true);
+    else ARL2_LAUNCH_FWD(false, true);
+  } else {
+    if (a.out_bf16) ARL2_LAUNCH_FWD(true, false);
+    else ARL2_LAUNCH_FWD(false, false);
+  }
+#undef ARL2_LAUNCH_FWD
   return hipGetLastError();
 }
 

@@ -14,13 +14,13 @@
 #include <string>
 
 #include "../../include/arl2.h"
+#include "arl2_host_util.h"
 #include "arl2_kernels.h"
 
-namespace {
+namespace arl2host {
 
 thread_local std::string g_last_error;
 
-arl2_status fail(arl2_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 arl2_status fail(arl2_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -41,7 +41,13 @@ bool debug_sync() {
   return on;
 }
 
-}  // namespace
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace arl2host
+
+using arl2host::aligned16;
+using arl2host::debug_sync;
+using arl2host::fail;
 
 struct arl2_layer {
   arl2_config cfg;
@@ -167,7 +173,7 @@ const char* arl2_status_string(arl2_status st) {
   return "unknown status";
 }
 
-const char* arl2_last_error(void) { return g_last_error.c_str(); }
+const char* arl2_last_error(void) { return arl2host::last_error(); }
 
 arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const void* phi_k, const void* phi_v,
                               void* stream_, arl2_layer** out_layer) {

@@ -1,0 +1,16 @@
+// Helpers shared by the library's host files (not part of the C interface): the calling
+// thread's last-error text that arl2_last_error() returns, and argument checks.
+#pragma once
+
+#include "../../include/arl2.h"
+
+namespace arl2host {
+
+// Records a formatted detail as the calling thread's last error and returns st.
+arl2_status fail(arl2_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+const char* last_error();
+bool aligned16(const void* p);
+// ARL2_DEBUG_SYNC=1: synchronise after every launch so that a kernel fault names its call.
+bool debug_sync();
+
+}  // namespace arl2host

@@ -33,6 +33,10 @@ struct WritePartialArgs {
 // (when w is not null), the latter as extra work-groups after the pass's in dispatch order.
 // wt_hi / wt_lo hold (phi_q S)^T split into two bf16 terms, layout [B][H][d / 16][dp][16]:
 // W^T[j][i] at [i / 16][j][i % 16] (k-step planes of the pass kernel's MFMA fragments).
+//
+// With Tk >= 0 the launch is plain softmax attention instead (no Q W term, no state write): the
+// T queries of q against keys / values [0, Tk) of k / v, whose per-stream slices hold kv_rows
+// rows ([B][kv_rows][H][d]): the retained softmax layers' attention over their K/V cache.
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -43,6 +47,8 @@ struct FwdArgs {
   int B, H, T;
   float scale_log2;  // softmax scale * log2(e)
   bool out_bf16;
+  int Tk = -1;       // keys of plain attention; -1: the ARL2 pass
+  int kv_rows = 0;   // rows per stream slice of k and v (plain attention)
 };
 hipError_t launch_fwd(int d, const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream);
 
@@ -63,6 +69,18 @@ struct CommitReduceArgs {
   int B, H;
 };
 hipError_t launch_commit_reduce(int d, const CommitReduceArgs& a, hipStream_t stream);
+
+// Copy one frame's k, v ([B][T][H][d] bf16) into rows [row0, row0 + T) of the K/V caches
+// kc, vc ([B][rows][H][d] bf16).
+struct KvAppendArgs {
+  const void* k;
+  const void* v;
+  void* kc;
+  void* vc;
+  int B, H, d, T;
+  int64_t row0, rows;
+};
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 
 // Working layouts of the maps from the caller's phi_q, phi_k, phi_v (bf16 [H][d][d]):
 // pq = phi_q padded to [H][dp][d]; pkt = phi_k^T and pvt = phi_v^T padded to [H][dp][dp].

@@ -1,4 +1,4 @@
-"""CPU oracle of the ARL2 layer's forward hot path.
+"""CPU oracles of the ARL2 layer's forward hot path and of the retained softmax layer.
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
 ``cpu_baseline`` leg may import this package.  The product library never does.
@@ -11,3 +11,4 @@ from .arl2_oracle import (  # noqa: F401
     softmax_attention,
     unit_rows,
 )
+from .softmax_oracle import SoftmaxOracle, cached_attention  # noqa: F401,E402

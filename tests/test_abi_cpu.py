@@ -1,5 +1,6 @@
-"""The C interface on the CPU: the library loads, exports every function include/arl2.h
-declares, and rejects bad arguments before touching a device.  No kernel runs here."""
+"""The C interfaces on the CPU: the library loads, exports every function include/arl2.h and
+include/arl2_softmax.h declare, and rejects bad arguments before touching a device.  No
+kernel runs here."""
 import ctypes
 import os
 import re
@@ -11,6 +12,7 @@ import gated_delta_linear_amd.arl2 as A
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2.h")
+SOFTMAX_HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2_softmax.h")
 
 
 @pytest.fixture(scope="module")
@@ -21,18 +23,19 @@ def lib():
     return A.load_library()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(arl2_[a-z_]+)\s*\(", text))
 
 
 def test_header_and_binding_agree():
     assert _declared_functions() == set(A.SIGNATURES)
+    assert _declared_functions(SOFTMAX_HEADER) == set(A.SOFTMAX_SIGNATURES)
 
 
 def test_every_declared_symbol_is_exported(lib):
-    for name in _declared_functions():
+    for name in _declared_functions() | _declared_functions(SOFTMAX_HEADER):
         assert hasattr(lib, name), name
 
 
@@ -109,3 +112,41 @@ def test_create_without_device_fails_cleanly(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         A.load_library(str(tmp_path / "libarl2.so"))
+
+
+# --- the retained softmax layer (include/arl2_softmax.h) -----------------------------------
+
+def _scfg(**kw):
+    c = dict(batch=1, heads=2, head_dim=128, tokens_per_frame=64, max_frames=4, out_dtype=A.ARL2_F32,
+             softmax_scale=0.0)
+    c.update(kw)
+    return A.SoftmaxConfig(**c)
+
+
+def test_softmax_null_layer_queries(lib):
+    assert lib.arl2_softmax_frame_index(None) == -1
+    assert lib.arl2_softmax_device_bytes(None) == 0
+    assert lib.arl2_softmax_destroy(None) == A.ARL2_OK
+    assert lib.arl2_softmax_reset(None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_softmax_pass(None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_softmax_commit(None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert b"NULL" in lib.arl2_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), A.ARL2_E_INVALID_ARG),
+    (dict(heads=70000), A.ARL2_E_INVALID_ARG),
+    (dict(tokens_per_frame=0), A.ARL2_E_INVALID_ARG),
+    (dict(max_frames=0), A.ARL2_E_INVALID_ARG),
+    (dict(head_dim=32), A.ARL2_E_UNSUPPORTED),
+    (dict(out_dtype=5), A.ARL2_E_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), A.ARL2_E_INVALID_ARG),
+    # one stream's cache of K (max_frames x T x H x d bf16) reaches 2 GiB
+    (dict(max_frames=1000, tokens_per_frame=1560, heads=12), A.ARL2_E_UNSUPPORTED),
+])
+def test_softmax_create_rejects_bad_config(lib, kw, status):
+    h = ctypes.c_void_p(123)
+    assert lib.arl2_softmax_layer_create(ctypes.byref(_scfg(**kw)), None, ctypes.byref(h)) == status
+    assert not h.value
+    assert lib.arl2_softmax_layer_create(None, None, ctypes.byref(h)) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_softmax_layer_create(ctypes.byref(_scfg()), None, None) == A.ARL2_E_INVALID_ARG
