@@ -71,16 +71,24 @@ def frame_flops(w) -> float:
     return (w.denoise_steps + 1) * pass_flops(w) + commit_flops(w)
 
 
-def stage_ring(w, torch):
-    """Device-resident inputs for RING frames: per frame, each pass's q, k, v and the gates."""
-    from synth import make_gates, make_pass_inputs
+def stage_ring(w, torch, gated=False):
+    """Device-resident inputs for RING frames: per frame, each pass's q, k, v and the gates
+    (beta, alpha), or with gated, the inputs of the gate projections (hidden states x, gate
+    weights and biases, beta scale) in place of beta and alpha."""
+    from synth import make_gate_weights, make_gates, make_hidden, make_pass_inputs
 
     dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dt)
+    if gated:
+        wg, bg = make_gate_weights(w)
+        wg, bg = dev(wg, torch.bfloat16), dev(bg, torch.float32)
     ring = []
     for f in range(RING):
         passes = [tuple(dev(x, torch.bfloat16) for x in make_pass_inputs(w, f, p)) for p in range(w.denoise_steps + 1)]
-        beta, alpha = make_gates(w, f)
-        ring.append((passes, dev(beta, torch.float32), dev(alpha, torch.float32)))
+        if gated:
+            ring.append((passes, (dev(make_hidden(w, f), torch.bfloat16), wg, bg, w.beta_scale), None))
+        else:
+            beta, alpha = make_gates(w, f)
+            ring.append((passes, dev(beta, torch.float32), dev(alpha, torch.float32)))
     torch.cuda.synchronize()
     return ring
 
@@ -102,6 +110,8 @@ def run_frames(layer, ring, w, n, out, stream, first=0):
         for p, (q, k, v) in enumerate(passes):
             if p < w.denoise_steps:
                 layer.denoise_step(q, k, v, out=out, stream=stream)
+            elif alpha is None:  # gated: beta holds (x, w_gates, b_gates, beta_scale)
+                layer.commit_frame_gated(q, k, v, *beta, out=out, stream=stream)
             else:
                 layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
 
@@ -156,7 +166,9 @@ def commit_launch_us(layer, ring, w, out, stream, torch, n=16):
     def one(i):
         passes, beta, alpha = ring[i % RING]
         q, k, v = passes[-1]
-        if out is None:
+        if alpha is None:
+            layer.commit_frame_gated(q, k, v, *beta, out=out, want_output=out is not None, stream=stream)
+        elif out is None:
             layer.commit_frame(q, k, v, beta, alpha, want_output=False, stream=stream)
         else:
             layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
@@ -225,7 +237,7 @@ def bench(args):
     stream = torch.cuda.Stream()  # default priority
     with torch.cuda.stream(stream):
         layer = make_layer(w, torch)
-        ring = stage_ring(w, torch)
+        ring = stage_ring(w, torch, gated=args.gated)
         out = layer.new_output()
         run_frames(layer, ring, w, args.warmup, out, stream)
         torch.cuda.synchronize()
@@ -269,9 +281,12 @@ def bench(args):
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.batch} stream(s) x {w.heads} heads x {w.tokens} tokens/frame, d={w.head_dim}, "
-                        f"{w.denoise_steps} denoising passes + 1 clean pass with state write per frame",
+                        f"{w.denoise_steps} denoising passes + 1 clean pass with state write per frame"
+                        + (" (alpha, beta from the gate projections of the hidden states)" if args.gated else ""),
             "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "tokens_per_frame": w.tokens,
-            "denoise_steps": w.denoise_steps, "beta": f"sigmoid(N(0,1)) * {w.beta_scale:.6g}",
+            "denoise_steps": w.denoise_steps,
+            "beta": (f"{w.beta_scale:.6g} * sigmoid(x . w_beta[h] + b_beta[h]), x ~ N(0,1), w ~ N(0, 1/(H d))"
+                     if args.gated else f"sigmoid(N(0,1)) * {w.beta_scale:.6g}"),
             "input_ring_frames": RING, "launch": "hip_graph_per_frame" if use_graph else "eager",
         },
         "roofline": {
@@ -478,6 +493,8 @@ def main():
     ap.add_argument("--workload", default="dit480p", choices=["dit480p", "long_stream", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="report the HIP-graph replay rate as the value")
+    ap.add_argument("--gated", action="store_true",
+                    help="clean passes take alpha and beta from the gate projections of synthetic hidden states")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work (min one frame)")
     ap.add_argument("--series", action="store_true")
     ap.add_argument("--compare-softmax", action="store_true",

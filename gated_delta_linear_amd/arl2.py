@@ -31,6 +31,8 @@ SIGNATURES = {
     "arl2_layer_create": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_void_p)]),
     "arl2_denoise_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "arl2_commit_frame": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_commit_frame_gated": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_float, c_void_p, c_void_p]),
     "arl2_destroy": (c_int, [c_void_p]),
     "arl2_state_read": (c_int, [c_void_p, c_void_p, c_void_p]),
     "arl2_state_write": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
@@ -201,6 +203,26 @@ class Arl2Layer:
             pq, po = (q.data_ptr() if isinstance(q, torch.Tensor) else None), None
         _check(self._lib.arl2_commit_frame(self._ptr(), pq, pk, pv, pb, pa, po, _stream_handle(stream)),
                "arl2_commit_frame")
+        return out
+
+    def commit_frame_gated(self, q, k, v, x, w_gates, b_gates, beta_scale: float = 1.0, out=None,
+                           want_output: bool = True, stream=None):
+        """The clean pass with alpha and beta from the gate projections of the hidden states x
+        (bf16 [B, T, H d]); w_gates bf16 [2H, H d], b_gates fp32 [2H] (see include/arl2.h)."""
+        B, T, H, d = self.frame_shape
+        pk = _dev_tensor(k, "k", torch.bfloat16, self.frame_shape)
+        pv = _dev_tensor(v, "v", torch.bfloat16, self.frame_shape)
+        px = _dev_tensor(x, "x", torch.bfloat16, (B, T, H * d))
+        pw = _dev_tensor(w_gates, "w_gates", torch.bfloat16, (2 * H, H * d))
+        pb = _dev_tensor(b_gates, "b_gates", torch.float32, (2 * H,))
+        if want_output or out is not None:
+            out = self.new_output() if out is None else out
+            pq = _dev_tensor(q, "q", torch.bfloat16, self.frame_shape)
+            po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        else:
+            pq, po = None, None
+        _check(self._lib.arl2_commit_frame_gated(self._ptr(), pq, pk, pv, px, pw, pb, float(beta_scale), po,
+                                                 _stream_handle(stream)), "arl2_commit_frame_gated")
         return out
 
     # --- checkpoint hooks ---------------------------------------------------------------

@@ -36,7 +36,8 @@ constexpr int kReduceThreads = 512;
 
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
-    const float* __restrict__ s_prev, const float* __restrict__ alpha, const float* __restrict__ partial,
+    const float* __restrict__ s_prev, const float* __restrict__ alpha, const float* __restrict__ alpha_part,
+    const float* __restrict__ alpha_bias, int n_ablk, int T, const float* __restrict__ partial,
     int chunks, const bf16* __restrict__ pq, float* __restrict__ s_new, bf16* __restrict__ sneg_hi,
     bf16* __restrict__ sneg_lo, bf16* __restrict__ wt_hi, bf16* __restrict__ wt_lo, int H) {
   using S = CommitShape<D>;
@@ -57,7 +58,16 @@ __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
 #pragma unroll
     for (int st = 0; st < KS; ++st) af[st] = ld_bf16x8(pqh + (32 * wave + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
   }
-  const float a = alpha ? alpha[bh] : 1.f;
+  float a = alpha ? alpha[bh] : 1.f;
+  if (alpha_part) {  // the per-frame decay from the gate projection: sigmoid(mean logit + bias)
+    // every wave adds the block partials the same way: lane l the blocks l, l + 64, .. in
+    // order, then a fixed butterfly over the lanes (bitwise the same result in every wave)
+    float z = 0.f;
+    for (int j = lane; j < n_ablk; j += 64) z += alpha_part[((int64_t)b * n_ablk + j) * H + h];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
+    a = 1.f / (1.f + expf(-(z / (float)T + alpha_bias[h])));
+  }
   constexpr int kStride = DP * DP / 4;  // float4 between consecutive chunks
 
   // S_new = alpha S_prev + sum_c P_c, chunks added in a fixed order.  Each thread owns PER
@@ -188,7 +198,7 @@ template <int D>
 hipError_t launch_reduce_d(const CommitReduceArgs& a, hipStream_t stream) {
   dim3 grid(CommitShape<D>::NB, a.H, a.B);
   hipLaunchKernelGGL((arl2_commit_reduce_kernel<D>), grid, dim3(kReduceThreads), 0, stream, a.s_prev, a.alpha,
-                     a.partial, a.chunks, static_cast<const bf16*>(a.pq), a.s_new, static_cast<bf16*>(a.sneg_hi),
+                     a.alpha_part, a.alpha_bias, a.n_ablk, a.T, a.partial, a.chunks, static_cast<const bf16*>(a.pq), a.s_new, static_cast<bf16*>(a.sneg_hi),
                      static_cast<bf16*>(a.sneg_lo), static_cast<bf16*>(a.wt_hi), static_cast<bf16*>(a.wt_lo),
                      a.H);
   return hipGetLastError();

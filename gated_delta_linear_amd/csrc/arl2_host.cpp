@@ -67,6 +67,9 @@ struct arl2_layer {
   void* pq = nullptr;                // maps' working layouts, bf16 [H][dp][d]
   void* pkt = nullptr;
   void* pvt = nullptr;
+  float* gate_beta = nullptr;        // beta from the gate projection, fp32 [B][T][H]
+  float* gate_alpha = nullptr;       // alpha logit sums per 32-token block, fp32 [B][gate_blocks(T)][H]
+  int n_ablk = 0;
   int64_t frame = 0;
   bool poisoned = false;
   hipStream_t last_stream = nullptr;
@@ -135,12 +138,19 @@ arl2_status launch_pass(arl2_layer* L, const void* q, const void* k, const void*
                       w ? "clean pass and state write launch" : "pass kernel launch");
 }
 
-// Derive S_N = alpha S_prev + partials (chunks may be 0) into s[dst], plus its derived forms.
+// Derive S_N = alpha S_prev + partials (chunks may be 0) into s[dst], plus its derived forms;
+// alpha from the gate projection's partial sums when alpha_bias is not null.
 arl2_status launch_reduce(arl2_layer* L, const float* s_prev, const float* alpha, int chunks, int dst,
-                          hipStream_t stream) {
+                          hipStream_t stream, const float* alpha_bias = nullptr) {
   arl2::CommitReduceArgs r;
   r.s_prev = s_prev;
   r.alpha = alpha;
+  if (alpha_bias) {
+    r.alpha_part = L->gate_alpha;
+    r.alpha_bias = alpha_bias;
+    r.n_ablk = L->n_ablk;
+    r.T = L->cfg.tokens_per_frame;
+  }
   r.partial = L->partial;
   r.chunks = chunks;
   r.pq = L->pq;
@@ -155,6 +165,33 @@ arl2_status launch_reduce(arl2_layer* L, const float* s_prev, const float* alpha
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The clean pass's launch (output, if wanted, and the state write's per-chunk sums with beta),
+// then the reduce with alpha, or with alpha from the gate projection when alpha_bias is given.
+arl2_status commit(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
+                   const float* alpha, const float* alpha_bias, void* out, hipStream_t stream) {
+  // One launch: the clean pass's output (when wanted) and the state write's per-chunk partial
+  // sums, the latter in work-groups that the dispatcher places after the pass's, on the CUs
+  // the pass leaves idle (as a second kernel, beside the pass on another stream or after it,
+  // the write either took CUs the pass needed or added its whole time to the frame).  Then the
+  // reduce, in stream order.
+  arl2::WritePartialArgs w;
+  w.k = k;
+  w.v = v;
+  w.beta = beta;
+  w.pkt = L->pkt;
+  w.pvt = L->pvt;
+  w.sneg_hi = L->sneg_hi;
+  w.sneg_lo = L->sneg_lo;
+  w.partial = L->partial;
+  w.knorm_eps = L->eps;
+  arl2_status st;
+  if ((st = launch_pass(L, q, k, v, out, &w, stream))) return st;
+  if ((st = launch_reduce(L, L->s[L->cur], alpha, L->chunks, L->cur ^ 1, stream, alpha_bias))) return st;
+  L->cur ^= 1;
+  L->frame += 1;
+  return ARL2_OK;
+}
 
 }  // namespace
 
@@ -237,7 +274,11 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   const size_t wt_bytes = align_up(BH * dp * d * 2);
   const size_t pq_bytes = align_up((size_t)c.heads * dp * d * 2);
   const size_t map_bytes = align_up((size_t)c.heads * dp * dp * 2);
-  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + pq_bytes + 2 * map_bytes;
+  L->n_ablk = arl2::gate_blocks(c.tokens_per_frame);
+  const size_t gbeta_bytes = align_up((size_t)c.batch * c.tokens_per_frame * c.heads * sizeof(float));
+  const size_t galpha_bytes = align_up((size_t)c.batch * L->n_ablk * c.heads * sizeof(float));
+  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + gbeta_bytes + galpha_bytes + pq_bytes +
+             2 * map_bytes;
   if ((e = hipMalloc(&L->slab, L->bytes)) != hipSuccess) {
     (void)hipGetLastError();
     const size_t want = L->bytes;
@@ -252,6 +293,8 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   L->sneg_lo = p; p += frag_bytes;
   L->wt_hi = p; p += wt_bytes;
   L->wt_lo = p; p += wt_bytes;
+  L->gate_beta = reinterpret_cast<float*>(p); p += gbeta_bytes;
+  L->gate_alpha = reinterpret_cast<float*>(p); p += galpha_bytes;
   L->pq = p; p += pq_bytes;
   L->pkt = p; p += map_bytes;
   L->pvt = p; p += map_bytes;
@@ -298,27 +341,31 @@ arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const
   if (out && !aligned16(out)) return fail(ARL2_E_INVALID_ARG, "out is not 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if ((st = use_stream(L, stream))) return st;
+  return commit(L, q, k, v, beta, alpha, nullptr, out, stream);
+}
 
-  // One launch: the clean pass's output (when wanted) and the state write's per-chunk partial
-  // sums, the latter in work-groups that the dispatcher places after the pass's, on the CUs
-  // the pass leaves idle (as a second kernel, beside the pass on another stream or after it,
-  // the write either took CUs the pass needed or added its whole time to the frame).  Then the
-  // reduce, in stream order.
-  arl2::WritePartialArgs w;
-  w.k = k;
-  w.v = v;
-  w.beta = beta;
-  w.pkt = L->pkt;
-  w.pvt = L->pvt;
-  w.sneg_hi = L->sneg_hi;
-  w.sneg_lo = L->sneg_lo;
-  w.partial = L->partial;
-  w.knorm_eps = L->eps;
-  if ((st = launch_pass(L, q, k, v, out, &w, stream))) return st;
-  if ((st = launch_reduce(L, L->s[L->cur], alpha, L->chunks, L->cur ^ 1, stream))) return st;
-  L->cur ^= 1;
-  L->frame += 1;
-  return ARL2_OK;
+arl2_status arl2_commit_frame_gated(arl2_layer* L, const void* q, const void* k, const void* v, const void* x,
+                                    const void* w_gates, const float* b_gates, float beta_scale, void* out,
+                                    void* stream_) {
+  arl2_status st;
+  if ((st = check_layer(L))) return st;
+  if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(x, "x")) ||
+      (st = check_ptr(w_gates, "w_gates")))
+    return st;
+  if (!b_gates) return fail(ARL2_E_INVALID_ARG, "b_gates is NULL");
+  if (!(beta_scale >= 0.f) || !std::isfinite(beta_scale))
+    return fail(ARL2_E_INVALID_ARG, "beta_scale must be finite and >= 0");
+  if (out && (st = check_ptr(q, "q"))) return st;
+  if (out && !aligned16(out)) return fail(ARL2_E_INVALID_ARG, "out is not 16-byte aligned");
+  // the gate kernel addresses the weights [2H][H d] with 32-bit byte offsets
+  if ((int64_t)2 * L->cfg.heads * L->cfg.heads * L->d * 2 >= (int64_t(1) << 31))
+    return fail(ARL2_E_UNSUPPORTED, "gate weights (2H x H d bf16) must stay below 2 GiB");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if ((st = use_stream(L, stream))) return st;
+  arl2::GateArgs g{x, w_gates, b_gates, beta_scale, L->gate_beta, L->gate_alpha,
+                   L->cfg.batch, L->cfg.heads, L->d, L->cfg.tokens_per_frame};
+  if ((st = after_launch(L, arl2::launch_gates(g, stream), stream, "gate projection launch"))) return st;
+  return commit(L, q, k, v, L->gate_beta, nullptr, b_gates + L->cfg.heads, out, stream);
 }
 
 arl2_status arl2_destroy(arl2_layer* L) {

@@ -52,12 +52,33 @@ struct FwdArgs {
 };
 hipError_t launch_fwd(int d, const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream);
 
+// Gate projections from the hidden states x [B][T][H d] bf16 and the weights w [2H][H d] bf16
+// (rows 0..H-1 beta, H..2H-1 alpha), bias [2H] fp32: beta [B][T][H] = beta_scale *
+// sigmoid(x w_beta^T + bias), and per 16-token block the sums of x w_alpha^T over its tokens,
+// alpha_part [B][gate_blocks(T)][H].
+struct GateArgs {
+  const void* x;
+  const void* w;
+  const float* bias;
+  float beta_scale;
+  float* beta;
+  float* alpha_part;
+  int B, H, d, T;
+};
+int gate_blocks(int T);
+hipError_t launch_gates(const GateArgs& a, hipStream_t stream);
+
 // S_new = alpha S_prev + sum over chunks of the partials (fixed order), then the derived
 // forms of S_new: -S_new as 16x16x32 B fragments (hi/lo) and (phi_q S_new)^T (hi/lo).
-// alpha == nullptr means alpha = 1; chunks == 0 means no partials (used to load a state).
+// alpha == nullptr means alpha = 1, unless alpha_part is given: then alpha = sigmoid(sum of the
+// n_ablk partials / T + alpha_bias[h]) (the gate projection's per-frame decay).  chunks == 0
+// means no partials (used to load a state).
 struct CommitReduceArgs {
   const float* s_prev;  // [B][H][d][d]
   const float* alpha;   // [B][H] or nullptr
+  const float* alpha_part = nullptr;  // [B][n_ablk][H] logit sums, or nullptr
+  const float* alpha_bias = nullptr;  // [H]
+  int n_ablk = 0, T = 0;
   const float* partial; // [B][H][chunks][dp/16][dp/16][4][64]
   int chunks;
   const void* pq;       // phi_q, [H][dp][d] (rows >= d zero)

@@ -108,6 +108,20 @@ arl2_status arl2_denoise_step(arl2_layer* layer, const void* q, const void* k, c
 arl2_status arl2_commit_frame(arl2_layer* layer, const void* q, const void* k, const void* v,
                               const float* beta, const float* alpha, void* out, void* stream);
 
+/* The clean pass with alpha and beta from the layer's gate projections (section 2.1: the
+ * forget gate alpha and the learning rate beta are learned projections of the tokens; section
+ * 3: head-wise gates), computed on the device from the frame's hidden states x, bf16
+ * [B][T][H d] (the input of the QKV projection), and the caller's gate weights w_gates, bf16
+ * [2H][H d] (row h: beta of head h; row H + h: alpha of head h), and biases b_gates, fp32 [2H]:
+ *   beta[b][t][h] = beta_scale * sigmoid(x[b][t] . w_gates[h] + b_gates[h])
+ *   alpha[b][h]   = sigmoid(mean over the frame's tokens t of x[b][t] . w_gates[H + h]
+ *                           + b_gates[H + h])
+ * (one decay per stream, head and frame, as the frame-level write applies it).  Otherwise as
+ * arl2_commit_frame.  ARL2_E_UNSUPPORTED if 2H x H d x 2 bytes of weights reach 2 GiB. */
+arl2_status arl2_commit_frame_gated(arl2_layer* layer, const void* q, const void* k, const void* v,
+                                    const void* x, const void* w_gates, const float* b_gates,
+                                    float beta_scale, void* out, void* stream);
+
 /* Synchronise the last stream the layer used and free everything.  NULL is accepted. */
 arl2_status arl2_destroy(arl2_layer* layer);
 

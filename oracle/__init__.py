@@ -7,6 +7,7 @@ from .arl2_oracle import (  # noqa: F401
     Arl2Oracle,
     delta_write,
     feature_map,
+    gate_projections,
     inter_read,
     softmax_attention,
     unit_rows,

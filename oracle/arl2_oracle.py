@@ -71,6 +71,26 @@ def inter_read(q_prime: np.ndarray, s: np.ndarray) -> np.ndarray:
     return q_prime @ s
 
 
+def gate_projections(x: np.ndarray, w_gates: np.ndarray, b_gates: np.ndarray, beta_scale: float = 1.0):
+    """alpha and beta from the layer's hidden states ([TS] 2.1: the forget gate alpha and the
+    learning rate beta are learned projections of the tokens; [TS] 3: head-wise gates).
+
+    x [B, T, H d]; w_gates [2H, H d] (row h: beta of head h, row H + h: alpha of head h);
+    b_gates [2H].  beta[b, t, h] = beta_scale * sigmoid(x[b, t] . w_gates[h] + b_gates[h]).
+    The frame-level write applies one decay per (stream, head) and frame, so the per-token alpha
+    logits are averaged over the frame's tokens before the sigmoid:
+    alpha[b, h] = sigmoid(mean_t x[b, t] . w_gates[H + h] + b_gates[H + h]).
+    Returns beta [B, T, H] and alpha [B, H]."""
+    x = np.asarray(x, dtype=np.float64)
+    w_gates = np.asarray(w_gates, dtype=np.float64)
+    b_gates = np.asarray(b_gates, dtype=np.float64)
+    H = w_gates.shape[0] // 2
+    z = x @ w_gates.T  # [B, T, 2H] per-token logits
+    beta = beta_scale / (1.0 + np.exp(-(z[..., :H] + b_gates[:H])))
+    alpha = 1.0 / (1.0 + np.exp(-(z[..., H:].mean(axis=1) + b_gates[H:])))
+    return beta, alpha
+
+
 def delta_write(s: np.ndarray, k_prime: np.ndarray, v_prime: np.ndarray, beta: np.ndarray,
                 alpha: float) -> np.ndarray:
     """Gated delta-rule frame write S_N = alpha S_{N-1} + K'^T diag(beta) (V' - K' S_{N-1})

@@ -9,7 +9,9 @@ from .arl2_inputs import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    make_gate_weights,
     make_gates,
+    make_hidden,
     make_pass_inputs,
     make_phi,
     round_bf16,

@@ -27,6 +27,8 @@ import numpy as np
 _NS_PASS = 0
 _NS_GATE = 1
 _NS_PHI = 2
+_NS_HIDDEN = 3
+_NS_GATE_W = 4
 
 _T_Q, _T_K, _T_V = 0, 1, 2
 _T_ALPHA, _T_BETA = 0, 1
@@ -135,3 +137,22 @@ def make_gates(w: Workload, frame: int) -> tuple[np.ndarray, np.ndarray]:
                                                                dtype=np.float32)
     beta = (_sigmoid32(b) * np.float32(w.beta_scale)).astype(np.float32)
     return beta, alpha
+
+
+def make_hidden(w: Workload, frame: int) -> np.ndarray:
+    """Hidden states x of the clean pass of one frame (the input of the gate projections), fp32
+    [B, T, H d] ~ N(0, 1), bf16-representable when the workload feeds bf16."""
+    x = _rng(w.seed, _NS_HIDDEN, frame).standard_normal((w.batch, w.tokens, w.heads * w.head_dim),
+                                                         dtype=np.float32)
+    return round_bf16(x) if w.bf16_inputs else x
+
+
+def make_gate_weights(w: Workload) -> tuple[np.ndarray, np.ndarray]:
+    """Random-init gate projection weights fp32 [2H, H d] ~ N(0, 1 / (H d)) (so that a gate's
+    logit for N(0, 1) hidden states is about N(0, 1)), bf16-representable, and biases fp32 [2H]:
+    0 for the beta rows, 2 for the alpha rows (alpha near sigmoid(2) ~ 0.88, as make_gates)."""
+    dm = w.heads * w.head_dim
+    wt = _rng(w.seed, _NS_GATE_W, 0).standard_normal((2 * w.heads, dm), dtype=np.float32)
+    wt = wt * np.float32(1.0 / np.sqrt(dm))
+    bias = np.concatenate([np.zeros(w.heads, np.float32), np.full(w.heads, 2.0, np.float32)])
+    return (round_bf16(wt) if w.bf16_inputs else wt), bias

@@ -12,8 +12,8 @@ import numpy as np
 import torch
 
 from gated_delta_linear_amd import Arl2Layer
-from oracle import Arl2Oracle
-from synth import make_gates, make_pass_inputs, make_phi
+from oracle import Arl2Oracle, gate_projections
+from synth import make_gate_weights, make_gates, make_hidden, make_pass_inputs, make_phi
 
 OUT_TOL = 2e-2
 STATE_TOL = 1e-3
@@ -45,7 +45,7 @@ def make_pair(w, out_dtype=torch.float32):
 
 
 def run_stream(w, check_frames=None, full_output_frames=(), sample_rows=64, out_dtype=torch.float32,
-               reuse_denoise=False, frames=None):
+               reuse_denoise=False, frames=None, gated=False):
     """Run `frames` frames of workload w (4-ish denoise passes + 1 clean pass each).
 
     Outputs are compared on every pass of the frames in `check_frames` (all frames if None):
@@ -53,10 +53,15 @@ def run_stream(w, check_frames=None, full_output_frames=(), sample_rows=64, out_
     `sample_rows` seeded random token rows.  The state is compared after every frame.
     With reuse_denoise, denoising passes reuse the clean pass's inputs (for long streams,
     where generating unique denoise inputs would dominate; S does not depend on them).
+    With gated, the clean pass takes alpha and beta from the gate projections of the frame's
+    hidden states (commit_frame_gated; the oracle's gate_projections on the same inputs).
     Returns dict(out_err=max over checks, state_err=list per frame)."""
     frames = w.frames if frames is None else frames
     layer, orc = make_pair(w, out_dtype)
     rng = np.random.default_rng(w.seed + 1000)
+    if gated:
+        wg, bg = make_gate_weights(w)
+        wg_d, bg_d = dev(wg, torch.bfloat16), dev(bg, torch.float32)
     worst_out, state_errs = 0.0, []
     try:
         for f in range(frames):
@@ -68,7 +73,12 @@ def run_stream(w, check_frames=None, full_output_frames=(), sample_rows=64, out_
                 is_clean = p == w.denoise_steps
                 q, k, v = clean if (is_clean or reuse_denoise) else make_pass_inputs(w, f, p)
                 qd, kd, vd = (dev(x, torch.bfloat16) for x in (q, k, v))
-                if is_clean:
+                if is_clean and gated:
+                    x = make_hidden(w, f)
+                    beta, alpha = gate_projections(x, wg, bg, w.beta_scale)
+                    got = layer.commit_frame_gated(qd, kd, vd, dev(x, torch.bfloat16), wg_d, bg_d, w.beta_scale,
+                                                   want_output=check)
+                elif is_clean:
                     beta, alpha = make_gates(w, f)
                     got = layer.commit_frame(qd, kd, vd, dev(beta, torch.float32), dev(alpha, torch.float32),
                                              want_output=check)

@@ -51,6 +51,8 @@ def test_null_layer_queries(lib):
     assert lib.arl2_destroy(None) == A.ARL2_OK
     assert lib.arl2_denoise_step(None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
     assert lib.arl2_commit_frame(None, None, None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_commit_frame_gated(None, None, None, None, None, None, None, 1.0, None, None) == \
+        A.ARL2_E_INVALID_ARG
     assert lib.arl2_state_read(None, None, None) == A.ARL2_E_INVALID_ARG
     assert lib.arl2_state_write(None, None, 0, None) == A.ARL2_E_INVALID_ARG
     assert b"NULL" in lib.arl2_last_error()
