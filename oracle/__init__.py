@@ -13,3 +13,4 @@ from .arl2_oracle import (  # noqa: F401
     unit_rows,
 )
 from .softmax_oracle import SoftmaxOracle, cached_attention  # noqa: F401,E402
+from .seq_oracle import Arl2SeqOracle, sequential_frame, sequential_frame_chunked  # noqa: F401,E402
