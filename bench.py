@@ -93,12 +93,12 @@ def stage_ring(w, torch, gated=False):
     return ring
 
 
-def make_layer(w, torch):
+def make_layer(w, torch, access="frame"):
     from gated_delta_linear_amd import Arl2Layer
     from synth import make_phi
 
     phis = [torch.from_numpy(p).to("cuda").to(torch.bfloat16) for p in make_phi(w)]
-    return Arl2Layer(*phis, batch=w.batch, tokens=w.tokens)
+    return Arl2Layer(*phis, batch=w.batch, tokens=w.tokens, access=access)
 
 
 def run_frames(layer, ring, w, n, out, stream, first=0):
@@ -108,7 +108,12 @@ def run_frames(layer, ring, w, n, out, stream, first=0):
     for i in range(n):
         passes, beta, alpha = ring[(first + i) % RING]
         for p, (q, k, v) in enumerate(passes):
-            if p < w.denoise_steps:
+            if layer.access == "token":  # the sequential A/B variant: every pass needs beta
+                if p < w.denoise_steps:
+                    layer.denoise_step_seq(q, k, v, beta, out=out, stream=stream)
+                else:
+                    layer.commit_frame_seq(q, k, v, beta, alpha, out=out, stream=stream)
+            elif p < w.denoise_steps:
                 layer.denoise_step(q, k, v, out=out, stream=stream)
             elif alpha is None:  # gated: beta holds (x, w_gates, b_gates, beta_scale)
                 layer.commit_frame_gated(q, k, v, *beta, out=out, stream=stream)
@@ -146,14 +151,18 @@ def pass_launch_us(layer, ring, w, out, stream, torch, n=40):
     """Average duration of the pass kernel: HIP events around n back-to-back denoising-pass
     launches on the layer's stream (an event pair around every launch would add its own queue
     overhead to each)."""
-    for i in range(4):
+    def one(i):
         q, k, v = ring[i % RING][0][i % w.denoise_steps]
-        layer.denoise_step(q, k, v, out=out, stream=stream)
+        if layer.access == "token":
+            layer.denoise_step_seq(q, k, v, ring[i % RING][1], out=out, stream=stream)
+        else:
+            layer.denoise_step(q, k, v, out=out, stream=stream)
+    for i in range(4):
+        one(i)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for i in range(n):
-        q, k, v = ring[i % RING][0][i % w.denoise_steps]
-        layer.denoise_step(q, k, v, out=out, stream=stream)
+        one(i)
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / n
@@ -166,7 +175,9 @@ def commit_launch_us(layer, ring, w, out, stream, torch, n=16):
     def one(i):
         passes, beta, alpha = ring[i % RING]
         q, k, v = passes[-1]
-        if alpha is None:
+        if layer.access == "token":
+            layer.commit_frame_seq(q, k, v, beta, alpha, out=out, want_output=out is not None, stream=stream)
+        elif alpha is None:
             layer.commit_frame_gated(q, k, v, *beta, out=out, want_output=out is not None, stream=stream)
         elif out is None:
             layer.commit_frame(q, k, v, beta, alpha, want_output=False, stream=stream)
@@ -236,7 +247,7 @@ def bench(args):
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()  # default priority
     with torch.cuda.stream(stream):
-        layer = make_layer(w, torch)
+        layer = make_layer(w, torch, access=args.access)
         ring = stage_ring(w, torch, gated=args.gated)
         out = layer.new_output()
         run_frames(layer, ring, w, args.warmup, out, stream)
@@ -282,7 +293,8 @@ def bench(args):
         "config": {
             "workload": f"{w.name}: {w.batch} stream(s) x {w.heads} heads x {w.tokens} tokens/frame, d={w.head_dim}, "
                         f"{w.denoise_steps} denoising passes + 1 clean pass with state write per frame"
-                        + (" (alpha, beta from the gate projections of the hidden states)" if args.gated else ""),
+                        + (" (alpha, beta from the gate projections of the hidden states)" if args.gated else "")
+                        + (" [token-level access: the sequential A/B variant]" if args.access == "token" else ""),
             "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "tokens_per_frame": w.tokens,
             "denoise_steps": w.denoise_steps,
             "beta": (f"{w.beta_scale:.6g} * sigmoid(x . w_beta[h] + b_beta[h]), x ~ N(0,1), w ~ N(0, 1/(H d))"
@@ -493,6 +505,8 @@ def main():
     ap.add_argument("--workload", default="dit480p", choices=["dit480p", "long_stream", "chunked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="report the HIP-graph replay rate as the value")
+    ap.add_argument("--access", default="frame", choices=["frame", "token"],
+                    help="token: the sequential (token-level access) variant, for the A/B against the method")
     ap.add_argument("--gated", action="store_true",
                     help="clean passes take alpha and beta from the gate projections of synthetic hidden states")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work (min one frame)")
@@ -502,6 +516,8 @@ def main():
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     args = ap.parse_args()
+    if args.gated and args.access == "token":
+        sys.exit("--gated applies to frame-level access only")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         sys.exit("bench.py measures one GPU: this layer runs without sharding or collectives on a "
                  "single MI355X; --gpus must be 1")

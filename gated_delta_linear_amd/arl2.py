@@ -24,6 +24,8 @@ ARL2_E_HIP = 5
 ARL2_E_PROTOCOL = 6
 ARL2_BF16 = 0
 ARL2_F32 = 1
+ARL2_ACCESS_FRAME = 0
+ARL2_ACCESS_TOKEN = 1
 ARL2_MAX_TOKENS = 1 << 20
 
 # every function declared in include/arl2.h, with its ctypes signature
@@ -33,6 +35,9 @@ SIGNATURES = {
     "arl2_commit_frame": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "arl2_commit_frame_gated": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_float, c_void_p, c_void_p]),
+    "arl2_denoise_step_seq": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_commit_frame_seq": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p]),
     "arl2_destroy": (c_int, [c_void_p]),
     "arl2_state_read": (c_int, [c_void_p, c_void_p, c_void_p]),
     "arl2_state_write": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
@@ -64,6 +69,7 @@ class Arl2Config(Structure):
         ("out_dtype", c_int32),
         ("softmax_scale", c_float),
         ("knorm_eps", c_float),
+        ("access", c_int32),
     ]
 
 
@@ -146,7 +152,7 @@ class Arl2Layer:
 
     def __init__(self, phi_q: torch.Tensor, phi_k: torch.Tensor, phi_v: torch.Tensor, batch: int, tokens: int,
                  out_dtype: torch.dtype = torch.float32, softmax_scale: float = 0.0, knorm_eps: float = 0.0,
-                 stream=None):
+                 stream=None, access: str = "frame"):
         self._lib = load_library()
         self._handle = c_void_p()
         heads, d, _ = phi_q.shape
@@ -157,8 +163,12 @@ class Arl2Layer:
         self.batch, self.heads, self.head_dim, self.tokens = int(batch), int(heads), int(d), int(tokens)
         self.out_dtype = out_dtype
         self.device = phi_q.device
+        if access not in ("frame", "token"):
+            raise ValueError("access must be 'frame' or 'token'")
+        self.access = access
         cfg = Arl2Config(self.batch, self.heads, self.head_dim, self.tokens, ARL2_BF16,
-                         ARL2_F32 if out_dtype == torch.float32 else ARL2_BF16, float(softmax_scale), float(knorm_eps))
+                         ARL2_F32 if out_dtype == torch.float32 else ARL2_BF16, float(softmax_scale), float(knorm_eps),
+                         ARL2_ACCESS_FRAME if access == "frame" else ARL2_ACCESS_TOKEN)
         with torch.cuda.device(self.device):
             st = self._lib.arl2_layer_create(byref(cfg), phi_q.data_ptr(), phi_k.data_ptr(), phi_v.data_ptr(),
                                              _stream_handle(stream), byref(self._handle))
@@ -223,6 +233,30 @@ class Arl2Layer:
             pq, po = None, None
         _check(self._lib.arl2_commit_frame_gated(self._ptr(), pq, pk, pv, px, pw, pb, float(beta_scale), po,
                                                  _stream_handle(stream)), "arl2_commit_frame_gated")
+        return out
+
+    # --- token-level access (access="token") --------------------------------------------
+    def denoise_step_seq(self, q, k, v, beta, out=None, stream=None) -> torch.Tensor:
+        B, T, H, _ = self.frame_shape
+        out = self.new_output() if out is None else out
+        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
+        po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        _check(self._lib.arl2_denoise_step_seq(self._ptr(), *args, pb, po, _stream_handle(stream)),
+               "arl2_denoise_step_seq")
+        return out
+
+    def commit_frame_seq(self, q, k, v, beta, alpha, out=None, want_output: bool = True, stream=None):
+        B, T, H, _ = self.frame_shape
+        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
+        pa = _dev_tensor(alpha, "alpha", torch.float32, (B, H))
+        po = None
+        if want_output or out is not None:
+            out = self.new_output() if out is None else out
+            po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
+        _check(self._lib.arl2_commit_frame_seq(self._ptr(), *args, pb, pa, po, _stream_handle(stream)),
+               "arl2_commit_frame_seq")
         return out
 
     # --- checkpoint hooks ---------------------------------------------------------------

@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
 template <int D>
 __global__ void arl2_prep_maps_kernel(const bf16* __restrict__ phi_q, const bf16* __restrict__ phi_k,
                                       const bf16* __restrict__ phi_v, bf16* __restrict__ pq, bf16* __restrict__ pkt,
-                                      bf16* __restrict__ pvt, int H) {
+                                      bf16* __restrict__ pvt, bf16* __restrict__ pqt, int H) {
   constexpr int DP = CommitShape<D>::DP;
   // pq [H][DP][D]: phi_q with zero rows past d
   const int64_t nq = (int64_t)H * DP * D;
@@ -191,6 +191,7 @@ __global__ void arl2_prep_maps_kernel(const bf16* __restrict__ phi_q, const bf16
     const int64_t srt = (hh * D + col) * D + row;  // phi[h][col][row]
     pkt[e] = ok ? phi_k[srt] : (bf16)0.f;
     pvt[e] = ok ? phi_v[srt] : (bf16)0.f;
+    pqt[e] = ok ? phi_q[srt] : (bf16)0.f;
   }
 }
 
@@ -211,7 +212,7 @@ hipError_t launch_prep_d(const PrepMapsArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((arl2_prep_maps_kernel<D>), dim3(blocks), dim3(256), 0, stream,
                      static_cast<const bf16*>(a.phi_q), static_cast<const bf16*>(a.phi_k),
                      static_cast<const bf16*>(a.phi_v), static_cast<bf16*>(a.pq), static_cast<bf16*>(a.pkt),
-                     static_cast<bf16*>(a.pvt), a.H);
+                     static_cast<bf16*>(a.pvt), static_cast<bf16*>(a.pqt), a.H);
   return hipGetLastError();
 }
 

@@ -143,13 +143,15 @@ __device__ __forceinline__ void wait_vmem_but() {
 
 // INTER: the ARL2 pass (the Q W term; state-write work-groups after n_pass_blocks).  Without it,
 // plain softmax attention of the T queries over keys [0, Tk) of k / v (whose stream slices are
-// kv_rows rows apart): the retained softmax layers' attention over their K/V cache.
+// kv_rows rows apart): the retained softmax layers' attention over their K/V cache, or, with
+// `add` (fp32, the output's layout) added to the result, the softmax branch of the
+// token-level access variant.
 template <int D, bool OUT_BF16, bool INTER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
     int T, int Tk, int kv_rows, int H, int nq, int n_bh, float scale_log2, int n_pass_blocks,
-    const WritePartialArgs wa, int n_write) {
+    const WritePartialArgs wa, int n_write, const float* __restrict__ add) {
   using S = FwdShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
                 KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB,
@@ -711,9 +713,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int i = 0; i < 32 / RPS; ++i) {
     const int r = RPS * i + lane / OC, c = lane % OC;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC)));
+    f32x4 x = *reinterpret_cast<const f32x4*>(ost + r * ORB + 16 * (c ^ (r % OC)));
     if (row0 + r < T) {
       const int64_t o = base + (int64_t)(row0 + r) * rs + 32 * o0 + 4 * c;
+      if (!INTER && add) x += *reinterpret_cast<const f32x4*>(add + o);
       if (OUT_BF16) {
         bf16x4 w;
 #pragma unroll
@@ -744,7 +747,7 @@ hipError_t launch_fwd_d(const FwdArgs& a, const WritePartialArgs* w, hipStream_t
   const bf16* wl = static_cast<const bf16*>(a.wt_lo);
 #define ARL2_LAUNCH_FWD(OB, IN)                                                                              \
   hipLaunchKernelGGL((arl2_fwd_kernel<D, OB, IN>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T, Tk, \
-                     kv_rows, a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write)
+                     kv_rows, a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write, a.add)
   if (inter) {
     if (a.out_bf16) ARL2_LAUNCH_FWD(true, true);
     else ARL2_LAUNCH_FWD(false, true);

@@ -67,6 +67,9 @@ struct arl2_layer {
   void* pq = nullptr;                // maps' working layouts, bf16 [H][dp][d]
   void* pkt = nullptr;
   void* pvt = nullptr;
+  void* pqt = nullptr;               // phi_q^T, bf16 [H][dp][dp]
+  void* seq_ws = nullptr;            // token-level access: chunk operands of the scan
+  float* o_inter = nullptr;          // token-level access: inter-frame reads, fp32 [B][T][H][d]
   float* gate_beta = nullptr;        // beta from the gate projection, fp32 [B][T][H]
   float* gate_alpha = nullptr;       // alpha logit sums per 32-token block, fp32 [B][gate_blocks(T)][H]
   int n_ablk = 0;
@@ -110,6 +113,13 @@ arl2_status check_layer(arl2_layer* L) {
   if (!L) return fail(ARL2_E_INVALID_ARG, "layer is NULL");
   if (L->poisoned) return fail(ARL2_E_PROTOCOL, "layer is poisoned by an earlier failure; restore a state first");
   return ARL2_OK;
+}
+
+arl2_status check_access(arl2_layer* L, int access) {
+  if (L->cfg.access == access) return ARL2_OK;
+  return fail(ARL2_E_INVALID_ARG, access == ARL2_ACCESS_FRAME
+                                      ? "the layer uses token-level access: call the *_seq entry points"
+                                      : "the layer uses frame-level access: the *_seq entry points do not apply");
 }
 
 arl2_status check_ptr(const void* p, const char* name) {
@@ -225,6 +235,9 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   if (c.head_dim != 16 && c.head_dim != 64 && c.head_dim != 128)
     return fail(ARL2_E_UNSUPPORTED, "head_dim %d not supported (16, 64, 128)", c.head_dim);
   if (c.io_dtype != ARL2_BF16) return fail(ARL2_E_UNSUPPORTED, "io_dtype must be ARL2_BF16");
+  if (c.access != ARL2_ACCESS_FRAME && c.access != ARL2_ACCESS_TOKEN) return fail(ARL2_E_INVALID_ARG, "bad access");
+  if (c.access == ARL2_ACCESS_TOKEN && c.head_dim == 16)
+    return fail(ARL2_E_UNSUPPORTED, "token-level access supports head_dim 64 and 128");
   if (c.out_dtype != ARL2_F32 && c.out_dtype != ARL2_BF16) return fail(ARL2_E_INVALID_ARG, "bad out_dtype");
   if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
     return fail(ARL2_E_INVALID_ARG, "softmax_scale must be finite and >= 0");
@@ -277,8 +290,11 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   L->n_ablk = arl2::gate_blocks(c.tokens_per_frame);
   const size_t gbeta_bytes = align_up((size_t)c.batch * c.tokens_per_frame * c.heads * sizeof(float));
   const size_t galpha_bytes = align_up((size_t)c.batch * L->n_ablk * c.heads * sizeof(float));
-  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + gbeta_bytes + galpha_bytes + pq_bytes +
-             2 * map_bytes;
+  const bool seq = c.access == ARL2_ACCESS_TOKEN;
+  const size_t seqws_bytes = seq ? align_up(arl2::seq_workspace_bytes(L->d, c.batch, c.heads, c.tokens_per_frame)) : 0;
+  const size_t oint_bytes = seq ? align_up((size_t)c.batch * c.tokens_per_frame * c.heads * d * sizeof(float)) : 0;
+  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + gbeta_bytes + galpha_bytes + seqws_bytes +
+             oint_bytes + pq_bytes + 3 * map_bytes;
   if ((e = hipMalloc(&L->slab, L->bytes)) != hipSuccess) {
     (void)hipGetLastError();
     const size_t want = L->bytes;
@@ -295,9 +311,14 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   L->wt_lo = p; p += wt_bytes;
   L->gate_beta = reinterpret_cast<float*>(p); p += gbeta_bytes;
   L->gate_alpha = reinterpret_cast<float*>(p); p += galpha_bytes;
+  if (seq) {
+    L->seq_ws = p; p += seqws_bytes;
+    L->o_inter = reinterpret_cast<float*>(p); p += oint_bytes;
+  }
   L->pq = p; p += pq_bytes;
   L->pkt = p; p += map_bytes;
   L->pvt = p; p += map_bytes;
+  L->pqt = p; p += map_bytes;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   auto bail = [&](hipError_t err, const char* what) {
@@ -309,9 +330,9 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   };
   if ((e = hipEventCreateWithFlags(&L->handoff, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
   // S_0 = 0 and everything derived from it is 0 as well.
-  if ((e = hipMemsetAsync(L->slab, 0, L->bytes - pq_bytes - 2 * map_bytes, stream)) != hipSuccess)
+  if ((e = hipMemsetAsync(L->slab, 0, L->bytes - pq_bytes - 3 * map_bytes, stream)) != hipSuccess)
     return bail(e, "hipMemsetAsync");
-  arl2::PrepMapsArgs pm{phi_q, phi_k, phi_v, L->pq, L->pkt, L->pvt, c.heads};
+  arl2::PrepMapsArgs pm{phi_q, phi_k, phi_v, L->pq, L->pkt, L->pvt, L->pqt, c.heads};
   if ((e = arl2::launch_prep_maps(L->d, pm, stream)) != hipSuccess) return bail(e, "map preparation launch");
   if (debug_sync() && (e = hipStreamSynchronize(stream)) != hipSuccess) return bail(e, "map preparation");
   L->last_stream = stream;
@@ -322,7 +343,7 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
 
 arl2_status arl2_denoise_step(arl2_layer* L, const void* q, const void* k, const void* v, void* out, void* stream_) {
   arl2_status st;
-  if ((st = check_layer(L))) return st;
+  if ((st = check_layer(L)) || (st = check_access(L, ARL2_ACCESS_FRAME))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
     return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -330,10 +351,82 @@ arl2_status arl2_denoise_step(arl2_layer* L, const void* q, const void* k, const
   return launch_pass(L, q, k, v, out, nullptr, stream);
 }
 
+// Token-level access: the chunked recurrence (inter-frame reads into o_inter, and S_N into the
+// other state buffer when alpha is given), then, if out, the softmax branch plus o_inter.
+static arl2_status seq_pass(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
+                            const float* alpha, void* out, hipStream_t stream) {
+  arl2_status st;
+  arl2::SeqArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.pqt = L->pqt;
+  a.pkt = L->pkt;
+  a.pvt = L->pvt;
+  a.ws = L->seq_ws;
+  a.s_prev = L->s[L->cur];
+  a.alpha = alpha;
+  a.s_new = alpha ? L->s[L->cur ^ 1] : nullptr;
+  a.o_inter = L->o_inter;
+  a.B = L->cfg.batch;
+  a.H = L->cfg.heads;
+  a.T = L->cfg.tokens_per_frame;
+  a.eps = L->eps;
+  // (q is read by the recurrence for Q'; with no output the clean pass still needs it)
+  if ((st = after_launch(L, arl2::launch_seq(L->d, a, stream), stream, "token-level recurrence launch"))) return st;
+  if (!out) return ARL2_OK;
+  arl2::FwdArgs f;
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.wt_hi = nullptr;
+  f.wt_lo = nullptr;
+  f.out = out;
+  f.B = L->cfg.batch;
+  f.H = L->cfg.heads;
+  f.T = L->cfg.tokens_per_frame;
+  f.scale_log2 = L->scale_log2;
+  f.out_bf16 = L->cfg.out_dtype == ARL2_BF16;
+  f.Tk = f.T;
+  f.kv_rows = f.T;
+  f.add = L->o_inter;
+  return after_launch(L, arl2::launch_fwd(L->d, f, nullptr, stream), stream, "pass kernel launch");
+}
+
+arl2_status arl2_denoise_step_seq(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
+                                  void* out, void* stream_) {
+  arl2_status st;
+  if ((st = check_layer(L)) || (st = check_access(L, ARL2_ACCESS_TOKEN))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(beta, "beta")) || (st = check_ptr(out, "out")))
+    return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if ((st = use_stream(L, stream))) return st;
+  return seq_pass(L, q, k, v, beta, nullptr, out, stream);
+}
+
+arl2_status arl2_commit_frame_seq(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
+                                  const float* alpha, void* out, void* stream_) {
+  arl2_status st;
+  if ((st = check_layer(L)) || (st = check_access(L, ARL2_ACCESS_TOKEN))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(beta, "beta")) || (st = check_ptr(alpha, "alpha")))
+    return st;
+  if (out && !aligned16(out)) return fail(ARL2_E_INVALID_ARG, "out is not 16-byte aligned");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if ((st = use_stream(L, stream))) return st;
+  if ((st = seq_pass(L, q, k, v, beta, alpha, out, stream))) return st;
+  // derived forms of S_N are only read by frame-level passes; the state buffers swap
+  L->cur ^= 1;
+  L->frame += 1;
+  return ARL2_OK;
+}
+
 arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const void* v, const float* beta,
                               const float* alpha, void* out, void* stream_) {
   arl2_status st;
-  if ((st = check_layer(L))) return st;
+  if ((st = check_layer(L)) || (st = check_access(L, ARL2_ACCESS_FRAME))) return st;
   if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(beta, "beta")) ||
       (st = check_ptr(alpha, "alpha")))
     return st;
@@ -348,7 +441,7 @@ arl2_status arl2_commit_frame_gated(arl2_layer* L, const void* q, const void* k,
                                     const void* w_gates, const float* b_gates, float beta_scale, void* out,
                                     void* stream_) {
   arl2_status st;
-  if ((st = check_layer(L))) return st;
+  if ((st = check_layer(L)) || (st = check_access(L, ARL2_ACCESS_FRAME))) return st;
   if ((st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(x, "x")) ||
       (st = check_ptr(w_gates, "w_gates")))
     return st;

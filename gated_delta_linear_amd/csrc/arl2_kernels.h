@@ -49,6 +49,7 @@ struct FwdArgs {
   bool out_bf16;
   int Tk = -1;       // keys of plain attention; -1: the ARL2 pass
   int kv_rows = 0;   // rows per stream slice of k and v (plain attention)
+  const float* add = nullptr;  // plain attention: fp32 [B][T][H][d] added to the output, or null
 };
 hipError_t launch_fwd(int d, const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream);
 
@@ -91,6 +92,30 @@ struct CommitReduceArgs {
 };
 hipError_t launch_commit_reduce(int d, const CommitReduceArgs& a, hipStream_t stream);
 
+// Token-level (sequential) access variant, the inter-frame part of one pass: per (stream, head)
+// the chunked recurrence over the frame's tokens from S_{N-1} = s_prev, writing o_inter
+// [B][T][H][d] fp32 (q'_t S^(t-1)) and, if s_new is not null, S_N = S^(T) - (1 - alpha) S_{N-1}
+// into s_new [B][H][d][d].  ws: workspace of seq_workspace_bytes(d, B, H, T).  d = 64 or 128.
+struct SeqArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;  // [B][T][H]
+  const void* pqt;    // phi_q^T [H][d][d]
+  const void* pkt;
+  const void* pvt;
+  void* ws;
+  const float* s_prev;
+  const float* alpha;  // [B][H] (used with s_new)
+  float* s_new;
+  float* o_inter;
+  int B, H, T;
+  float eps;
+};
+int seq_chunks(int T);
+size_t seq_workspace_bytes(int d, int B, int H, int T);
+hipError_t launch_seq(int d, const SeqArgs& a, hipStream_t stream);
+
 // Copy one frame's k, v ([B][T][H][d] bf16) into rows [row0, row0 + T) of the K/V caches
 // kc, vc ([B][rows][H][d] bf16).
 struct KvAppendArgs {
@@ -104,7 +129,8 @@ struct KvAppendArgs {
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 
 // Working layouts of the maps from the caller's phi_q, phi_k, phi_v (bf16 [H][d][d]):
-// pq = phi_q padded to [H][dp][d]; pkt = phi_k^T and pvt = phi_v^T padded to [H][dp][dp].
+// pq = phi_q padded to [H][dp][d]; pkt = phi_k^T, pvt = phi_v^T and pqt = phi_q^T padded to
+// [H][dp][dp].
 struct PrepMapsArgs {
   const void* phi_q;
   const void* phi_k;
@@ -112,6 +138,7 @@ struct PrepMapsArgs {
   void* pq;
   void* pkt;
   void* pvt;
+  void* pqt;
   int H;
 };
 hipError_t launch_prep_maps(int d, const PrepMapsArgs& a, hipStream_t stream);

@@ -84,7 +84,18 @@ typedef struct {
   int32_t out_dtype;        /* ARL2_F32 (recommended) or ARL2_BF16 (round to nearest even) */
   float softmax_scale;      /* 0 selects 1/sqrt(d) */
   float knorm_eps;          /* 0 selects 1e-6 */
+  int32_t access;           /* ARL2_ACCESS_FRAME (the method) or ARL2_ACCESS_TOKEN (the sequential
+                               variant the pages reject, for A/B; head_dim 64 or 128) */
 } arl2_config;
+
+/* Frame-level access: every token of a frame reads S_{N-1} and the write takes every token's
+ * residual against it (section 2.2).  Token-level access: token t reads, and takes its residual
+ * against, the state updated by the frame's earlier tokens,
+ *   o_t = softmax branch_t + (q_t phi_q) S^(t-1),  S^(0) = S_{N-1},
+ *   S^(t) = S^(t-1) + beta_t k'_t^T (v'_t - k'_t S^(t-1)),  clean pass: S_N = S^(T) - (1 - alpha) S_{N-1};
+ * every pass needs beta, so such a layer runs arl2_denoise_step_seq / arl2_commit_frame_seq
+ * instead of arl2_denoise_step / arl2_commit_frame (ARL2_E_INVALID_ARG either way round). */
+enum { ARL2_ACCESS_FRAME = 0, ARL2_ACCESS_TOKEN = 1 };
 
 #define ARL2_MAX_TOKENS (1 << 20)
 
@@ -121,6 +132,14 @@ arl2_status arl2_commit_frame(arl2_layer* layer, const void* q, const void* k, c
 arl2_status arl2_commit_frame_gated(arl2_layer* layer, const void* q, const void* k, const void* v,
                                     const void* x, const void* w_gates, const float* b_gates,
                                     float beta_scale, void* out, void* stream);
+
+/* Token-level access layers: a denoising pass (beta [B][T][H] of the pass's tokens; the state is
+ * not written) and the clean pass (writes S_N with beta and alpha [B][H], then advances the frame
+ * index; `out` may be NULL; q is always read, by the recurrence). */
+arl2_status arl2_denoise_step_seq(arl2_layer* layer, const void* q, const void* k, const void* v,
+                                  const float* beta, void* out, void* stream);
+arl2_status arl2_commit_frame_seq(arl2_layer* layer, const void* q, const void* k, const void* v,
+                                  const float* beta, const float* alpha, void* out, void* stream);
 
 /* Synchronise the last stream the layer used and free everything.  NULL is accepted. */
 arl2_status arl2_destroy(arl2_layer* layer);

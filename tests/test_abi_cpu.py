@@ -53,6 +53,8 @@ def test_null_layer_queries(lib):
     assert lib.arl2_commit_frame(None, None, None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
     assert lib.arl2_commit_frame_gated(None, None, None, None, None, None, None, 1.0, None, None) == \
         A.ARL2_E_INVALID_ARG
+    assert lib.arl2_denoise_step_seq(None, None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_commit_frame_seq(None, None, None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
     assert lib.arl2_state_read(None, None, None) == A.ARL2_E_INVALID_ARG
     assert lib.arl2_state_write(None, None, 0, None) == A.ARL2_E_INVALID_ARG
     assert b"NULL" in lib.arl2_last_error()
@@ -60,7 +62,7 @@ def test_null_layer_queries(lib):
 
 def _cfg(**kw):
     c = dict(batch=1, heads=2, head_dim=128, tokens_per_frame=64, io_dtype=A.ARL2_BF16, out_dtype=A.ARL2_F32,
-             softmax_scale=0.0, knorm_eps=0.0)
+             softmax_scale=0.0, knorm_eps=0.0, access=A.ARL2_ACCESS_FRAME)
     c.update(kw)
     return A.Arl2Config(**c)
 
@@ -82,6 +84,8 @@ FAKE = 0x10000
     (dict(softmax_scale=-1.0), A.ARL2_E_INVALID_ARG),
     (dict(softmax_scale=float("nan")), A.ARL2_E_INVALID_ARG),
     (dict(knorm_eps=float("inf")), A.ARL2_E_INVALID_ARG),
+    (dict(access=2), A.ARL2_E_INVALID_ARG),
+    (dict(access=A.ARL2_ACCESS_TOKEN, head_dim=16), A.ARL2_E_UNSUPPORTED),
     # a stream's frame slice reaches 2 GiB
     (dict(heads=8192, tokens_per_frame=1024), A.ARL2_E_UNSUPPORTED),
     # the pass kernel's grid: ceil(T / 128) x B x H work-groups beyond 2^24
