@@ -58,6 +58,19 @@ SOFTMAX_SIGNATURES = {
     "arl2_softmax_device_bytes": (c_size_t, [c_void_p]),
 }
 
+# every function declared in include/arl2_bwd.h (the layer's backward)
+BWD_SIGNATURES = {
+    "arl2_bwd_create": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_void_p)]),
+    "arl2_bwd_begin": (c_int, [c_void_p, c_void_p, c_void_p]),
+    "arl2_bwd_pass": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p]),
+    "arl2_bwd_commit": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p]),
+    "arl2_bwd_read": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "arl2_bwd_destroy": (c_int, [c_void_p]),
+    "arl2_bwd_device_bytes": (c_size_t, [c_void_p]),
+}
+
 
 class Arl2Config(Structure):
     _fields_ = [
@@ -103,7 +116,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_linear_amd.build` "
                            "(the ARL2 layer has no fallback implementation)")
     lib = ctypes.CDLL(path)
-    for name, (res, args) in {**SIGNATURES, **SOFTMAX_SIGNATURES}.items():
+    for name, (res, args) in {**SIGNATURES, **SOFTMAX_SIGNATURES, **BWD_SIGNATURES}.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
@@ -377,3 +390,107 @@ class SoftmaxLayer:
 
     def __exit__(self, *exc):
         self.close()
+
+
+class Arl2Backward:
+    """Backward of an ARL2 layer over a stream of frames, walked in reverse (see
+    include/arl2_bwd.h).  phi_q, phi_k, phi_v: bf16 [H, d, d] device tensors (copied).  Per frame
+    N = F-1 .. 0: pass() for every pass whose output enters the loss, then commit(); read() gives
+    dL/dS_0 and the dphi sums.  Frame tensors as Arl2Layer's; gradients fp32."""
+
+    def __init__(self, phi_q: torch.Tensor, phi_k: torch.Tensor, phi_v: torch.Tensor, batch: int, tokens: int,
+                 softmax_scale: float = 0.0, knorm_eps: float = 0.0, stream=None):
+        self._lib = load_library()
+        self._handle = c_void_p()
+        heads, d, _ = phi_q.shape
+        for name, t in (("phi_q", phi_q), ("phi_k", phi_k), ("phi_v", phi_v)):
+            _dev_tensor(t, name, torch.bfloat16, (heads, d, d))
+        self.batch, self.heads, self.head_dim, self.tokens = int(batch), int(heads), int(d), int(tokens)
+        self.device = phi_q.device
+        cfg = Arl2Config(self.batch, self.heads, self.head_dim, self.tokens, ARL2_BF16, ARL2_F32,
+                         float(softmax_scale), float(knorm_eps), ARL2_ACCESS_FRAME)
+        with torch.cuda.device(self.device):
+            st = self._lib.arl2_bwd_create(byref(cfg), phi_q.data_ptr(), phi_k.data_ptr(), phi_v.data_ptr(),
+                                           _stream_handle(stream), byref(self._handle))
+        _check(st, "arl2_bwd_create")
+
+    @property
+    def frame_shape(self) -> tuple:
+        return (self.batch, self.tokens, self.heads, self.head_dim)
+
+    @property
+    def state_shape(self) -> tuple:
+        return (self.batch, self.heads, self.head_dim, self.head_dim)
+
+    @property
+    def map_shape(self) -> tuple:
+        return (self.heads, self.head_dim, self.head_dim)
+
+    def _ptr(self):
+        if not self._handle:
+            raise Arl2Error(ARL2_E_PROTOCOL, "backward object has been closed")
+        return self._handle
+
+    def _f32(self, shape):
+        return torch.empty(shape, dtype=torch.float32, device=self.device)
+
+    def begin(self, ds_last=None, stream=None) -> None:
+        p = None if ds_last is None else _dev_tensor(ds_last, "ds_last", torch.float32, self.state_shape)
+        _check(self._lib.arl2_bwd_begin(self._ptr(), p, _stream_handle(stream)), "arl2_bwd_begin")
+
+    def pass_(self, q, k, v, s_prev, d_out, dq=None, dk=None, dv=None, stream=None):
+        """Backward of one pass of the current frame: returns (dq, dk, dv)."""
+        fs = self.frame_shape
+        dq, dk, dv = (self._f32(fs) if x is None else x for x in (dq, dk, dv))
+        args = [_dev_tensor(x, n, torch.bfloat16, fs) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        ps = _dev_tensor(s_prev, "s_prev", torch.float32, self.state_shape)
+        pd = _dev_tensor(d_out, "d_out", torch.float32, fs)
+        grads = [_dev_tensor(x, n, torch.float32, fs) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+        _check(self._lib.arl2_bwd_pass(self._ptr(), *args, ps, pd, *grads, _stream_handle(stream)), "arl2_bwd_pass")
+        return dq, dk, dv
+
+    def commit(self, k, v, beta, alpha, s_prev, dk, dv, dbeta=None, dalpha=None, stream=None):
+        """Backward of the current frame's state write: adds to dk, dv; returns (dbeta, dalpha)."""
+        B, T, H, d = self.frame_shape
+        dbeta = self._f32((B, T, H)) if dbeta is None else dbeta
+        dalpha = self._f32((B, H)) if dalpha is None else dalpha
+        pk, pv = (_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((k, "k"), (v, "v")))
+        pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
+        pa = _dev_tensor(alpha, "alpha", torch.float32, (B, H))
+        ps = _dev_tensor(s_prev, "s_prev", torch.float32, self.state_shape)
+        pdk, pdv = (_dev_tensor(x, n, torch.float32, self.frame_shape) for x, n in ((dk, "dk"), (dv, "dv")))
+        pdb = _dev_tensor(dbeta, "dbeta", torch.float32, (B, T, H))
+        pda = _dev_tensor(dalpha, "dalpha", torch.float32, (B, H))
+        _check(self._lib.arl2_bwd_commit(self._ptr(), pk, pv, pb, pa, ps, pdk, pdv, pdb, pda, _stream_handle(stream)),
+               "arl2_bwd_commit")
+        return dbeta, dalpha
+
+    def read(self, stream=None):
+        """(dL/dS at the current frame, dphi_q, dphi_k, dphi_v) as new fp32 tensors."""
+        ds = self._f32(self.state_shape)
+        dq, dk, dv = (self._f32(self.map_shape) for _ in range(3))
+        _check(self._lib.arl2_bwd_read(self._ptr(), ds.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                       _stream_handle(stream)), "arl2_bwd_read")
+        return ds, dq, dk, dv
+
+    @property
+    def device_bytes(self) -> int:
+        return int(self._lib.arl2_bwd_device_bytes(self._ptr()))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            h, self._handle = self._handle, c_void_p()
+            _check(self._lib.arl2_bwd_destroy(h), "arl2_bwd_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wt_hi, const bf16* __restrict__ wt_lo, void* __restrict__ out,
     int T, int Tk, int kv_rows, int H, int nq, int n_bh, float scale_log2, int n_pass_blocks,
-    const WritePartialArgs wa, int n_write, const float* __restrict__ add) {
+    const WritePartialArgs wa, int n_write, const float* __restrict__ add, float* __restrict__ lse) {
   using S = FwdShape<D>;
   constexpr int DP = S::DP, KS = S::KS, MB = S::MB, VLD = S::VLD, VBLK = S::VBLK, VPT = S::VPT,
                 KH_BYTES = S::KH_BYTES, VT_BYTES = S::VT_BYTES, NA = S::NA, NB = S::NB, FA = S::FA, FB = S::FB,
@@ -659,7 +659,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float e0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
     const float e1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
     const float lsum = l_run * e0 + l1 * e1;
-    const float inv = 1.f / (lsum + other_half(lsum, lane));
+    const float ltot = lsum + other_half(lsum, lane);
+    const float inv = 1.f / ltot;
+    // plain attention: the row's log-sum-exp of the scaled scores in log2 units, for a backward
+    if (!INTER && lse && grp == 0 && lane < 32 && qt * kQTile + rb * 32 + lane < T)
+      lse[(int64_t)bh * T + qt * kQTile + rb * 32 + lane] = m * scale_log2 + log2f(ltot);
     const float a0 = e0 * inv, a1 = e1 * inv;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -747,7 +751,7 @@ hipError_t launch_fwd_d(const FwdArgs& a, const WritePartialArgs* w, hipStream_t
   const bf16* wl = static_cast<const bf16*>(a.wt_lo);
 #define ARL2_LAUNCH_FWD(OB, IN)                                                                              \
   hipLaunchKernelGGL((arl2_fwd_kernel<D, OB, IN>), grid, dim3(kThreads), 0, stream, q, k, v, wh, wl, a.out, a.T, Tk, \
-                     kv_rows, a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write, a.add)
+                     kv_rows, a.H, nq, n_bh, a.scale_log2, n_pass_blocks, wa, n_write, a.add, a.lse)
   if (inter) {
     if (a.out_bf16) ARL2_LAUNCH_FWD(true, true);
     else ARL2_LAUNCH_FWD(false, true);

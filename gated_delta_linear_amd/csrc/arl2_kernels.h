@@ -50,6 +50,7 @@ struct FwdArgs {
   int Tk = -1;       // keys of plain attention; -1: the ARL2 pass
   int kv_rows = 0;   // rows per stream slice of k and v (plain attention)
   const float* add = nullptr;  // plain attention: fp32 [B][T][H][d] added to the output, or null
+  float* lse = nullptr;        // plain attention: fp32 [B][H][T] row log-sum-exp (log2 units), or null
 };
 hipError_t launch_fwd(int d, const FwdArgs& a, const WritePartialArgs* w, hipStream_t stream);
 
@@ -142,5 +143,82 @@ struct PrepMapsArgs {
   int H;
 };
 hipError_t launch_prep_maps(int d, const PrepMapsArgs& a, hipStream_t stream);
+
+// --- backward (arl2_bwd.hip) -------------------------------------------------------------------
+// Per (stream, head) d x d matrices in 16x16x32 B-fragment order ([d/32][d/16][64][8] bf16:
+// lane l of fragment (s, nb) holds M[32 s + 8 (l / 16) + j][16 nb + l % 16]), split into hi + lo
+// for fp32 matrices.  Token tensors are [B][T][H][d].
+int bwd_chunks(int T);  // 128-token chunks of the token kernels
+// dst = src (n floats, n % 4 == 0), or zeros when src is null
+hipError_t launch_bwd_fill(float* dst, const float* src, size_t n, hipStream_t stream);
+
+struct BwdTokArgs {
+  const void* q;          // bf16 inputs of the pass (read) or of the clean pass (write)
+  const void* k;
+  const void* v;
+  const float* d_out;     // fp32 output gradient of the pass (read kernel)
+  const float* beta;      // [B][T][H] (write kernel)
+  float* dq;              // accumulated (+=) by the token kernels
+  float* dk;
+  float* dv;
+  float* dbeta;           // [B][T][H], written by the write kernel
+  const void* s_hi;       // S_{N-1}, S_{N-1}^T, G = dL/dS_N, G^T as split fragments, [B][H]
+  const void* s_lo;
+  const void* st_hi;
+  const void* st_lo;
+  const void* g_hi;
+  const void* g_lo;
+  const void* gt_hi;
+  const void* gt_lo;
+  const void* phik;       // phi_k, phi_v, phi_k^T, phi_v^T, phi_q^T fragments, [H]
+  const void* phiv;
+  const void* phikt;
+  const void* phivt;
+  const void* pqt;
+  float* part;            // chunk partials: read [B][H][chunks][d][d], write [B][H][chunks][3][d][d]
+  int B, H, T;
+  float knorm_eps;
+};
+
+struct BwdPassArgs {
+  BwdTokArgs tok;         // q, k, v, d_out, dq, dk, dv (written), st, pqt, part (read partials)
+  const float* d_out;
+  const float* o_sm;      // the softmax branch's output of the pass, recomputed, fp32
+  const float* lse;       // its rows' log-sum-exp (log2 units), [B][H][T]
+  void* do_h;             // workspace: d_out in fp16
+  float* dvec;            // workspace: dO . O per row, [B][H][T]
+  float* gr;              // sum over the frame's passes of Q^T dO, [B][H][d][d]
+  bool gr_first;          // first pass of the frame: gr is overwritten
+  int B, H, T;
+  float scale, scale_log2;
+};
+hipError_t launch_bwd_pass(int d, const BwdPassArgs& a, hipStream_t stream);
+
+struct BwdFragJobs {
+  struct Job {
+    const float* src;     // [B][H][d][d] fp32
+    void* hi;             // fragment order, [B][H]
+    void* lo;
+    int transpose;        // fragments of src^T
+  } job[4];
+};
+hipError_t launch_bwd_frags(int d, const BwdFragJobs& j, int BH, int n_jobs, hipStream_t stream);
+
+struct BwdFrameArgs {
+  const float* g;         // dL/dS_N [B][H][d][d]
+  const float* s_prev;    // S_{N-1}
+  const float* alpha;     // [B][H]
+  const float* gr;        // sum of Q^T dO over the frame's passes, or null (no pass)
+  const float* part;      // write partials
+  const void* phi_q;      // bf16 [H][d][d]
+  float* ds_prev;         // dL/dS_{N-1}
+  float* dalpha;          // [B][H]
+  float* dphi_q;          // accumulated, [H][d][d]
+  float* dphi_k;
+  float* dphi_v;
+  int B, H, chunks;
+};
+hipError_t launch_bwd_commit(int d, const BwdTokArgs& t, const BwdFrameArgs& f, hipStream_t stream);
+hipError_t launch_bwd_phi_frags(int d, const void* phi, void* dst, int H, bool transpose, hipStream_t stream);
 
 }  // namespace arl2

@@ -12,7 +12,9 @@ from .arl2_inputs import (  # noqa: F401
     make_gate_weights,
     make_gates,
     make_hidden,
+    make_out_grad,
     make_pass_inputs,
     make_phi,
+    make_state_grad,
     round_bf16,
 )

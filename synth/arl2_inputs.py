@@ -12,6 +12,8 @@ Distributions (one recipe for all workloads):
   alpha (frame, b, h) = sigmoid(N(2, 0.5))
   beta (frame, b, t, h) = sigmoid(N(0, 1)) * min(1, d / T)   ("eff" mode, the default)
                         = sigmoid(N(0, 1))                    ("literal" mode)
+  dL/d out (frame, pass) ~ N(0, 1) fp32;  dL/dS after the last frame ~ N(0, 1 / d) fp32
+                        (the backward's incoming gradients)
 
 The min(1, d/T) factor keeps the frame-parallel write contractive when a frame holds far
 more tokens than the head dimension; the update formula itself is untouched (beta is an
@@ -29,6 +31,7 @@ _NS_GATE = 1
 _NS_PHI = 2
 _NS_HIDDEN = 3
 _NS_GATE_W = 4
+_NS_GRAD = 5
 
 _T_Q, _T_K, _T_V = 0, 1, 2
 _T_ALPHA, _T_BETA = 0, 1
@@ -156,3 +159,17 @@ def make_gate_weights(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     wt = wt * np.float32(1.0 / np.sqrt(dm))
     bias = np.concatenate([np.zeros(w.heads, np.float32), np.full(w.heads, 2.0, np.float32)])
     return (round_bf16(wt) if w.bf16_inputs else wt), bias
+
+
+def make_out_grad(w: Workload, frame: int, pass_idx: int) -> np.ndarray:
+    """Gradient of a loss with respect to one pass's output, fp32 [B, T, H, d] ~ N(0, 1)."""
+    return _rng(w.seed, _NS_GRAD, frame, pass_idx).standard_normal(
+        (w.batch, w.tokens, w.heads, w.head_dim), dtype=np.float32)
+
+
+def make_state_grad(w: Workload) -> np.ndarray:
+    """Gradient with respect to the state after the last frame, fp32 [B, H, d, d] ~ N(0, 1 / d)."""
+    g = _rng(w.seed, _NS_GRAD, 1 << 20).standard_normal((w.batch, w.heads, w.head_dim, w.head_dim),
+                                                      dtype=np.float32)
+    return g * np.float32(1.0 / np.sqrt(w.head_dim))
+

@@ -1,6 +1,6 @@
-"""The C interfaces on the CPU: the library loads, exports every function include/arl2.h and
-include/arl2_softmax.h declare, and rejects bad arguments before touching a device.  No
-kernel runs here."""
+"""The C interfaces on the CPU: the library loads, exports every function include/arl2.h,
+include/arl2_softmax.h and include/arl2_bwd.h declare, and rejects bad arguments before touching
+a device.  No kernel runs here."""
 import ctypes
 import os
 import re
@@ -13,6 +13,7 @@ import gated_delta_linear_amd.arl2 as A
 HERE = os.path.dirname(os.path.abspath(__file__))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2.h")
 SOFTMAX_HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2_softmax.h")
+BWD_HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2_bwd.h")
 
 
 @pytest.fixture(scope="module")
@@ -32,10 +33,11 @@ def _declared_functions(header=HEADER):
 def test_header_and_binding_agree():
     assert _declared_functions() == set(A.SIGNATURES)
     assert _declared_functions(SOFTMAX_HEADER) == set(A.SOFTMAX_SIGNATURES)
+    assert _declared_functions(BWD_HEADER) == set(A.BWD_SIGNATURES)
 
 
 def test_every_declared_symbol_is_exported(lib):
-    for name in _declared_functions() | _declared_functions(SOFTMAX_HEADER):
+    for name in _declared_functions() | _declared_functions(SOFTMAX_HEADER) | _declared_functions(BWD_HEADER):
         assert hasattr(lib, name), name
 
 
@@ -156,3 +158,34 @@ def test_softmax_create_rejects_bad_config(lib, kw, status):
     assert not h.value
     assert lib.arl2_softmax_layer_create(None, None, ctypes.byref(h)) == A.ARL2_E_INVALID_ARG
     assert lib.arl2_softmax_layer_create(ctypes.byref(_scfg()), None, None) == A.ARL2_E_INVALID_ARG
+
+
+# --- the backward (include/arl2_bwd.h) -------------------------------------------------------
+
+def test_bwd_null_object(lib):
+    assert lib.arl2_bwd_device_bytes(None) == 0
+    assert lib.arl2_bwd_destroy(None) == A.ARL2_OK
+    assert lib.arl2_bwd_begin(None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_bwd_pass(None, None, None, None, None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert lib.arl2_bwd_commit(None, None, None, None, None, None, None, None, None, None, None) == \
+        A.ARL2_E_INVALID_ARG
+    assert lib.arl2_bwd_read(None, None, None, None, None, None) == A.ARL2_E_INVALID_ARG
+    assert b"NULL" in lib.arl2_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), A.ARL2_E_INVALID_ARG),
+    (dict(tokens_per_frame=0), A.ARL2_E_INVALID_ARG),
+    (dict(head_dim=16), A.ARL2_E_UNSUPPORTED),
+    (dict(access=A.ARL2_ACCESS_TOKEN), A.ARL2_E_UNSUPPORTED),
+    (dict(io_dtype=A.ARL2_F32), A.ARL2_E_UNSUPPORTED),
+    (dict(knorm_eps=-1.0), A.ARL2_E_INVALID_ARG),
+])
+def test_bwd_create_rejects_bad_config(lib, kw, status):
+    c = dict(batch=1, heads=2, head_dim=128, tokens_per_frame=64, io_dtype=A.ARL2_BF16, out_dtype=A.ARL2_F32,
+             softmax_scale=0.0, knorm_eps=0.0, access=A.ARL2_ACCESS_FRAME)
+    c.update(kw)
+    h = ctypes.c_void_p(123)
+    assert lib.arl2_bwd_create(ctypes.byref(A.Arl2Config(**c)), None, None, None, None, ctypes.byref(h)) == status
+    assert not h.value
+
