@@ -17,6 +17,7 @@ layer's stream, against the bf16 MFMA peak, and the CPU oracle's rate on a bound
   python bench.py [--steps K] [--warmup W] [--graph] [--workload dit480p|chunked|long_stream]
   python bench.py --series            per-frame GPU time over the whole stream
   python bench.py --compare-softmax   the retained softmax layer vs the ARL2 layer as its cache grows
+  python bench.py --backward          the layer's backward per frame (one pass + the state write)
   python bench.py --pmc-target        a short run for rocprofv3 counter passes (kernels + a copy)
   python bench.py --summarize-pmc DIR rocprofv3 counter CSVs -> profiles/ traffic summary
 """
@@ -431,6 +432,85 @@ def compare_softmax(args):
     print(json.dumps(res), flush=True)
 
 
+def backward_flops(w) -> float:
+    """Algorithmic FLOPs of the backward of one frame (one pass with an output gradient + the state
+    write), per (stream, head): the softmax branch's dV, dP, dQ, dK (8 T^2 d); the inter-frame
+    read's dO S^T, (.) phi_q^T and Q^T dO (6 T d^2); the state write's per-token products (K phi_k,
+    V phi_v, K' S, K' G, R G^T, dR S^T, dR phi_v^T, dU phi_k^T: 16 T d^2) and token sums (K'^T dR,
+    V^T dR, K^T dU: 6 T d^2)."""
+    T, d = w.tokens, w.head_dim
+    return float(w.batch * w.heads * (8 * T * T * d + 28 * T * d * d))
+
+
+def backward_bench(args):
+    """The layer's backward at the workload's shape: one frame = arl2_bwd_pass (the clean pass's
+    output gradient) + arl2_bwd_commit, frames cycling through a ring of RING staged frames (the
+    forward states S_{N-1} from the GPU forward itself), after W untimed frames.  Also the pass
+    and the commit timed alone (HIP events around n back-to-back calls)."""
+    import torch
+
+    from gated_delta_linear_amd import Arl2Backward
+    from synth import WORKLOADS, make_out_grad, make_phi, make_state_grad
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()  # default priority
+    dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dt)
+    with torch.cuda.stream(stream):
+        ring = stage_ring(w, torch)
+        layer = make_layer(w, torch)
+        states = []
+        for f in range(RING):  # S_{N-1} of ring frame f: the state before its commit
+            states.append(layer.state(stream=stream))
+            run_frames(layer, ring, w, 1, layer.new_output(), stream, first=f)
+        layer.close()
+        d_outs = [dev(make_out_grad(w, f, w.denoise_steps), torch.float32) for f in range(RING)]
+        bw = Arl2Backward(*[dev(p, torch.bfloat16) for p in make_phi(w)], batch=w.batch, tokens=w.tokens, stream=stream)
+        bw.begin(dev(make_state_grad(w), torch.float32), stream=stream)
+        fs = bw.frame_shape
+        dq, dk, dv = (torch.empty(fs, dtype=torch.float32, device="cuda") for _ in range(3))
+        dbeta = torch.empty(fs[:3], dtype=torch.float32, device="cuda")
+        dalpha = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+
+        def one_pass(i):
+            (q, k, v), s = ring[i % RING][0][-1], states[i % RING]
+            bw.pass_(q, k, v, s, d_outs[i % RING], dq, dk, dv, stream=stream)
+
+        def one_commit(i):
+            passes, beta, alpha = ring[i % RING]
+            _, k, v = passes[-1]
+            bw.commit(k, v, beta, alpha, states[i % RING], dk, dv, dbeta, dalpha, stream=stream)
+
+        def frames(n, first=0):
+            for i in range(first, first + n):
+                one_pass(RING - 1 - i % RING)  # frames walked in reverse
+                one_commit(RING - 1 - i % RING)
+        frames(args.warmup)
+        ms, wall = time_region(stream, torch, lambda: frames(args.steps))
+        n = 20
+        pass_ms, _ = time_region(stream, torch, lambda: [one_pass(i) for i in range(n)])
+        commit_ms, _ = time_region(stream, torch, lambda: [one_commit(i) for i in range(n)])
+        dev_bytes = bw.device_bytes
+        bw.close()
+    frame_us = ms / args.steps * 1e3
+    tokens = w.batch * w.tokens
+    line = {
+        "metric": "backward frame-tokens/sec per ARL2 layer (one pass with output gradient + state write)",
+        "value": tokens / (frame_us * 1e-6), "unit": "frame-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": frame_us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16/bf16 MFMA, fp32 accumulation", "data": "synthetic",
+        "config": {"workload": f"{w.name}: backward, {w.batch} stream(s) x {w.heads} heads x {w.tokens} tokens/frame, "
+                               f"d={w.head_dim}, frames walked in reverse", "batch": w.batch, "heads": w.heads,
+                   "head_dim": w.head_dim, "tokens_per_frame": w.tokens},
+        "breakdown": {"frame_us": frame_us, "pass_us": pass_ms / n * 1e3, "commit_us": commit_ms / n * 1e3,
+                      "host_wall_s": wall, "device_bytes": dev_bytes,
+                      "algorithmic_gflop_per_frame": backward_flops(w) / 1e9,
+                      "frame_tflops": backward_flops(w) / (frame_us * 1e-6) / 1e12,
+                      "frame_mfma_frac": backward_flops(w) / (frame_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS},
+    }
+    print(json.dumps(line), flush=True)
+
+
 COPY_BYTES = 2**30  # calibration copy: 1 GiB each way, four times the 256 MB last-level cache
 
 
@@ -520,6 +600,7 @@ def main():
     ap.add_argument("--series", action="store_true")
     ap.add_argument("--compare-softmax", action="store_true",
                     help="the retained softmax layer against the ARL2 layer as the K/V cache grows")
+    ap.add_argument("--backward", action="store_true", help="the layer's backward (arl2_bwd.h) per frame")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     args = ap.parse_args()
@@ -536,6 +617,8 @@ def main():
         series(args)
     elif args.compare_softmax:
         compare_softmax(args)
+    elif args.backward:
+        backward_bench(args)
     else:
         bench(args)
 

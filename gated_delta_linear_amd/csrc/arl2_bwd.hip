@@ -134,21 +134,38 @@ __device__ __forceinline__ f16x8 load_f16x8(const T* p) {
   else return to_f16(ld_bf16x8(p));
 }
 
-// 64 rows r0.. of one (stream, head) slice of a [.][T][H][D] bf16 or fp16 tensor into LDS as fp16,
-// row-major (pitch LR) and, when tr is not null, transposed (pitch LT: tr[f][r]).  Rows past T
-// are zeros.  Each thread moves a 4-row x 8-feature block.
-template <int D, typename TIn>
-__device__ __forceinline__ void stage_tile(const TIn* __restrict__ src, int64_t base, int64_t rs, int r0, int T,
-                                           f16* rowm, f16* tr) {
-  using Sh = BwdShape<D>;
-  constexpr int CH = D / 8;
-  for (int it = threadIdx.x; it < 16 * CH; it += 256) {
-    const int rg = it / CH, cc = it % CH;
-    f16x8 x[4];
+// One 4-row x 8-feature block of a 64-row tile of a [.][T][H][D] bf16 or fp16 tensor, staged
+// through registers into LDS as fp16: row-major (pitch LR) and, when tr is not null, transposed
+// (pitch LT: tr[f][r]).  Rows past T are zeros.  Block i of a tile is (row group i % 16, feature
+// chunk i / 16): the 16 lanes of a group take the 16 row groups of one feature chunk, so that every
+// transposed write instruction fills whole 128-byte rows of the tile.
+template <int D>
+struct TileBlock {
+  uint4 raw[4];  // the rows' bits as loaded (bf16 or fp16): converted only when stored, so that a
+                 // load issued before the current block's products is not waited for until then
+  int rg, cc;
+  bool on, from_bf16;
+  __device__ __forceinline__ void init(int i, bool bf) {
+    on = i < 16 * (D / 8);
+    rg = i % 16;
+    cc = i / 16;
+    from_bf16 = bf;
+  }
+  __device__ __forceinline__ void load(const void* __restrict__ src, int64_t base, int64_t rs, int r0, int T) {
+    const uint16_t* p = static_cast<const uint16_t*>(src);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + 4 * rg + e;
-      x[e] = r < T ? load_f16x8(src + base + (int64_t)r * rs + 8 * cc) : f16x8{};
+      raw[e] = on && r < T ? *reinterpret_cast<const uint4*>(p + base + (int64_t)r * rs + 8 * cc) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(f16* rowm, f16* tr) const {
+    if (!on) return;
+    using Sh = BwdShape<D>;
+    f16x8 x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = from_bf16 ? to_f16(__builtin_bit_cast(bf16x8, raw[e])) : __builtin_bit_cast(f16x8, raw[e]);
       *reinterpret_cast<f16x8*>(rowm + (4 * rg + e) * Sh::LR + 8 * cc) = x[e];
     }
     if (tr) {
@@ -161,7 +178,7 @@ __device__ __forceinline__ void stage_tile(const TIn* __restrict__ src, int64_t 
       }
     }
   }
-}
+};
 
 // A fragment of a contraction over 32 staged rows (k-step s2 of a 64-row block) from a transposed
 // tile, in the row order of two stacked 16x16 C blocks: element j <-> row 32 s2 + 16 (j / 4) +
@@ -173,12 +190,17 @@ __device__ __forceinline__ f16x8 tr_frag(const f16* tr, int f, int s2, int g) {
   return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// dK, dV of 64 keys of one (stream, head): wave w owns keys 16 w .. 16 w + 15.  Per query block:
-// S = Q K^T and dP = dO V^T (16x16 C blocks: lane l, register i <-> query 16 m + 4 (l / 16) + i,
-// key l % 16), P = exp2(S scale log2 e - lse), dS = P (dP - Dv); then dV^T += dO^T P and dK^T +=
-// Q^T dS with P, dS as the B operands straight from the C registers.
+// exp2 on the transcendental unit (arguments are at most about 0 here: lse bounds every score)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// dK, dV of 64 keys of one (stream, head).  8 waves, two per SIMD: wave w owns keys 16 (w % 4) ..
+// +15 and the query half w / 4 of every 64-query block; the halves are added at the end.  Per
+// query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l, register i <-> query 16 m +
+// 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS = P (dP - Dv); then dV^T +=
+// dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from the C registers.  The next
+// block's Q and dO rows are loaded into registers while the current block is multiplied.
 template <int D>
-__global__ __launch_bounds__(256) void arl2_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                             const bf16* __restrict__ v, const f16* __restrict__ doh,
                                                             const float* __restrict__ lse,
                                                             const float* __restrict__ dvec, float* __restrict__ dk,
@@ -186,13 +208,15 @@ __global__ __launch_bounds__(256) void arl2_bwd_dkdv_kernel(const bf16* __restri
                                                             float scale_log2) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NB = Sh::NB, LR = Sh::LR;
-  __shared__ __align__(16) f16 qr[kAttnBlock * LR], dor[kAttnBlock * LR];
-  __shared__ __align__(16) f16 qtr[D * Sh::LT], dotr[D * Sh::LT];
+  constexpr int TILE = kAttnBlock * LR + D * Sh::LT;  // f16 elements of one staged tile (rows + transposed)
+  __shared__ __align__(16) f16 lds[2 * TILE];
   __shared__ __align__(16) float lse_s[kAttnBlock], dv_s[kAttnBlock];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  f16 *qr = lds, *qtr = lds + kAttnBlock * LR, *dor = lds + TILE, *dotr = lds + TILE + kAttnBlock * LR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int kg = wave & 3, qh = wave >> 2;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int key = blockIdx.x * kAttnBlock + 16 * wave + l16;
+  const int key = blockIdx.x * kAttnBlock + 16 * kg + l16;
   f16x8 kf[KS], vf[KS];  // B operands: K^T, V^T columns of this wave's keys
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -202,21 +226,34 @@ __global__ __launch_bounds__(256) void arl2_bwd_dkdv_kernel(const bf16* __restri
   f32x4 dkt[NB], dvt[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) dkt[n] = dvt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // staging: threads 0..255 move the Q tile, 256..511 the dO tile; threads 0..63 also lse, Dv
+  const bool stage_q = tid < 256;
+  TileBlock<D> tb;
+  tb.init(tid & 255, stage_q);
+  float lse_r = 0.f, dv_r = 0.f;
+  auto load_block = [&](int r0) {
+    tb.load(stage_q ? static_cast<const void*>(q) : static_cast<const void*>(doh), base, rs, r0, T);
+    if (tid < kAttnBlock) {
+      const int r = r0 + tid;
+      lse_r = r < T ? lse[(int64_t)bh * T + r] : INFINITY;  // rows past T get P = 0
+      dv_r = r < T ? dvec[(int64_t)bh * T + r] : 0.f;
+    }
+  };
   const int nqb = (T + kAttnBlock - 1) / kAttnBlock;
+  load_block(0);
   for (int qb = 0; qb < nqb; ++qb) {
-    const int r0 = qb * kAttnBlock;
     __syncthreads();  // the previous block's LDS reads are done
-    stage_tile<D>(q, base, rs, r0, T, qr, qtr);
-    stage_tile<D>(doh, base, rs, r0, T, dor, dotr);
-    if (threadIdx.x < kAttnBlock) {
-      const int r = r0 + threadIdx.x;
-      lse_s[threadIdx.x] = r < T ? lse[(int64_t)bh * T + r] : INFINITY;  // rows past T get P = 0
-      dv_s[threadIdx.x] = r < T ? dvec[(int64_t)bh * T + r] : 0.f;
+    tb.store(stage_q ? qr : dor, stage_q ? qtr : dotr);
+    if (tid < kAttnBlock) {
+      lse_s[tid] = lse_r;
+      dv_s[tid] = dv_r;
     }
     __syncthreads();
-    f16x8 pb[2], dsb[2];
+    if (qb + 1 < nqb) load_block((qb + 1) * kAttnBlock);
+    f16x8 pb, dsb;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * qh + mm;
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -229,47 +266,60 @@ __global__ __launch_bounds__(256) void arl2_bwd_dkdv_kernel(const bf16* __restri
       const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_s + 16 * m + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sc[i] * scale_log2 - L[i]);
-        pb[m >> 1][4 * (m & 1) + i] = (f16)p;
-        dsb[m >> 1][4 * (m & 1) + i] = (f16)(p * (dp[i] - Dd[i]));
+        const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
+        pb[4 * mm + i] = (f16)p;
+        dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd[i]));
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, s2, g), pb[s2], dvt[mb]);
-        dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, s2, g), dsb[s2], dkt[mb]);
-      }
+    for (int mb = 0; mb < NB; ++mb) {
+      dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, qh, g), pb, dvt[mb]);
+      dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, qh, g), dsb, dkt[mb]);
+    }
   }
-  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 w + l % 16
-  if (key < T) {
+  // the query halves: waves 4..7 hand their sums to waves 0..3 through LDS
+  __syncthreads();
+  f32x4* xs = reinterpret_cast<f32x4*>(lds) + (size_t)kg * 2 * NB * 64;
+  static_assert(4 * 2 * NB * 64 * 16 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
+  if (qh) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      xs[mb * 64 + lane] = dkt[mb];
+      xs[(NB + mb) * 64 + lane] = dvt[mb];
+    }
+  }
+  __syncthreads();
+  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 (w % 4) + l % 16
+  if (!qh && key < T) {
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb) {
       const int64_t o = base + (int64_t)key * rs + 16 * mb + 4 * g;
-      *reinterpret_cast<f32x4*>(dk + o) = dkt[mb] * scale;
-      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb];
+      *reinterpret_cast<f32x4*>(dk + o) = (dkt[mb] + xs[mb * 64 + lane]) * scale;
+      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb] + xs[(NB + mb) * 64 + lane];
     }
   }
 }
 
-// dQ of 64 queries of one (stream, head): wave w owns queries 16 w .. 16 w + 15.  Per key block:
-// S^T = K Q^T and dP^T = V dO^T (lane l, register i <-> key 16 m + 4 (l / 16) + i, query l % 16),
-// dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T.
+// dQ of 64 queries of one (stream, head).  8 waves: wave w owns queries 16 (w % 4) .. +15 and the
+// key half w / 4 of every 64-key block; the halves are added at the end.  Per key block: S^T =
+// K Q^T and dP^T = V dO^T (lane l, register i <-> key 16 m + 4 (l / 16) + i, query l % 16),
+// dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T.  The next block's K and V rows are loaded into
+// registers while the current block is multiplied.
 template <int D>
-__global__ __launch_bounds__(256) void arl2_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void arl2_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const f16* __restrict__ doh,
                                                           const float* __restrict__ lse, const float* __restrict__ dvec,
                                                           float* __restrict__ dq, int T, int H, float scale,
                                                           float scale_log2) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NB = Sh::NB, LR = Sh::LR;
-  __shared__ __align__(16) f16 kr[kAttnBlock * LR], vr[kAttnBlock * LR];
-  __shared__ __align__(16) f16 ktr[D * Sh::LT];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  __shared__ __align__(16) f16 lds[2 * kAttnBlock * LR + D * Sh::LT];
+  f16 *kr = lds, *vr = lds + kAttnBlock * LR, *ktr = lds + 2 * kAttnBlock * LR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int qg = wave & 3, kh = wave >> 2;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int qi = blockIdx.x * kAttnBlock + 16 * wave + l16;
+  const int qi = blockIdx.x * kAttnBlock + 16 * qg + l16;
   f16x8 qf[KS], df[KS];  // B operands: Q^T, dO^T columns of this wave's queries
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -281,16 +331,22 @@ __global__ __launch_bounds__(256) void arl2_bwd_dq_kernel(const bf16* __restrict
   f32x4 dqt[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) dqt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // staging: threads 0..255 move the K tile (with its transpose), 256..511 the V tile
+  const bool stage_k = tid < 256;
+  TileBlock<D> tb;
+  tb.init(tid & 255, true);
   const int nkb = (T + kAttnBlock - 1) / kAttnBlock;
+  tb.load(stage_k ? k : v, base, rs, 0, T);
   for (int kb = 0; kb < nkb; ++kb) {
     const int r0 = kb * kAttnBlock;
     __syncthreads();
-    stage_tile<D>(k, base, rs, r0, T, kr, ktr);
-    stage_tile<D>(v, base, rs, r0, T, vr, static_cast<f16*>(nullptr));
+    tb.store(stage_k ? kr : vr, stage_k ? ktr : nullptr);
     __syncthreads();
-    f16x8 dsb[2];
+    if (kb + 1 < nkb) tb.load(stage_k ? k : v, base, rs, r0 + kAttnBlock, T);
+    f16x8 dsb;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * kh + mm;
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -302,19 +358,25 @@ __global__ __launch_bounds__(256) void arl2_bwd_dq_kernel(const bf16* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = r0 + 16 * m + 4 * g + i;
-        const float p = key < T ? exp2f(sc[i] * scale_log2 - L) : 0.f;
-        dsb[m >> 1][4 * (m & 1) + i] = (f16)(p * (dp[i] - Dd));
+        const float p = key < T ? fast_exp2(sc[i] * scale_log2 - L) : 0.f;
+        dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd));
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) dqt[mb] = mfma16h(tr_frag<D>(ktr, 16 * mb + l16, s2, g), dsb[s2], dqt[mb]);
+    for (int mb = 0; mb < NB; ++mb) dqt[mb] = mfma16h(tr_frag<D>(ktr, 16 * mb + l16, kh, g), dsb, dqt[mb]);
   }
-  if (qi < T) {
+  __syncthreads();
+  f32x4* xs = reinterpret_cast<f32x4*>(lds) + (size_t)qg * NB * 64;
+  static_assert(4 * NB * 64 * 16 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
+  if (kh) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) xs[mb * 64 + lane] = dqt[mb];
+  }
+  __syncthreads();
+  if (!kh && qi < T) {
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
-      *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 16 * mb + 4 * g) = dqt[mb] * scale;
+      *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 16 * mb + 4 * g) = (dqt[mb] + xs[mb * 64 + lane]) * scale;
   }
 }
 
@@ -647,7 +709,11 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
   }
   // chunk sums K'^T dR and V^T dR: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1)
   const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
-  float* part = a.part + ((int64_t)bh * nch + chunk) * 3 * D * D;
+  // partial sum p of 16-column block nb at [bh][p][nb][chunk][row][16]: each (p, nb) strip of all
+  // chunks is contiguous for the per-head kernel that adds them
+  auto pidx = [&](int p, int nb, int row) -> int64_t {
+    return ((((int64_t)bh * 3 + p) * NB + nb) * nch + chunk) * D * 16 + row * 16 + l16;
+  };
   {
     f32x4 p[BPW];
 #pragma unroll
@@ -667,7 +733,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int n = 0; n < BPW; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[(16 * mb + 4 * g + i) * D + 16 * (nb0 + n) + l16] = p[n][i];
+      for (int i = 0; i < 4; ++i) a.part[pidx(0, nb0 + n, 16 * mb + 4 * g + i)] = p[n][i];
 #pragma unroll
     for (int n = 0; n < BPW; ++n) p[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -685,7 +751,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int n = 0; n < BPW; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[D * D + (16 * mb + 4 * g + i) * D + 16 * (nb0 + n) + l16] = p[n][i];
+      for (int i = 0; i < 4; ++i) a.part[pidx(1, nb0 + n, 16 * mb + 4 * g + i)] = p[n][i];
   }
   __syncthreads();  // K' is no longer read: dU replaces it
 #pragma unroll
@@ -730,7 +796,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int n = 0; n < BPW; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[2 * D * D + (16 * mb + 4 * g + i) * D + 16 * (nb0 + n) + l16] = p3[n][i];
+      for (int i = 0; i < 4; ++i) a.part[pidx(2, nb0 + n, 16 * mb + 4 * g + i)] = p3[n][i];
   }
 }
 
@@ -747,72 +813,79 @@ __global__ __launch_bounds__(256) void arl2_bwd_gsum_kernel(const float* __restr
   reinterpret_cast<f32x4*>(gr + (int64_t)bh * dd)[i4] = s;
 }
 
-// End of a frame's backward, per (head, 16 columns), streams in order:
+// End of a frame's backward, per (head, 16 x 16 output tile), streams in order:
 //   dS_{N-1} = alpha G - sum_chunks K'^T dR + phi_q^T Gr,   dalpha = <G, S_{N-1}>,
 //   dphi_q += Gr S^T,  dphi_k += sum_chunks K^T dU,  dphi_v += sum_chunks V^T dR.
+// Thread t owns element (t / 16, t % 16) of the tile; the strips of Gr, S and phi_q that the
+// d-long dot products read come through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void arl2_bwd_frame_kernel(const BwdFrameArgs a) {
-  constexpr int TPR = 256 / D, CPT = 16 / TPR;  // threads per row, columns per thread
+  constexpr int NB = D / 16, CP = 17, RP = D + 4;
+  __shared__ float gcol[D * CP];  // Gr[k][16 ct + c]
+  __shared__ float phc[D * CP];   // phi_q[k][16 rt + r]
+  __shared__ __align__(16) float grow[16 * RP];  // Gr[16 rt + r][k]
+  __shared__ __align__(16) float srow[16 * RP];  // S[16 ct + c][k]
   __shared__ float red[256];
-  const int h = blockIdx.y, ct = blockIdx.x;
-  const int row = threadIdx.x / TPR, c0 = 16 * ct + (threadIdx.x % TPR) * CPT;
-  const bf16* phq = static_cast<const bf16*>(a.phi_q) + (int64_t)h * D * D;
+  const int ct = blockIdx.x, rt = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
+  const int r = tid / 16, c = tid % 16, row = 16 * rt + r, col = 16 * ct + c;
   const int64_t dd = (int64_t)D * D;
-  float aq[CPT], ak[CPT], av[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) aq[c] = ak[c] = av[c] = 0.f;
+  if (a.gr) {
+    const bf16* ph = static_cast<const bf16*>(a.phi_q) + h * dd;
+    for (int i = tid; i < 16 * D; i += 256) phc[(i / 16) * CP + i % 16] = (float)ph[(i / 16) * D + 16 * rt + i % 16];
+  }
+  float aq = 0.f, ak = 0.f, av = 0.f;
   for (int b = 0; b < a.B; ++b) {
     const int64_t bh = (int64_t)b * a.H + h;
     const float* G = a.g + bh * dd;
     const float* S = a.s_prev + bh * dd;
-    const float* gr = a.gr ? a.gr + bh * dd : nullptr;
-    const float* part = a.part + bh * a.chunks * 3 * dd;
-    const float alpha = a.alpha[bh];
-    float ds[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) ds[c] = alpha * G[row * D + c0 + c];
+    // the 16-column strips of the three sums, chunk after chunk ([bh][sum][strip][chunk][row][16])
+    const float* part = a.part + ((bh * 3) * NB + ct) * a.chunks * D * 16 + row * 16 + c;
+    const int64_t pstride = (int64_t)NB * a.chunks * D * 16;  // from one sum to the next
+    float ds = a.alpha[bh] * G[row * D + col];
+#pragma unroll 8
     for (int ch = 0; ch < a.chunks; ++ch) {
-      const float* p = part + (int64_t)ch * 3 * dd + row * D + c0;
+      const float* p = part + (int64_t)ch * D * 16;
+      ds -= p[0];
+      av += p[pstride];
+      ak += p[2 * pstride];
+    }
+    if (a.gr) {
+      const float* gr = a.gr + bh * dd;
+      __syncthreads();  // the previous stream's strips are no longer read
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        ds[c] -= p[c];
-        av[c] += p[dd + c];
-        ak[c] += p[2 * dd + c];
+      for (int i = tid; i < 16 * D; i += 256) {
+        gcol[(i / 16) * CP + i % 16] = gr[(i / 16) * D + 16 * ct + i % 16];
+        grow[(i / D) * RP + i % D] = gr[(16 * rt + i / D) * D + i % D];
+        srow[(i / D) * RP + i % D] = S[(16 * ct + i / D) * D + i % D];
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int k = 0; k < D; ++k) {
+        ds += phc[k * CP + r] * gcol[k * CP + c];   // (phi_q^T Gr)[row][col]
+        aq += grow[r * RP + k] * srow[c * RP + k];  // (Gr S^T)[row][col]
       }
     }
-    if (gr) {
-      for (int kk = 0; kk < D; ++kk) {
-        const float f = (float)phq[kk * D + row];  // phi_q^T[row][kk]
-        const float gv = gr[row * D + kk];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          ds[c] += f * gr[kk * D + c0 + c];
-          aq[c] += gv * S[(c0 + c) * D + kk];  // (Gr S^T)[row][c]
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) a.ds_prev[bh * dd + row * D + c0 + c] = ds[c];
-    if (ct == 0) {  // dalpha over the whole matrix
+    a.ds_prev[bh * dd + row * D + col] = ds;
+    if (ct == 0 && rt == 0) {  // dalpha over the whole matrix (all loads of a thread in flight at once)
       float s = 0.f;
-      for (int i = threadIdx.x; i < D * D; i += 256) s += G[i] * S[i];
-      red[threadIdx.x] = s;
+#pragma unroll
+      for (int i = tid; i < D * D / 4; i += 256) {
+        const f32x4 x = reinterpret_cast<const f32x4*>(G)[i], y = reinterpret_cast<const f32x4*>(S)[i];
+        s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+      }
+      red[tid] = s;
       __syncthreads();
       for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        if (tid < w) red[tid] += red[tid + w];
         __syncthreads();
       }
-      if (threadIdx.x == 0) a.dalpha[bh] = red[0];
-      __syncthreads();
+      if (tid == 0) a.dalpha[bh] = red[0];
     }
   }
-  const int64_t o = (int64_t)h * dd + row * D + c0;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    a.dphi_q[o + c] += aq[c];
-    a.dphi_k[o + c] += ak[c];
-    a.dphi_v[o + c] += av[c];
-  }
+  const int64_t o = (int64_t)h * dd + row * D + col;
+  a.dphi_q[o] += aq;
+  a.dphi_k[o] += ak;
+  a.dphi_v[o] += av;
 }
 
 // dst[i] = src ? src[i] : 0 (n4 float4 elements); a kernel rather than a memset node, so that the
@@ -834,9 +907,9 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
   const bf16* k = static_cast<const bf16*>(a.tok.k);
   const bf16* v = static_cast<const bf16*>(a.tok.v);
   const f16* doh = static_cast<const f16*>(a.do_h);
-  hipLaunchKernelGGL(arl2_bwd_dkdv_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dk,
+  hipLaunchKernelGGL(arl2_bwd_dkdv_kernel<D>, dim3(nb, BH), dim3(512), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dk,
                      a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
-  hipLaunchKernelGGL(arl2_bwd_dq_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dq,
+  hipLaunchKernelGGL(arl2_bwd_dq_kernel<D>, dim3(nb, BH), dim3(512), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dq,
                      a.T, a.H, a.scale, a.scale_log2);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
   hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(nch * BH), dim3(512), 0, stream, a.tok);
@@ -855,7 +928,7 @@ template <int D>
 hipError_t launch_bwd_commit_d(const BwdTokArgs& t, const BwdFrameArgs& f, hipStream_t stream) {
   const int nch = (t.T + kTokChunk - 1) / kTokChunk;
   hipLaunchKernelGGL(arl2_bwd_write_kernel<D>, dim3(nch * t.B * t.H), dim3(512), 0, stream, t);
-  hipLaunchKernelGGL(arl2_bwd_frame_kernel<D>, dim3(D / 16, t.H), dim3(256), 0, stream, f);
+  hipLaunchKernelGGL(arl2_bwd_frame_kernel<D>, dim3(D / 16, D / 16, t.H), dim3(256), 0, stream, f);
   return hipGetLastError();
 }
 

@@ -175,7 +175,8 @@ struct BwdTokArgs {
   const void* phikt;
   const void* phivt;
   const void* pqt;
-  float* part;            // chunk partials: read [B][H][chunks][d][d], write [B][H][chunks][3][d][d]
+  float* part;            // chunk partials: read [B][H][chunks][d][d]; write [B][H][3][d/16][chunks][d][16]
+                          // (the sums K^T dR, V^T dR, K^T dU in 16-column strips)
   int B, H, T;
   float knorm_eps;
 };
