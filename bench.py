@@ -201,15 +201,15 @@ def commit_launch_us(layer, ring, w, out, stream, torch, pass_out, n=16):
     return a.elapsed_time(b) * 1e3 / n
 
 
-def load_traffic():
+def load_traffic(workload: str):
     """HBM bytes per launch of the pass kernel from committed counter passes, if they were
-    taken on the current kernel source."""
+    taken on the current kernel source and on this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or not str(t.get("workload", "")).startswith(workload):
         return None
     return t
 
@@ -284,7 +284,7 @@ def bench(args):
     ms_per_step = elapsed_ms / args.steps
     value = w.batch * w.tokens * args.steps / (elapsed_ms / 1e3)
     achieved = pass_flops(w) / (pass_us * 1e-6) / 1e12
-    traffic = load_traffic()
+    traffic = load_traffic(w.name)
     line = {
         "metric": METRIC,
         "value": value,
@@ -330,35 +330,53 @@ def bench(args):
 
 
 def series(args):
-    """Per-frame GPU time and device memory over a whole stream (constant-cost check)."""
+    """Per-frame GPU time and device memory over a whole stream (the constant-cost check): W
+    frames of a throwaway layer are enqueued first (the GPU's clock settles over the first few
+    hundred, and they leave a backlog, so that the host's own pace, about the GPU's, does not
+    open gaps inside the timed frames), then a fresh layer's frames back to back, an event pair
+    around each and no host synchronisation in between; free device memory is read before and
+    after the stream."""
     import torch
 
     from synth import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    layer = make_layer(w, torch)
-    ring = stage_ring(w, torch)
-    out = layer.new_output()
-    stream = torch.cuda.current_stream()
-    times, mem = [], []
-    for f in range(w.frames):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        run_frames(layer, ring, w, 1, out, stream, first=f)
-        b.record(stream)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(stream):
+        ring = stage_ring(w, torch)
+        warm = make_layer(w, torch)
+        layer = make_layer(w, torch)
+        out = warm.new_output()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.frames)]
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e3)
-        mem.append(torch.cuda.mem_get_info()[0])
-        if f % 50 == 0:
-            print(f"frame {f}: {times[-1]:.1f} us", flush=True)
-    t = np.array(times[2:])
-    x = np.arange(len(t))
-    slope = float(np.polyfit(x, t, 1)[0]) if len(t) > 2 else 0.0
-    print(json.dumps({"workload": w.name, "frames": w.frames, "median_us": float(np.median(t)),
+        free0 = torch.cuda.mem_get_info()[0]
+        run_frames(warm, ring, w, args.warmup, out, stream)
+        free_at = {}
+        for f in range(w.frames):
+            ev[f][0].record(stream)
+            run_frames(layer, ring, w, 1, out, stream, first=f)
+            ev[f][1].record(stream)
+            if f + 1 in (1, 21, 115, 231):  # allocations happen on the host, at enqueue time
+                free_at[str(f + 1)] = torch.cuda.mem_get_info()[0]
+        torch.cuda.synchronize()
+        free1 = torch.cuda.mem_get_info()[0]
+        times = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        dev_bytes = layer.device_bytes
+        layer.close()
+        warm.close()
+    t = np.array(times)
+    slope = float(np.polyfit(np.arange(len(t)), t, 1)[0]) if len(t) > 2 else 0.0
+    at = {str(n): times[n - 1] for n in (1, 2, 21, 115, 231) if n <= len(times)}
+    print(json.dumps({"workload": w.name, "frames": w.frames, "warmup_frames": args.warmup,
+                      "mean_us": float(t.mean()), "median_us": float(np.median(t)),
                       "p10_us": float(np.percentile(t, 10)), "p90_us": float(np.percentile(t, 90)),
-                      "slope_us_per_100_frames": slope * 100, "free_mem_bytes_min": int(min(mem)),
-                      "free_mem_bytes_max": int(max(mem)), "device_bytes": layer.device_bytes}), flush=True)
-    layer.close()
+                      "min_us": float(t.min()), "max_us": float(t.max()), "frame_us_at": at,
+                      "slope_us_per_100_frames": slope * 100,
+                      "slope_pct_of_mean_per_100_frames": slope * 100 / float(t.mean()) * 100,
+                      "free_mem_before": int(free0), "free_mem_after_frame": free_at, "free_mem_after": int(free1),
+                      "device_bytes": dev_bytes}),
+          flush=True)
 
 
 def compare_softmax(args):
