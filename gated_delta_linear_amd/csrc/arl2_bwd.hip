@@ -300,83 +300,99 @@ __global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restri
   }
 }
 
-// dQ of 64 queries of one (stream, head).  8 waves: wave w owns queries 16 (w % 4) .. +15 and the
-// key half w / 4 of every 64-key block; the halves are added at the end.  Per key block: S^T =
-// K Q^T and dP^T = V dO^T (lane l, register i <-> key 16 m + 4 (l / 16) + i, query l % 16),
-// dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T.  The next block's K and V rows are loaded into
-// registers while the current block is multiplied.
+// dQ of 64 queries of one (stream, head), with 32x32x16 MFMAs.  4 waves: wave w owns queries
+// 32 (w % 2) .. +31 and the key half w / 2 of every 64-key block; the halves are added at the
+// end.  Per key block: S^T = K Q^T and dP^T = V dO^T (32x32 C blocks: lane l, register i <-> key
+// 8 (i / 4) + 4 (l / 32) + i % 4 of the wave's 32, query l % 32: every lane holds one query, so
+// its lse and Dv are one value each), dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T with dS^T as
+// the B operand straight from the C registers (k-step h: registers 8 h .. 8 h + 7).  A 32x32x16
+// product reads one 1 KB operand from LDS per 32 K multiply-adds, twice the 16x16x32 ratio.  The
+// next block's K and V rows are loaded into registers while the current block is multiplied.
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void arl2_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const f16* __restrict__ doh,
                                                           const float* __restrict__ lse, const float* __restrict__ dvec,
                                                           float* __restrict__ dq, int T, int H, float scale,
                                                           float scale_log2) {
   using Sh = BwdShape<D>;
-  constexpr int KS = Sh::KS, NB = Sh::NB, LR = Sh::LR;
-  __shared__ __align__(16) f16 lds[2 * kAttnBlock * LR + D * Sh::LT];
+  constexpr int K16 = D / 16, FB = D / 32, LR = Sh::LR, LT = Sh::LT;
+  __shared__ __align__(16) f16 lds[2 * kAttnBlock * LR + D * LT];
   f16 *kr = lds, *vr = lds + kAttnBlock * LR, *ktr = lds + 2 * kAttnBlock * LR;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const int qg = wave & 3, kh = wave >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int qh = wave & 1, kh = wave >> 1;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int qi = blockIdx.x * kAttnBlock + 16 * qg + l16;
-  f16x8 qf[KS], df[KS];  // B operands: Q^T, dO^T columns of this wave's queries
+  const int qi = blockIdx.x * kAttnBlock + 32 * qh + l32;
+  f16x8 qf[K16], df[K16];  // B operands: lane l holds Q (dO) of query qi, features 16 s + 8 (l / 32) ..
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    qf[s] = qi < T ? load_f16x8(q + base + (int64_t)qi * rs + 32 * s + 8 * g) : f16x8{};
-    df[s] = qi < T ? load_f16x8(doh + base + (int64_t)qi * rs + 32 * s + 8 * g) : f16x8{};
+  for (int s = 0; s < K16; ++s) {
+    qf[s] = qi < T ? load_f16x8(q + base + (int64_t)qi * rs + 16 * s + 8 * hi) : f16x8{};
+    df[s] = qi < T ? load_f16x8(doh + base + (int64_t)qi * rs + 16 * s + 8 * hi) : f16x8{};
   }
   const float L = qi < T ? lse[(int64_t)bh * T + qi] : 0.f;
   const float Dd = qi < T ? dvec[(int64_t)bh * T + qi] : 0.f;
-  f32x4 dqt[NB];
+  f32x16 dqt[FB];
 #pragma unroll
-  for (int n = 0; n < NB; ++n) dqt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // staging: threads 0..255 move the K tile (with its transpose), 256..511 the V tile
-  const bool stage_k = tid < 256;
-  TileBlock<D> tb;
-  tb.init(tid & 255, true);
+  for (int n = 0; n < FB; ++n) dqt[n] = zero16();
+  TileBlock<D> tk, tv;  // every thread moves one block of the K tile (with its transpose) and one of V
+  tk.init(tid, true);
+  tv.init(tid, true);
   const int nkb = (T + kAttnBlock - 1) / kAttnBlock;
-  tb.load(stage_k ? k : v, base, rs, 0, T);
+  tk.load(k, base, rs, 0, T);
+  tv.load(v, base, rs, 0, T);
   for (int kb = 0; kb < nkb; ++kb) {
     const int r0 = kb * kAttnBlock;
     __syncthreads();
-    tb.store(stage_k ? kr : vr, stage_k ? ktr : nullptr);
+    tk.store(kr, ktr);
+    tv.store(vr, nullptr);
     __syncthreads();
-    if (kb + 1 < nkb) tb.load(stage_k ? k : v, base, rs, r0 + kAttnBlock, T);
-    f16x8 dsb;
+    if (kb + 1 < nkb) {
+      tk.load(k, base, rs, r0 + kAttnBlock, T);
+      tv.load(v, base, rs, r0 + kAttnBlock, T);
+    }
+    f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int m = 2 * kh + mm;
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < K16; ++s) {
+      const f16x8 ak = *reinterpret_cast<const f16x8*>(kr + (32 * kh + l32) * LR + 16 * s + 8 * hi);
+      const f16x8 av = *reinterpret_cast<const f16x8*>(vr + (32 * kh + l32) * LR + 16 * s + 8 * hi);
+      sc = mfma32(ak, qf[s], sc);
+      dp = mfma32(av, df[s], dp);
+    }
+    f16x8 dsb[2];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const f16x8 ak = *reinterpret_cast<const f16x8*>(kr + (16 * m + l16) * LR + 32 * s + 8 * g);
-        const f16x8 av = *reinterpret_cast<const f16x8*>(vr + (16 * m + l16) * LR + 32 * s + 8 * g);
-        sc = mfma16h(ak, qf[s], sc);
-        dp = mfma16h(av, df[s], dp);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = r0 + 16 * m + 4 * g + i;
-        const float p = key < T ? fast_exp2(sc[i] * scale_log2 - L) : 0.f;
-        dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd));
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int key = r0 + 32 * kh + 8 * (i / 4) + 4 * hi + i % 4;
+      const float p = key < T ? fast_exp2(sc[i] * scale_log2 - L) : 0.f;
+      dsb[i / 8][i % 8] = (f16)(p * (dp[i] - Dd));
     }
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) dqt[mb] = mfma16h(tr_frag<D>(ktr, 16 * mb + l16, kh, g), dsb, dqt[mb]);
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // A: K^T rows 32 fb + l % 32, keys 32 kh + 16 hh + 8 (j / 4) + 4 (l / 32) + j % 4
+        const f16* pa = ktr + (32 * fb + l32) * LT + 32 * kh + 16 * hh + 4 * hi;
+        const f16x4 a0 = *reinterpret_cast<const f16x4*>(pa), a1 = *reinterpret_cast<const f16x4*>(pa + 8);
+        dqt[fb] = mfma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, dsb[hh], dqt[fb]);
+      }
   }
   __syncthreads();
-  f32x4* xs = reinterpret_cast<f32x4*>(lds) + (size_t)qg * NB * 64;
-  static_assert(4 * NB * 64 * 16 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
+  f32x16* xs = reinterpret_cast<f32x16*>(lds) + (size_t)qh * FB * 64;
+  static_assert(2 * FB * 64 * 64 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
   if (kh) {
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) xs[mb * 64 + lane] = dqt[mb];
+    for (int fb = 0; fb < FB; ++fb) xs[fb * 64 + lane] = dqt[fb];
   }
   __syncthreads();
+  // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of query qi
   if (!kh && qi < T) {
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-      *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 16 * mb + 4 * g) = (dqt[mb] + xs[mb * 64 + lane]) * scale;
+    for (int fb = 0; fb < FB; ++fb) {
+      const f32x16 x = dqt[fb] + xs[fb * 64 + lane];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi) =
+            f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
+    }
   }
 }
 
@@ -853,7 +869,8 @@ __global__ __launch_bounds__(256) void arl2_bwd_frame_kernel(const BwdFrameArgs 
       const float* gr = a.gr + bh * dd;
       __syncthreads();  // the previous stream's strips are no longer read
 #pragma unroll
-      for (int i = tid; i < 16 * D; i += 256) {
+      for (int it = 0; it < 16 * D / 256; ++it) {
+        const int i = tid + 256 * it;
         gcol[(i / 16) * CP + i % 16] = gr[(i / 16) * D + 16 * ct + i % 16];
         grow[(i / D) * RP + i % D] = gr[(16 * rt + i / D) * D + i % D];
         srow[(i / D) * RP + i % D] = S[(16 * ct + i / D) * D + i % D];
@@ -869,7 +886,8 @@ __global__ __launch_bounds__(256) void arl2_bwd_frame_kernel(const BwdFrameArgs 
     if (ct == 0 && rt == 0) {  // dalpha over the whole matrix (all loads of a thread in flight at once)
       float s = 0.f;
 #pragma unroll
-      for (int i = tid; i < D * D / 4; i += 256) {
+      for (int it = 0; it < D * D / 1024; ++it) {
+        const int i = tid + 256 * it;
         const f32x4 x = reinterpret_cast<const f32x4*>(G)[i], y = reinterpret_cast<const f32x4*>(S)[i];
         s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
       }
@@ -909,7 +927,7 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
   const f16* doh = static_cast<const f16*>(a.do_h);
   hipLaunchKernelGGL(arl2_bwd_dkdv_kernel<D>, dim3(nb, BH), dim3(512), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dk,
                      a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
-  hipLaunchKernelGGL(arl2_bwd_dq_kernel<D>, dim3(nb, BH), dim3(512), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dq,
+  hipLaunchKernelGGL(arl2_bwd_dq_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dq,
                      a.T, a.H, a.scale, a.scale_log2);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
   hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(nch * BH), dim3(512), 0, stream, a.tok);
