@@ -193,19 +193,17 @@ __device__ __forceinline__ f16x8 tr_frag(const f16* tr, int f, int s2, int g) {
 // exp2 on the transcendental unit (arguments are at most about 0 here: lse bounds every score)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// dK, dV of 64 keys of one (stream, head).  8 waves, two per SIMD: wave w owns keys 16 (w % 4) ..
-// +15 and the query half w / 4 of every 64-query block; the halves are added at the end.  Per
+// dK, dV of 64 keys of one (stream, head).  4 waves, wave w owning keys 16 w .. 16 w + 15 (two
+// work-groups share a CU, so all of a dit480p launch's work-groups are resident at once).  Per
 // query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l, register i <-> query 16 m +
 // 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS = P (dP - Dv); then dV^T +=
 // dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from the C registers.  The next
 // block's Q and dO rows are loaded into registers while the current block is multiplied.
 template <int D>
-__global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                            const bf16* __restrict__ v, const f16* __restrict__ doh,
-                                                            const float* __restrict__ lse,
-                                                            const float* __restrict__ dvec, float* __restrict__ dk,
-                                                            float* __restrict__ dv, int T, int H, float scale,
-                                                            float scale_log2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
+    const float* __restrict__ lse, const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv,
+    int T, int H, float scale, float scale_log2) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NB = Sh::NB, LR = Sh::LR;
   constexpr int TILE = kAttnBlock * LR + D * Sh::LT;  // f16 elements of one staged tile (rows + transposed)
@@ -213,10 +211,9 @@ __global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restri
   __shared__ __align__(16) float lse_s[kAttnBlock], dv_s[kAttnBlock];
   f16 *qr = lds, *qtr = lds + kAttnBlock * LR, *dor = lds + TILE, *dotr = lds + TILE + kAttnBlock * LR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const int kg = wave & 3, qh = wave >> 2;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int key = blockIdx.x * kAttnBlock + 16 * kg + l16;
+  const int key = blockIdx.x * kAttnBlock + 16 * wave + l16;
   f16x8 kf[KS], vf[KS];  // B operands: K^T, V^T columns of this wave's keys
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -226,13 +223,13 @@ __global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restri
   f32x4 dkt[NB], dvt[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) dkt[n] = dvt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // staging: threads 0..255 move the Q tile, 256..511 the dO tile; threads 0..63 also lse, Dv
-  const bool stage_q = tid < 256;
-  TileBlock<D> tb;
-  tb.init(tid & 255, stage_q);
+  TileBlock<D> tq, to;  // every thread moves one block of the Q tile and one of the dO tile
+  tq.init(tid, true);
+  to.init(tid, false);
   float lse_r = 0.f, dv_r = 0.f;
   auto load_block = [&](int r0) {
-    tb.load(stage_q ? static_cast<const void*>(q) : static_cast<const void*>(doh), base, rs, r0, T);
+    tq.load(q, base, rs, r0, T);
+    to.load(doh, base, rs, r0, T);
     if (tid < kAttnBlock) {
       const int r = r0 + tid;
       lse_r = r < T ? lse[(int64_t)bh * T + r] : INFINITY;  // rows past T get P = 0
@@ -243,17 +240,17 @@ __global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restri
   load_block(0);
   for (int qb = 0; qb < nqb; ++qb) {
     __syncthreads();  // the previous block's LDS reads are done
-    tb.store(stage_q ? qr : dor, stage_q ? qtr : dotr);
+    tq.store(qr, qtr);
+    to.store(dor, dotr);
     if (tid < kAttnBlock) {
       lse_s[tid] = lse_r;
       dv_s[tid] = dv_r;
     }
     __syncthreads();
     if (qb + 1 < nqb) load_block((qb + 1) * kAttnBlock);
-    f16x8 pb, dsb;
+    f16x8 pb[2], dsb[2];
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int m = 2 * qh + mm;
+    for (int m = 0; m < 4; ++m) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -267,35 +264,25 @@ __global__ __launch_bounds__(512) void arl2_bwd_dkdv_kernel(const bf16* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
-        pb[4 * mm + i] = (f16)p;
-        dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd[i]));
+        pb[m >> 1][4 * (m & 1) + i] = (f16)p;
+        dsb[m >> 1][4 * (m & 1) + i] = (f16)(p * (dp[i] - Dd[i]));
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-      dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, qh, g), pb, dvt[mb]);
-      dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, qh, g), dsb, dkt[mb]);
-    }
-  }
-  // the query halves: waves 4..7 hand their sums to waves 0..3 through LDS
-  __syncthreads();
-  f32x4* xs = reinterpret_cast<f32x4*>(lds) + (size_t)kg * 2 * NB * 64;
-  static_assert(4 * 2 * NB * 64 * 16 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
-  if (qh) {
+    for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-      xs[mb * 64 + lane] = dkt[mb];
-      xs[(NB + mb) * 64 + lane] = dvt[mb];
-    }
+      for (int s2 = 0; s2 < 2; ++s2) {
+        dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, s2, g), pb[s2], dvt[mb]);
+        dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, s2, g), dsb[s2], dkt[mb]);
+      }
   }
-  __syncthreads();
-  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 (w % 4) + l % 16
-  if (!qh && key < T) {
+  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 w + l % 16
+  if (key < T) {
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb) {
       const int64_t o = base + (int64_t)key * rs + 16 * mb + 4 * g;
-      *reinterpret_cast<f32x4*>(dk + o) = (dkt[mb] + xs[mb * 64 + lane]) * scale;
-      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb] + xs[(NB + mb) * 64 + lane];
+      *reinterpret_cast<f32x4*>(dk + o) = dkt[mb] * scale;
+      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb];
     }
   }
 }
@@ -925,7 +912,7 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
   const bf16* k = static_cast<const bf16*>(a.tok.k);
   const bf16* v = static_cast<const bf16*>(a.tok.v);
   const f16* doh = static_cast<const f16*>(a.do_h);
-  hipLaunchKernelGGL(arl2_bwd_dkdv_kernel<D>, dim3(nb, BH), dim3(512), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dk,
+  hipLaunchKernelGGL(arl2_bwd_dkdv_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dk,
                      a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
   hipLaunchKernelGGL(arl2_bwd_dq_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dq,
                      a.T, a.H, a.scale, a.scale_log2);
