@@ -506,7 +506,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
 #pragma unroll
     for (int s = 0; s < KS; ++s) y = mfma3(y, xh[s], xl[s], frag<D>(st_hi, s, nb, lane), frag<D>(st_lo, s, nb, lane));
     store_rows(ybuf, LF, r0, g, 16 * nb + l16, y);
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   __syncthreads();
 #pragma unroll
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
       const int t = t0 + r0 + 4 * g + i;
       if (t < T) a.dq[base + (int64_t)t * rs + 16 * nb + l16] += c[i];
     }
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   // Gr partial: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1) of Q^T dO
   const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int s = 0; s < KS; ++s) u = mfma16(ka[s], frag<D>(phik, s, nb, lane), u);
     kp[nb] = u;
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   float nrm[4], inv[4], bet[4];
 #pragma unroll
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) kp[nb][i] *= inv[i];
     store_rows(abuf, LF, r0, g, 16 * nb + l16, kp[nb]);
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   __syncthreads();
   bf16x8 kh[KS], kl[KS];  // K' as split A fragments
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
       c = mfma3(c, kh[s], kl[s], frag<D>(s_hi, s, nb, lane), frag<D>(s_lo, s, nb, lane));
     }
     store_rows(bbuf, LF, r0, g, 16 * nb + l16, w - c);
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   __syncthreads();
   // X3 = R G^T (becomes dK')
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
       for (int s = 0; s < KS; ++s) c = mfma3(c, rh[s], rl[s], frag<D>(gt_hi, s, nb, lane), frag<D>(gt_lo, s, nb, lane));
       dkp[nb] = c;
-      ARL2_BLOCK_FENCE();
+      if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
     }
   }
   // X = K' G; dbeta = x . r; dR = beta X
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
       db[i] += c[i] * bbuf[(r0 + 4 * g + i) * LF + 16 * nb + l16];  // x . r
       dr[nb][i] = bet[i] * c[i];
     }
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
       dkp[nb][i] = bet[i] * dkp[nb][i] - c[i];
       cdot[i] += abuf[(r0 + 4 * g + i) * LF + 16 * nb + l16] * dkp[nb][i];  // k' . dK'
     }
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -708,7 +708,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
       const int t = t0 + r0 + 4 * g + i;
       if (t < T) a.dv[base + (int64_t)t * rs + 16 * nb + l16] += c[i];
     }
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   // chunk sums K'^T dR and V^T dR: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1)
   const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
@@ -777,7 +777,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
       const int t = t0 + r0 + 4 * g + i;
       if (t < T) a.dk[base + (int64_t)t * rs + 16 * nb + l16] += c[i];
     }
-    ARL2_BLOCK_FENCE();
+    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   // chunk sum K^T dU
   {
