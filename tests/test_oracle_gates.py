@@ -4,7 +4,7 @@ invariants, and planted mistakes that must each fail a pin.
 Source: "Attend Locally, Remember Linearly" technical summary (gist.science), section 2.1 (alpha,
 the forget gate, and beta, the learning rate, are learned projections of the tokens) and section
 3 (head-wise gates); the frame-level write takes one alpha per (stream, head) and frame, so the
-per-token alpha logits are averaged over the frame before the sigmoid (a reading of this build).
+per-token alpha logits are averaged over the frame before the sigmoid (the reading taken here).
 """
 import math
 
