@@ -214,17 +214,44 @@ def load_traffic(workload: str):
     return t
 
 
+def gemm_reference_tflops(torch, n=8192, reps=10) -> float:
+    """A measured dense bf16 MFMA reference on the same GPU: torch.matmul (hipBLASLt) of two
+    contiguous n x n bf16 matrices, after a warm-up, with HIP events around reps products."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (numpy fp64) on the first frames of the same stream, in full: every pass's
     output and the state write, until the time budget is spent (at least one frame)."""
     from oracle import Arl2Oracle
     from synth import make_gates, make_pass_inputs, make_phi
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 1) for i in pools), default=1)
+        if pools:
+            blas = f"{pools[0].get('internal_api', '?')} {pools[0].get('version', '?')}"
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:  # pragma: no cover
+        pass
     orc = Arl2Oracle(*[p.astype(np.float64) for p in make_phi(w)], batch=w.batch)
     frames, busy = 0, 0.0
     while frames < w.frames and (frames == 0 or busy < budget_s):
@@ -239,7 +266,7 @@ def cpu_baseline(w, budget_s: float):
         busy += time.perf_counter() - t0
         frames += 1
     return {"value": w.batch * w.tokens * frames / busy, "unit": "frame-tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
             "sample": f"{w.name} frames 0..{frames - 1} in full ({w.denoise_steps} denoising passes + clean pass "
                       f"+ state write each), numpy fp64, {busy:.1f} s of CPU work, input generation excluded"}
 
@@ -278,6 +305,7 @@ def bench(args):
         torch.cuda.synchronize()
         device_bytes = layer.device_bytes
         layer.close()
+        gemm_tflops = gemm_reference_tflops(torch)  # last: a long GEMM heats the GPU
 
     use_graph = args.graph
     elapsed_ms = graph_ms if use_graph else eager_ms
@@ -314,6 +342,8 @@ def bench(args):
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic["bytes_per_launch"] if traffic else None,
             "flops_per_launch": pass_flops(w), "avg_launch_us": pass_us,
+            "measured_reference": {"what": "torch.matmul bf16 8192^3 (hipBLASLt) on the same GPU",
+                                   "tflops": gemm_tflops, "frac": achieved / gemm_tflops},
         },
         "breakdown": {
             "pass_us": pass_us, "clean_pass_with_write_us": clean_us, "state_write_alone_us": write_us,

@@ -6,8 +6,10 @@ import numpy as np
 import pytest
 import torch
 
-from synth import WORKLOADS, Workload
-from tests.arl2_harness import OUT_TOL, STATE_TOL, log, run_stream
+from gated_delta_linear_amd import Arl2Layer
+from oracle import Arl2Oracle
+from synth import WORKLOADS, Workload, make_gates, make_pass_inputs, make_phi
+from tests.arl2_harness import OUT_TOL, STATE_TOL, dev, log, run_stream, state_err
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +86,38 @@ def test_long_stream_state_drift():
     for f in (20, 114, 230):
         log(f"long_stream: state_err after frame {f + 1}: {res['state_err'][f]:.3e}")
     _check(res, "long_stream")
+
+
+def test_chunked_state_drift_77_chunks():
+    """The chunked workload's whole stream: 77 commits of 4 streams x 12 heads x 4680 tokens (the
+    clean passes' K, V and gates of 8 seeded chunks, cycled), state only.  S after chunks 1, 38 and
+    77 against the oracle on streams 0 and 3, heads 0, 5 and 11 (every (stream, head) state is
+    independent of the others)."""
+    w = WORKLOADS["chunked"]
+    ring = 8
+    phis = make_phi(w)
+    inputs = []
+    for f in range(ring):
+        _, k, v = make_pass_inputs(w, f, w.denoise_steps)
+        beta, alpha = make_gates(w, f)
+        inputs.append((k, v, beta, alpha))
+    layer = Arl2Layer(*[dev(p, torch.bfloat16) for p in phis], batch=w.batch, tokens=w.tokens)
+    bs, hs = [0, 3], [0, 5, 11]
+    orcs = [Arl2Oracle(*[p[hs].astype(np.float64) for p in phis], batch=1) for _ in bs]
+    staged = [tuple(dev(x, torch.bfloat16 if i < 2 else torch.float32) for i, x in enumerate(t)) for t in inputs]
+    worst = 0.0
+    for n in range(w.frames):
+        k, v, beta, alpha = staged[n % ring]
+        layer.commit_frame(None, k, v, beta, alpha, want_output=False)
+        hk, hv, hb, ha = inputs[n % ring]
+        for i, b in enumerate(bs):
+            orcs[i].commit(None, hk[b:b + 1, :, hs], hv[b:b + 1, :, hs], hb[b:b + 1, :, hs], ha[b:b + 1, hs],
+                           want_output=False)
+        if n + 1 in (1, 38, 77):
+            got = layer.state().cpu().numpy()
+            err = max(state_err(got[b][hs], orcs[i].state[0]) for i, b in enumerate(bs))
+            log(f"chunked: state_err after chunk {n + 1}: {err:.3e}")
+            worst = max(worst, err)
+    layer.close()
+    assert worst <= STATE_TOL, worst
+
