@@ -238,6 +238,9 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   if (c.access != ARL2_ACCESS_FRAME && c.access != ARL2_ACCESS_TOKEN) return fail(ARL2_E_INVALID_ARG, "bad access");
   if (c.access == ARL2_ACCESS_TOKEN && c.head_dim == 16)
     return fail(ARL2_E_UNSUPPORTED, "token-level access supports head_dim 64 and 128");
+  // token-level access addresses one stream's fp32 inter-frame reads [T][H][d] with 32-bit byte offsets
+  if (c.access == ARL2_ACCESS_TOKEN && ((int64_t)c.tokens_per_frame + 64) * c.heads * c.head_dim * 4 >= (int64_t(1) << 31))
+    return fail(ARL2_E_UNSUPPORTED, "token-level access: one stream's frame (T x H x d fp32) must stay below 2 GiB");
   if (c.out_dtype != ARL2_F32 && c.out_dtype != ARL2_BF16) return fail(ARL2_E_INVALID_ARG, "bad out_dtype");
   if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
     return fail(ARL2_E_INVALID_ARG, "softmax_scale must be finite and >= 0");
