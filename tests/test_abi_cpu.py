@@ -88,6 +88,8 @@ FAKE = 0x10000
     (dict(knorm_eps=float("inf")), A.ARL2_E_INVALID_ARG),
     (dict(access=2), A.ARL2_E_INVALID_ARG),
     (dict(access=A.ARL2_ACCESS_TOKEN, head_dim=16), A.ARL2_E_UNSUPPORTED),
+    # token-level access: a stream's fp32 inter-frame reads reach 2 GiB (bf16 inputs would not)
+    (dict(access=A.ARL2_ACCESS_TOKEN, heads=3000, tokens_per_frame=1500), A.ARL2_E_UNSUPPORTED),
     # a stream's frame slice reaches 2 GiB
     (dict(heads=8192, tokens_per_frame=1024), A.ARL2_E_UNSUPPORTED),
     # the pass kernel's grid: ceil(T / 128) x B x H work-groups beyond 2^24
