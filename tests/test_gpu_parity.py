@@ -88,6 +88,17 @@ def test_long_stream_state_drift():
     _check(res, "long_stream")
 
 
+def test_maximum_tokens_per_frame():
+    """T = ARL2_MAX_TOKENS (2^20 tokens in one frame), one stream and head, d = 64: 8192 query
+    tiles and 8192 state-write chunks per launch.  2 frames of a denoising pass + the clean pass;
+    16 sampled output rows per pass and the full state after each frame."""
+    from gated_delta_linear_amd.arl2 import ARL2_MAX_TOKENS
+    w = Workload("max_tokens", batch=1, heads=1, head_dim=64, tokens=ARL2_MAX_TOKENS, frames=2, denoise_steps=1,
+                 seed=71)
+    res = run_stream(w, sample_rows=16, reuse_denoise=True)
+    _check(res, "max_tokens")
+
+
 def test_chunked_state_drift_77_chunks():
     """The chunked workload's whole stream: 77 commits of 4 streams x 12 heads x 4680 tokens (the
     clean passes' K, V and gates of 8 seeded chunks, cycled), state only.  S after chunks 1, 38 and
