@@ -18,6 +18,7 @@ layer's stream, against the bf16 MFMA peak, and the CPU oracle's rate on a bound
   python bench.py --series            per-frame GPU time over the whole stream
   python bench.py --compare-softmax   the retained softmax layer vs the ARL2 layer as its cache grows
   python bench.py --backward          the layer's backward per frame (one pass + the state write)
+  python bench.py --stack             a 30-layer attention stack (23 ARL2 + 7 softmax) vs all softmax
   python bench.py --pmc-target        a short run for rocprofv3 counter passes (kernels + a copy)
   python bench.py --summarize-pmc DIR rocprofv3 counter CSVs -> profiles/ traffic summary
 """
@@ -480,6 +481,115 @@ def compare_softmax(args):
     print(json.dumps(res), flush=True)
 
 
+STACK_LAYERS = 30
+STACK_SOFTMAX = (2, 6, 10, 14, 18, 22, 26)  # the 7 of 30 layers kept as softmax attention (every 4th)
+
+
+def stack_bench(args):
+    """The pages' 75 % hybrid stack, attention layers only: 30 attention layers of the workload's
+    shape, 23 ARL2 + 7 retained softmax layers (indices STACK_SOFTMAX), each fed by its own Q, K, V
+    projections of the previous layer's output and followed by its output projection (seeded
+    random-init bf16 weights ~ N(0, 1/(H d)), torch.matmul / hipBLASLt; no norms, MLPs or
+    residuals), against the same stack with all 30 layers softmax.  Per-frame time (4 denoising
+    passes + the clean pass through all 30 layers, launches enqueued back to back; 4 frames timed
+    after warm-up) at frames 1, 21 and 231 (the softmax caches pre-filled with 0, 20 and 230 clean
+    frames), and the layers' device memory."""
+    import torch
+
+    from gated_delta_linear_amd import Arl2Layer, SoftmaxLayer
+    from synth import WORKLOADS, make_gates, make_phi
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()  # default priority
+    B, T, H, d = w.batch, w.tokens, w.heads, w.head_dim
+    hd = H * d
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 4242)
+    timed, cached = 4, (0, 20, 230)
+    max_frames = max(cached) + timed
+    with torch.cuda.stream(stream):
+        def rnd(*shape, scale=1.0):
+            return (torch.randn(*shape, device="cuda", generator=gen) * scale).to(torch.bfloat16)
+        wq, wk, wv, wo = ([rnd(hd, hd, scale=hd ** -0.5) for _ in range(STACK_LAYERS)] for _ in range(4))
+        x_in = [rnd(B * T, hd) for _ in range(w.denoise_steps + 1)]  # the stack's input per pass
+        beta, alpha = (torch.from_numpy(g).to("cuda") for g in make_gates(w, 0))
+        phis = [torch.from_numpy(p).to("cuda").to(torch.bfloat16) for p in make_phi(w)]
+        arl2 = {i: Arl2Layer(*phis, batch=B, tokens=T, out_dtype=torch.bfloat16) for i in range(STACK_LAYERS)}
+        soft = {i: SoftmaxLayer(B, H, d, T, max_frames, out_dtype=torch.bfloat16) for i in range(STACK_LAYERS)}
+        weight_bytes = 4 * STACK_LAYERS * hd * hd * 2
+        o = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+
+        def frame(hybrid):
+            for p in range(w.denoise_steps + 1):
+                clean = p == w.denoise_steps
+                x = x_in[p]
+                for i in range(STACK_LAYERS):
+                    q, k, v = (torch.matmul(x, wm[i]).view(B, T, H, d) for wm in (wq, wk, wv))
+                    if hybrid and i not in STACK_SOFTMAX:
+                        if clean:
+                            arl2[i].commit_frame(q, k, v, beta, alpha, out=o, stream=stream)
+                        else:
+                            arl2[i].denoise_step(q, k, v, out=o, stream=stream)
+                    elif clean:
+                        soft[i].commit_frame(q, k, v, out=o, stream=stream)
+                    else:
+                        soft[i].denoise_step(q, k, v, out=o, stream=stream)
+                    x = torch.matmul(o.view(B * T, hd), wo[i])
+
+        def prefill(n):
+            q = x_in[0].view(B, T, H, d)
+            for i in range(STACK_LAYERS):
+                soft[i].reset()
+                for _ in range(n):
+                    soft[i].commit_frame(None, q, q, want_output=False, stream=stream)
+
+        def projections_only():
+            for p in range(w.denoise_steps + 1):
+                x = x_in[p]
+                for i in range(STACK_LAYERS):
+                    for wm in (wq, wk, wv):
+                        torch.matmul(x, wm[i])
+                    x = torch.matmul(o.view(B * T, hd), wo[i])
+
+        prefill(0)
+        for _ in range(20):  # warm-up (the clock settles; every layer's frame count stays small)
+            frame(True)
+        points = []
+        for n in cached:
+            pt = {"frames_cached": n, "frame_index": n + 1}
+            for hybrid in (True, False):
+                prefill(n)
+                torch.cuda.synchronize()
+                ms, _ = time_region(stream, torch, lambda: [frame(hybrid) for _ in range(timed)])
+                key = "hybrid" if hybrid else "all_softmax"
+                pt[key + "_ms_per_frame"] = ms / timed
+                n_soft = len(STACK_SOFTMAX) if hybrid else STACK_LAYERS
+                cache = 2 * (n + timed) * B * T * H * d * 2  # K and V of one softmax layer after the timed frames
+                pt[key + "_layer_bytes"] = n_soft * cache + (STACK_LAYERS - n_soft) * arl2[0].device_bytes
+            pt["speedup"] = pt["all_softmax_ms_per_frame"] / pt["hybrid_ms_per_frame"]
+            pt["memory_reduction"] = 1 - pt["hybrid_layer_bytes"] / pt["all_softmax_layer_bytes"]
+            points.append(pt)
+        proj_ms, _ = time_region(stream, torch, lambda: [projections_only() for _ in range(timed)])
+        for layer in list(arl2.values()) + list(soft.values()):
+            layer.close()
+    # per-frame time grows linearly with the cache; the average over a stream of F = 231 frames
+    F = 231
+    avg = {}
+    for key in ("hybrid", "all_softmax"):
+        xs = [p["frames_cached"] for p in points]
+        ys = [p[key + "_ms_per_frame"] for p in points]
+        slope, icpt = np.polyfit(xs, ys, 1)
+        avg[key] = float(icpt + slope * (F - 1) / 2)
+    res = {"metric": "per-frame time and memory of a 30-layer attention stack: 23 ARL2 + 7 softmax layers vs all softmax",
+           "workload": f"{w.name}: {B} x {H} heads x {T} tokens/frame, d={d}, {w.denoise_steps} denoising passes + clean "
+                       f"pass per frame; softmax layers {list(STACK_SOFTMAX)}; Q/K/V/output projections of random-init "
+                       f"bf16 weights (torch.matmul); no norms, MLPs or residuals",
+           "points": points, "projections_ms_per_frame": proj_ms / timed, "weight_bytes": weight_bytes,
+           "stream_average_ms_per_frame": avg, "stream_frames": F,
+           "stream_average_speedup": avg["all_softmax"] / avg["hybrid"]}
+    print(json.dumps(res), flush=True)
+
+
 def backward_flops(w) -> float:
     """Algorithmic FLOPs of the backward of one frame (one pass with an output gradient + the state
     write), per (stream, head): the softmax branch's dV, dP, dQ, dK (8 T^2 d); the inter-frame
@@ -649,6 +759,8 @@ def main():
     ap.add_argument("--compare-softmax", action="store_true",
                     help="the retained softmax layer against the ARL2 layer as the K/V cache grows")
     ap.add_argument("--backward", action="store_true", help="the layer's backward (arl2_bwd.h) per frame")
+    ap.add_argument("--stack", action="store_true",
+                    help="a 30-layer attention stack, 23 ARL2 + 7 softmax layers, against all softmax")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     args = ap.parse_args()
@@ -667,6 +779,8 @@ def main():
         compare_softmax(args)
     elif args.backward:
         backward_bench(args)
+    elif args.stack:
+        stack_bench(args)
     else:
         bench(args)
 
