@@ -27,6 +27,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -48,10 +49,14 @@ RING = 8
 
 
 def kernel_source_hash() -> str:
+    """Hash of the pass kernel's sources with comments, trailing blanks and empty lines removed
+    (an edit of a comment leaves the counters taken on the kernel valid)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(line.rstrip() for line in text.splitlines() if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

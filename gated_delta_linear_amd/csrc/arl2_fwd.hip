@@ -32,8 +32,9 @@
 // Precision.  The P V product runs in fp16 (same MFMA rate as bf16): P, at most 2^8 (see
 // below), is rounded to nearest fp16 (relative step 2^-11, eight times finer than bf16, whose
 // rounding of P alone puts the output error at the edge of a 2e-2 budget on long streams),
-// and V converts from bf16 to fp16 exactly for |v| <= 65504 (values beyond become infinite,
-// so they show up instead of being clipped).  Q K^T and the Q W term stay bf16 x bf16 with
+// and V converts from bf16 to fp16 exactly for 2^-14 <= |v| <= 65504 (smaller values round
+// to fp16 subnormals, absolute step 2^-24; larger ones become infinite, so they show up
+// instead of being clipped).  Q K^T and the Q W term stay bf16 x bf16 with
 // fp32 accumulation.
 //
 // Scores are transposed so that every lane holds one query row and 16 of the unit's keys:

@@ -37,6 +37,12 @@
  *   phi_q/k/v   bf16  [H][d][d]           phi[h][i][j], read once by arl2_layer_create
  *   state       fp32  [B][H][d][d]        S[b][h][i][j]: i = key feature, j = value feature
  *
+ * Arithmetic: Q K^T and the inter-frame read use bf16 products with fp32 accumulation (the
+ * read as Q (phi_q S_{N-1}), its d x d factor split into two bf16 terms); the softmax runs in
+ * fp32; P V multiplies P rounded to fp16 by V converted to fp16, which is exact for
+ * 2^-14 <= |v| <= 65504 (smaller |v| round to fp16 subnormals, larger ones become infinite);
+ * the state write uses split-bf16 products (about fp32 accuracy) and keeps S in fp32.
+ *
  * Streams: every call enqueues its work on `stream` (a hipStream_t; NULL = the null
  * stream) and returns without waiting.  If a call uses a different stream from the
  * previous call on the same layer, the library makes the new stream wait for the old one.

@@ -33,9 +33,10 @@
  *   dbeta, dalpha     fp32 [B][T][H], [B][H] (4-byte aligned), written by arl2_bwd_commit
  *   ds_last, ds0      fp32 [B][H][d][d]   dL/dS after the last frame (in), dL/dS_0 (out)
  *   dphi_q/k/v        fp32 [H][d][d]      accumulated over the frames since arl2_bwd_begin
- * Precision: the softmax branch's backward multiplies bf16 operands (P, dS and dO rounded to
- * bf16) with fp32 accumulation; the inter-frame read and the state write use split-bf16
- * products (about fp32 accuracy).  Results are bitwise reproducible (no atomics).
+ * Precision: the softmax branch's backward multiplies fp16 operands with fp32 accumulation (q,
+ * k, v converted from bf16, exact for 2^-14 <= |x| <= 65504; P, dS and dO rounded to fp16); the
+ * inter-frame read and the state write use split-bf16 products (about fp32 accuracy).  Results
+ * are bitwise reproducible (no atomics).
  * Status codes, arl2_last_error() and the stream rule (a call on a different stream than the
  * previous one waits for it) are those of arl2.h.  A failed launch poisons the object
  * (ARL2_E_PROTOCOL) until arl2_bwd_begin.

@@ -27,6 +27,7 @@
  * valid until the enqueued work has finished):
  *   q, k, v   bf16  [B][T][H][d]
  *   out       fp32 or bf16 (config) [B][T][H][d]
+ * Arithmetic: that of arl2.h's softmax branch (bf16 Q K^T, fp32 softmax, fp16 P and V in P V).
  * Status codes, the stream rule (a call on a different stream than the previous one waits
  * for it) and arl2_last_error() are those of arl2.h.  A failed launch poisons the layer
  * (later calls return ARL2_E_PROTOCOL) until arl2_softmax_reset.

@@ -2,9 +2,9 @@
 (oracle.bwd_oracle.layer_backward), frames walked in reverse.
 
 Bars (derived from the arithmetic of each path):
-  dq, dk, dv      max |err| / rms(oracle) <= 2e-2: the softmax branch's backward multiplies P, dS and
-                  dO rounded to bf16 (relative step 2^-9) with fp32 accumulation, like the forward's
-                  bf16 products, so the same bar as the forward's output;
+  dq, dk, dv      max |err| / rms(oracle) <= 2e-2: the softmax branch's backward multiplies fp16
+                  operands (P, dS and dO rounded at relative step 2^-11) with fp32 accumulation,
+                  and its scores recompute the forward's bf16 Q K^T; the forward output's bar;
   dbeta           max |err| / rms(oracle) <= 1e-3;
   dalpha, dS_0, dphi_q, dphi_k, dphi_v   ||err||_F / ||oracle||_F <= 1e-3 (split-bf16 products,
                   about fp32 accuracy, as the forward's state bar).
