@@ -7,7 +7,7 @@
 //
 // The per-chunk partial sums P_c = K'_c^T diag(beta_c) (V'_c - K'_c S_{N-1}) run as extra
 // work-groups of the clean pass's launch (arl2_write_partial.h).  arl2_commit_reduce: one
-// work-group per (stream, head, 32 value columns) adds alpha S_{N-1} and the partials in a
+// work-group per (stream, head, 16 value columns) adds alpha S_{N-1} and the partials in a
 // fixed order (bitwise reproducible), stores S_N, and prepares what the next frame reads:
 // -S_N as MFMA B fragments (for the next write's K' S product) and (phi_q S_N)^T (for the
 // passes' inter read).
@@ -25,15 +25,16 @@ namespace {
 template <int D>
 struct CommitShape {
   static constexpr int DP = D < 32 ? 32 : D;
-  static constexpr int KS = D / 16;   // k-steps over input features
-  static constexpr int MB = DP / 32;  // 32-blocks over key features (rows of S)
-  static constexpr int NB = DP / 32;  // 32-blocks over value features (columns of S)
-  static constexpr int FB = DP / 16;  // 16-blocks of the state write's partials and -S fragments
-  static constexpr int KS32 = DP / 32;  // 32-deep k-steps of the -S fragments
+  static constexpr int NB = DP / 16;    // 16-column stripes of S (one work-group each)
+  static constexpr int FB = DP / 16;    // 16-blocks of the state write's partials and -S fragments
+  static constexpr int KS32 = DP / 32;  // 32-deep k-steps (the -S fragments, and W = phi_q S)
 };
 
 constexpr int kReduceThreads = 512;
 
+// One work-group per (stream, head, 16 value columns): a 16-column stripe keeps the chunk sum
+// spread over DP / 16 work-groups per head (the partials are read once, and one CU's load path
+// is what bounds each work-group), and it is one 16x16 MFMA block wide for W.
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
     const float* __restrict__ s_prev, const float* __restrict__ alpha, const float* __restrict__ alpha_part,
@@ -41,22 +42,26 @@ __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
     int chunks, const bf16* __restrict__ pq, float* __restrict__ s_new, bf16* __restrict__ sneg_hi,
     bf16* __restrict__ sneg_lo, bf16* __restrict__ wt_hi, bf16* __restrict__ wt_lo, int H) {
   using S = CommitShape<D>;
-  constexpr int DP = S::DP, KS = S::KS, MB = S::MB, FB = S::FB, KS32 = S::KS32;
-  constexpr int V4 = DP * 8;  // float4 groups of the 32-column block
-  constexpr int PER = (V4 + kReduceThreads - 1) / kReduceThreads;
-  constexpr int kUnroll = 8;  // chunk loads in flight per group
-  __shared__ float tile[DP][33];  // S_new[:, 32 nb .. 32 nb + 31], padded against bank conflicts
+  constexpr int DP = S::DP, FB = S::FB, KS32 = S::KS32;
+  constexpr int V4 = DP * 4;  // float4 groups of the 16-column stripe
+  static_assert(V4 <= kReduceThreads, "one float4 group per thread");
+  static_assert(FB <= kReduceThreads / 64, "one W block per wave");
+  constexpr int kUnroll = 16;  // chunk loads in flight per thread (a 2048-token frame in one round)
+  __shared__ float tile[DP][17];  // S_new[:, 16 nb .. 16 nb + 15], padded against bank conflicts
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
-  static_assert(MB <= kReduceThreads / 64, "one W block per wave");
-  // phi_q rows of this wave's W block (A fragments), loaded first: they depend on nothing.
+  // phi_q rows of this wave's 16-row W block (A fragments of 16x16x32 MFMAs: lane l holds row
+  // l % 16, k 32 st + 8 (l / 16) .. + 7), loaded first: they depend on nothing.
   const bf16* pqh = pq + (int64_t)h * DP * D;
-  bf16x8 af[KS];
-  if (wave < MB) {
+  bf16x8 af[KS32];
+  if (wave < FB) {
 #pragma unroll
-    for (int st = 0; st < KS; ++st) af[st] = ld_bf16x8(pqh + (32 * wave + (lane & 31)) * D + 16 * st + 8 * (lane >> 5));
+    for (int st = 0; st < KS32; ++st) {
+      const int k0 = 32 * st + 8 * (lane >> 4);
+      af[st] = k0 < D ? ld_bf16x8(pqh + (16 * wave + (lane & 15)) * D + k0) : bf16x8{};
+    }
   }
   float a = alpha ? alpha[bh] : 1.f;
   if (alpha_part) {  // the per-frame decay from the gate projection: sigmoid(mean logit + bias)
@@ -70,102 +75,80 @@ __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
   }
   constexpr int kStride = DP * DP / 4;  // float4 between consecutive chunks
 
-  // S_new = alpha S_prev + sum_c P_c, chunks added in a fixed order.  Each thread owns PER
-  // float4 groups (4 adjacent columns of a row) and keeps all their loads of a round in flight.
-  // The partials are stored as 16 x 16 blocks in 16x16 MFMA C-register order ([row block][column
-  // block][register i][lane l] = P[16 rb + 4 (l / 16) + i][16 cb + l % 16]); group e of this
-  // column stripe is block e / 64 (row block e / 128, column block 2 nb + (e / 64) % 2),
-  // register (e % 64) / 16, lanes 4 (e % 16) .. 4 (e % 16) + 3.
-  f32x4 acc[PER];
-  bool ok[PER];
-  const f32x4* pp[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + kReduceThreads * u;
-    const int blk = e >> 6, i = (e >> 4) & 3, q = e & 15;
-    const int row = 16 * (blk >> 1) + 4 * (q >> 2) + i, col = 32 * nb + 16 * (blk & 1) + 4 * (q & 3);
-    ok[u] = e < V4 && row < D && col < D;
-    acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int pblk = (blk >> 1) * FB + 2 * nb + (blk & 1);
-    pp[u] = reinterpret_cast<const f32x4*>(partial + bh * chunks * DP * DP + (pblk * 4 + i) * 64 + 4 * q);
-    if (ok[u]) acc[u] = a * *reinterpret_cast<const f32x4*>(s_prev + (bh * D + row) * D + col);
-  }
+  // S_new = alpha S_prev + sum_c P_c, chunks added in a fixed order.  The partials are stored
+  // as 16 x 16 blocks in 16x16 MFMA C-register order ([row block][column block][register i]
+  // [lane l] = P[16 rb + 4 (l / 16) + i][16 cb + l % 16]); thread e < V4 owns row block e / 64,
+  // register (e / 16) % 4 and lanes 4 (e % 16) .. + 3 of column block nb: 4 adjacent columns.
+  const int e = tid;
+  const int rb = e >> 6, ri = (e >> 4) & 3, q = e & 15;
+  const int row = 16 * rb + 4 * (q >> 2) + ri, c4 = 4 * (q & 3), col = 16 * nb + c4;
+  const bool ok = e < V4 && row < D && col < D;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4* pp = reinterpret_cast<const f32x4*>(partial + bh * chunks * DP * DP + ((rb * FB + nb) * 4 + ri) * 64 + 4 * q);
+  if (ok) acc = a * *reinterpret_cast<const f32x4*>(s_prev + (bh * D + row) * D + col);
   for (int c = 0; c < chunks; c += kUnroll) {
-    f32x4 x[PER][kUnroll];
+    f32x4 x[kUnroll];
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
+    for (int w = 0; w < kUnroll; ++w)
+      x[w] = (ok && c + w < chunks) ? pp[(int64_t)(c + w) * kStride] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < kUnroll; ++w)
-        x[u][w] = (ok[u] && c + w < chunks) ? pp[u][(int64_t)(c + w) * kStride] : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-#pragma unroll
-      for (int w = 0; w < kUnroll; ++w)
-        if (c + w < chunks) acc[u] += x[u][w];
+    for (int w = 0; w < kUnroll; ++w)
+      if (c + w < chunks) acc += x[w];
   }
+  if (e < V4) {
+    if (ok) *reinterpret_cast<f32x4*>(s_new + (bh * D + row) * D + col) = acc;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + kReduceThreads * u;
-    if (e >= V4) continue;
-    const int blk = e >> 6, i = (e >> 4) & 3, q = e & 15;
-    const int row = 16 * (blk >> 1) + 4 * (q >> 2) + i, c4 = 16 * (blk & 1) + 4 * (q & 3), col = 32 * nb + c4;
-    if (ok[u]) *reinterpret_cast<f32x4*>(s_new + (bh * D + row) * D + col) = acc[u];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) tile[row][c4 + c] = acc[u][c];
+    for (int c = 0; c < 4; ++c) tile[row][c4 + c] = acc[c];  // zeros outside d x d
   }
   __syncthreads();
 
   // -S_new as 16x16x32 B fragments for the next write's K' S: fragment (k-step ks, value block
-  // vb), lane l, element j <-> -S[32 ks + 16 (j / 4) + 4 (l / 16) + j % 4][16 vb + l % 16] (the
+  // nb), lane l, element j <-> -S[32 ks + 16 (j / 4) + 4 (l / 16) + j % 4][16 nb + l % 16] (the
   // row order of two stacked 16x16 C blocks, in which K' enters as the A operand).
-  for (int e = tid; e < KS32 * 2 * 64; e += kReduceThreads) {
-    const int ks = e >> 7, half = (e >> 6) & 1, l = e & 63;
+  if (tid < KS32 * 64) {
+    const int ks = tid >> 6;
     bf16x8 hi, lo;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const Bf16Pair sp = split_bf16(-tile[32 * ks + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3)][16 * half + (l & 15)]);
+      const Bf16Pair sp = split_bf16(-tile[32 * ks + 16 * (j >> 2) + 4 * (lane >> 4) + (j & 3)][lane & 15]);
       hi[j] = sp.hi;
       lo[j] = sp.lo;
     }
-    const int64_t fo = ((bh * KS32 + ks) * FB + 2 * nb + half) * 64 + l;
+    const int64_t fo = ((bh * KS32 + ks) * FB + nb) * 64 + lane;
     reinterpret_cast<bf16x8*>(sneg_hi)[fo] = hi;
     reinterpret_cast<bf16x8*>(sneg_lo)[fo] = lo;
   }
 
-  // W = phi_q S_new on this column block; stored transposed and split, W^T[j][i], as the pass
-  // kernel stages it: k-step planes [i / 16][j][i % 16], so that every kilobyte it loads is
-  // contiguous.
-  if (wave < MB) {
-    const int mb = wave;
-    f32x16 w = zero16();
+  // W = phi_q S_new on this column stripe, wave w the rows 16 w .. 16 w + 15 (16x16x32 MFMAs;
+  // B lane l holds S rows 32 st + 8 (l / 16) .. + 7 of column l % 16, split hi + lo).  Stored
+  // transposed and split, W^T[j][i], as the pass kernel stages it: k-step planes
+  // [i / 16][j][i % 16], so that every kilobyte it loads is contiguous.
+  if (wave < FB) {
+    f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
+    for (int st = 0; st < KS32; ++st) {
       bf16x8 bhi, blo;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const Bf16Pair sp = split_bf16(tile[16 * st + 8 * (lane >> 5) + j][lane & 31]);
+        const Bf16Pair sp = split_bf16(tile[32 * st + 8 * (lane >> 4) + j][lane & 15]);
         bhi[j] = sp.hi;
         blo[j] = sp.lo;
       }
-      w = mfma32(af[st], bhi, w);
-      w = mfma32(af[st], blo, w);
+      w = mfma16(af[st], bhi, w);
+      w = mfma16(af[st], blo, w);
     }
-    const int col = 32 * nb + (lane & 31);  // value feature j = row of W^T
+    const int i0 = 16 * wave + 4 * (lane >> 4);  // C lane l, register r: W[i0 + r][16 nb + l % 16]
+    if (i0 < D) {
+      bf16x4 hi, lo;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int i0 = 32 * mb + 8 * g + 4 * (lane >> 5);
-      if (i0 < D) {
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const Bf16Pair sp = split_bf16(w[4 * g + e]);
-          hi[e] = sp.hi;
-          lo[e] = sp.lo;
-        }
-        const int64_t o = bh * DP * D + ((int64_t)(i0 >> 4) * DP + col) * 16 + (i0 & 15);
-        *reinterpret_cast<bf16x4*>(wt_hi + o) = hi;
-        *reinterpret_cast<bf16x4*>(wt_lo + o) = lo;
+      for (int r = 0; r < 4; ++r) {
+        const Bf16Pair sp = split_bf16(w[r]);
+        hi[r] = sp.hi;
+        lo[r] = sp.lo;
       }
+      const int64_t o = bh * DP * D + ((int64_t)(i0 >> 4) * DP + 16 * nb + (lane & 15)) * 16 + (i0 & 15);
+      *reinterpret_cast<bf16x4*>(wt_hi + o) = hi;
+      *reinterpret_cast<bf16x4*>(wt_lo + o) = lo;
     }
   }
 }
