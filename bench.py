@@ -44,6 +44,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FWD_KERNEL = "arl2_fwd_kernel"
 KERNEL_SOURCES = ["gated_delta_linear_amd/csrc/arl2_fwd.hip", "gated_delta_linear_amd/csrc/arl2_write_partial.h",
                   "gated_delta_linear_amd/csrc/arl2_device.h", "gated_delta_linear_amd/csrc/arl2_kernels.h"]
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "arl2_fwd_dit480p_traffic.json")
 RING = 8
 
@@ -76,6 +77,28 @@ def commit_flops(w) -> float:
 
 def frame_flops(w) -> float:
     return (w.denoise_steps + 1) * pass_flops(w) + commit_flops(w)
+
+
+def state_write_bytes(w) -> float:
+    """Algorithmic HBM bytes of the state write alone: per (stream, head) the clean pass's K, V
+    (bf16), beta (fp32), S_{N-1} read and S_N written (fp32); per head the maps phi_k, phi_v (bf16)."""
+    T, d = w.tokens, w.head_dim
+    return float(w.batch * w.heads * (2 * T * d * 2 + 4 * T + 2 * d * d * 4) + w.heads * 2 * d * d * 2)
+
+
+def frame_distribution(layer, ring, w, out, stream, torch, n=100, backlog=50):
+    """Per-frame GPU time of n frames, an event pair around each, enqueued behind a backlog of
+    frames (so that the host's pace opens no gaps inside them)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    run_frames(layer, ring, w, backlog, out, stream)
+    for f in range(n):
+        ev[f][0].record(stream)
+        run_frames(layer, ring, w, 1, out, stream, first=f)
+        ev[f][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"frames": n, "median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90)), "min_us": float(t.min()), "max_us": float(t.max())}
 
 
 def stage_ring(w, torch, gated=False):
@@ -308,6 +331,7 @@ def bench(args):
         pass_us = pass_launch_us(layer, ring, w, out, stream, torch)
         write_us = commit_launch_us(layer, ring, w, None, stream, torch, out)
         clean_us = commit_launch_us(layer, ring, w, out, stream, torch, out)
+        dist = frame_distribution(layer, ring, w, out, stream, torch)
         torch.cuda.synchronize()
         device_bytes = layer.device_bytes
         layer.close()
@@ -353,6 +377,9 @@ def bench(args):
         },
         "breakdown": {
             "pass_us": pass_us, "clean_pass_with_write_us": clean_us, "state_write_alone_us": write_us,
+            "state_write_alone_GBps": state_write_bytes(w) / (write_us * 1e-6) / 1e9,
+            "state_write_alone_hbm_frac": state_write_bytes(w) / (write_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "per_frame_us": dist,
             "frame_us_graph": graph_ms / args.steps * 1e3, "frame_us_eager": eager_ms / args.steps * 1e3,
             "host_wall_s_graph": graph_wall, "host_wall_s_eager": eager_wall,
             "frame_mfma_frac": frame_flops(w) / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
