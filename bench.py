@@ -260,12 +260,8 @@ def gemm_reference_tflops(torch, n=8192, reps=10) -> float:
     return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle (numpy fp64) on the first frames of the same stream, in full: every pass's
-    output and the state write, until the time budget is spent (at least one frame)."""
-    from oracle import Arl2Oracle
-    from synth import make_gates, make_pass_inputs, make_phi
-
+def cpu_env():
+    """BLAS threads the oracle uses, the BLAS build and the CPU model."""
     blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
@@ -281,23 +277,137 @@ def cpu_baseline(w, budget_s: float):
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
     except OSError:  # pragma: no cover
         pass
-    orc = Arl2Oracle(*[p.astype(np.float64) for p in make_phi(w)], batch=w.batch)
+    return int(threads), blas, cpu_model
+
+
+def _cpu_line(value, unit, sample, **extra):
+    threads, blas, cpu_model = cpu_env()
+    line = {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
+            "sample": sample}
+    line.update(extra)
+    return line
+
+
+def cpu_baseline(w, budget_s: float, gated: bool = False, access: str = "frame"):
+    """The oracle (numpy fp64) on the first frames of the same stream, in full: every pass's
+    output and the state write, until the time budget is spent (at least one frame).  gated:
+    beta, alpha from the oracle's gate projections of the hidden states; access "token": the
+    token-level (sequential) oracle."""
+    from oracle import Arl2Oracle, Arl2SeqOracle, gate_projections
+    from synth import make_gate_weights, make_gates, make_hidden, make_pass_inputs, make_phi
+
+    phis = [p.astype(np.float64) for p in make_phi(w)]
+    orc = Arl2SeqOracle(*phis, batch=w.batch) if access == "token" else Arl2Oracle(*phis, batch=w.batch)
+    if gated:
+        wg, bg = make_gate_weights(w)
     frames, busy = 0, 0.0
     while frames < w.frames and (frames == 0 or busy < budget_s):
         inputs = [make_pass_inputs(w, frames, p) for p in range(w.denoise_steps + 1)]
-        beta, alpha = make_gates(w, frames)
+        hidden = make_hidden(w, frames) if gated else None
+        beta, alpha = (None, None) if gated else make_gates(w, frames)
         t0 = time.perf_counter()
+        if gated:
+            beta, alpha = gate_projections(hidden.astype(np.float64), wg.astype(np.float64), bg.astype(np.float64),
+                                           w.beta_scale)
         for p, (q, k, v) in enumerate(inputs):
-            if p < w.denoise_steps:
+            if access == "token":
+                if p < w.denoise_steps:
+                    orc.denoise_step(q, k, v, beta)
+                else:
+                    orc.commit(q, k, v, beta, alpha)
+            elif p < w.denoise_steps:
                 orc.denoise_step(q, k, v)
             else:
                 orc.commit(q, k, v, beta, alpha)
         busy += time.perf_counter() - t0
         frames += 1
-    return {"value": w.batch * w.tokens * frames / busy, "unit": "frame-tokens/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
-            "sample": f"{w.name} frames 0..{frames - 1} in full ({w.denoise_steps} denoising passes + clean pass "
-                      f"+ state write each), numpy fp64, {busy:.1f} s of CPU work, input generation excluded"}
+    what = ("token-level oracle" if access == "token" else "oracle") + (", gates from the hidden states" if gated else "")
+    return _cpu_line(w.batch * w.tokens * frames / busy, "frame-tokens/s",
+                     f"{w.name} frames 0..{frames - 1} in full ({w.denoise_steps} denoising passes + clean pass + "
+                     f"state write each; {what}), numpy fp64, {busy:.1f} s of CPU work, input generation excluded")
+
+
+def cpu_baseline_recurrence(w, budget_s: float):
+    """The oracle's state recurrence alone (the state write of every frame, no outputs) over the
+    stream, its clean passes cycling through RING staged frames as on the GPU, until the stream
+    ends or the time budget is spent."""
+    from oracle import Arl2Oracle
+    from synth import make_gates, make_pass_inputs, make_phi
+
+    orc = Arl2Oracle(*[p.astype(np.float64) for p in make_phi(w)], batch=w.batch)
+    ring = []
+    for f in range(RING):
+        _, k, v = make_pass_inputs(w, f, w.denoise_steps)
+        ring.append((k, v) + tuple(make_gates(w, f)))
+    frames, busy = 0, 0.0
+    while frames < w.frames and (frames == 0 or busy < budget_s):
+        k, v, beta, alpha = ring[frames % RING]
+        t0 = time.perf_counter()
+        orc.commit(None, k, v, beta, alpha, want_output=False)
+        busy += time.perf_counter() - t0
+        frames += 1
+    return _cpu_line(frames / busy, "state writes/s",
+                     f"{w.name}: the oracle's state recurrence alone, frames 0..{frames - 1} of {w.frames} (clean passes "
+                     f"of {RING} staged frames, cycled), numpy fp64, {busy:.1f} s of CPU work",
+                     ms_per_state_write=busy / frames * 1e3)
+
+
+def cpu_baseline_softmax(w, budget_s: float):
+    """The retained softmax layer's oracle over the first frames of the stream, in full (every
+    pass attends over the cached clean frames and its own), until the time budget is spent."""
+    from oracle import SoftmaxOracle
+    from synth import make_pass_inputs
+
+    orc = SoftmaxOracle(w.head_dim)
+    frames, busy, per_frame = 0, 0.0, []
+    while frames < w.frames and (frames == 0 or busy < budget_s):
+        inputs = [make_pass_inputs(w, frames, p) for p in range(w.denoise_steps + 1)]
+        t0 = time.perf_counter()
+        for p, (q, k, v) in enumerate(inputs):
+            if p < w.denoise_steps:
+                orc.denoise_step(q, k, v)
+            else:
+                orc.commit_frame(q, k, v)
+        dt = time.perf_counter() - t0
+        busy += dt
+        per_frame.append(dt * 1e3)
+        frames += 1
+    return _cpu_line(w.batch * w.tokens * frames / busy, "frame-tokens/s",
+                     f"{w.name}: the softmax layer's oracle, frames 0..{frames - 1} in full (frame N attends over N "
+                     f"cached frames + its own), numpy fp64, {busy:.1f} s of CPU work, input generation excluded",
+                     ms_per_frame=per_frame)
+
+
+def cpu_baseline_backward(w, budget_s: float):
+    """The backward oracle on frames of the same ring as the GPU backward: per frame the clean
+    pass's backward (pass_backward) and the state write's (write_backward), with S_{N-1} from the
+    oracle's recurrence, until the time budget is spent."""
+    from oracle import pass_backward, write_backward
+    from oracle.bwd_oracle import forward_states
+    from synth import make_gates, make_out_grad, make_pass_inputs, make_phi, make_state_grad
+
+    phi_q, phi_k, phi_v = (p.astype(np.float64) for p in make_phi(w))
+    ring = []
+    for f in range(RING):
+        beta, alpha = make_gates(w, f)
+        ring.append({"passes": [make_pass_inputs(w, f, w.denoise_steps)], "beta": beta, "alpha": alpha})
+    d = w.head_dim
+    states = forward_states(phi_k, phi_v, ring, np.zeros((w.batch, w.heads, d, d)))
+    g = make_state_grad(w).astype(np.float64)
+    scale = 1.0 / np.sqrt(d)
+    frames, busy = 0, 0.0
+    while frames == 0 or (busy < budget_s and frames < RING):
+        n = RING - 1 - frames  # frames walked in reverse
+        (q, k, v), fr = ring[n]["passes"][0], ring[n]
+        d_o = make_out_grad(w, n, w.denoise_steps)
+        t0 = time.perf_counter()
+        pass_backward(q, k, v, d_o, states[n], phi_q, scale)
+        write_backward(k, v, fr["beta"], fr["alpha"], states[n], g, phi_k, phi_v)
+        busy += time.perf_counter() - t0
+        frames += 1
+    return _cpu_line(w.batch * w.tokens * frames / busy, "frame-tokens/s",
+                     f"{w.name}: the backward oracle, {frames} frame(s) (the clean pass's backward + the state "
+                     f"write's), numpy fp64, {busy:.1f} s of CPU work, input generation excluded")
 
 
 def bench(args):
@@ -388,7 +498,7 @@ def bench(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, gated=args.gated, access=args.access)
     print(json.dumps(line), flush=True)
 
 
@@ -438,7 +548,8 @@ def series(args):
                       "slope_us_per_100_frames": slope * 100,
                       "slope_pct_of_mean_per_100_frames": slope * 100 / float(t.mean()) * 100,
                       "free_mem_before": int(free0), "free_mem_after_frame": free_at, "free_mem_after": int(free1),
-                      "device_bytes": dev_bytes}),
+                      "device_bytes": dev_bytes,
+                      "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_recurrence(w, args.cpu_budget)}),
           flush=True)
 
 
@@ -510,6 +621,7 @@ def compare_softmax(args):
                 point["attention_mfma_frac"] = point["attention_tflops"] / PEAK_BF16_TFLOPS
             res["points"].append(point)
             sm.close()
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_softmax(w, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 
@@ -697,6 +809,7 @@ def backward_bench(args):
                       "algorithmic_gflop_per_frame": backward_flops(w) / 1e9,
                       "frame_tflops": backward_flops(w) / (frame_us * 1e-6) / 1e12,
                       "frame_mfma_frac": backward_flops(w) / (frame_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(w, args.cpu_budget),
     }
     print(json.dumps(line), flush=True)
 
