@@ -146,7 +146,7 @@ struct TileBlock {
   int rg, cc;
   bool on, from_bf16;
   __device__ __forceinline__ void init(int i, bool bf) {
-    on = i < 16 * (D / 8);
+    on = i >= 0 && i < 16 * (D / 8);
     rg = i % 16;
     cc = i / 16;
     from_bf16 = bf;
@@ -193,27 +193,31 @@ __device__ __forceinline__ f16x8 tr_frag(const f16* tr, int f, int s2, int g) {
 // exp2 on the transcendental unit (arguments are at most about 0 here: lse bounds every score)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// dK, dV of 64 keys of one (stream, head).  4 waves, wave w owning keys 16 w .. 16 w + 15 (two
-// work-groups share a CU, so all of a dit480p launch's work-groups are resident at once).  Per
-// query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l, register i <-> query 16 m +
-// 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS = P (dP - Dv); then dV^T +=
-// dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from the C registers.  The next
-// block's Q and dO rows are loaded into registers while the current block is multiplied.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
+// dK, dV of 16 NW keys of one (stream, head).  NW waves, wave w owning keys 16 w .. 16 w + 15; every
+// key block reads the head's whole Q and dO, so wider work-groups cut that stream (and the staging
+// per wave) in proportion.  Per query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l,
+// register i <-> query 16 m + 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS =
+// P (dP - Dv); then dV^T += dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from
+// the C registers.  The next block's Q and dO rows are loaded into registers while the current
+// block is multiplied: with 64 NW >= 2 x the tile's blocks each thread moves one block of one
+// tile, otherwise one block of each.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
     const float* __restrict__ lse, const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv,
     int T, int H, float scale, float scale_log2) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NB = Sh::NB, LR = Sh::LR;
   constexpr int TILE = kAttnBlock * LR + D * Sh::LT;  // f16 elements of one staged tile (rows + transposed)
+  constexpr int NBLK = 16 * (D / 8);                  // 4-row x 8-feature blocks of one tile
+  constexpr bool SPLIT = 64 * NW >= 2 * NBLK;         // one block of one tile per thread
   __shared__ __align__(16) f16 lds[2 * TILE];
   __shared__ __align__(16) float lse_s[kAttnBlock], dv_s[kAttnBlock];
   f16 *qr = lds, *qtr = lds + kAttnBlock * LR, *dor = lds + TILE, *dotr = lds + TILE + kAttnBlock * LR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int key = blockIdx.x * kAttnBlock + 16 * wave + l16;
+  const int key = blockIdx.x * (16 * NW) + 16 * wave + l16;
   f16x8 kf[KS], vf[KS];  // B operands: K^T, V^T columns of this wave's keys
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -223,13 +227,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x4 dkt[NB], dvt[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) dkt[n] = dvt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  TileBlock<D> tq, to;  // every thread moves one block of the Q tile and one of the dO tile
-  tq.init(tid, true);
-  to.init(tid, false);
+  // SPLIT: threads [0, NBLK) move Q blocks and [NBLK, 2 NBLK) dO blocks (whole waves either way),
+  // through one register block; otherwise every thread moves block tid of both tiles.
+  const bool mover_q = !SPLIT || tid < NBLK;
+  TileBlock<D> tq, to;
+  if constexpr (SPLIT) {
+    tq.init(mover_q ? tid : tid - NBLK, mover_q);
+  } else {
+    tq.init(tid, true);
+    to.init(tid, false);
+  }
   float lse_r = 0.f, dv_r = 0.f;
   auto load_block = [&](int r0) {
-    tq.load(q, base, rs, r0, T);
-    to.load(doh, base, rs, r0, T);
+    if constexpr (SPLIT) {
+      if (mover_q) tq.load(q, base, rs, r0, T);
+      else tq.load(doh, base, rs, r0, T);
+    } else {
+      tq.load(q, base, rs, r0, T);
+      to.load(doh, base, rs, r0, T);
+    }
     if (tid < kAttnBlock) {
       const int r = r0 + tid;
       lse_r = r < T ? lse[(int64_t)bh * T + r] : INFINITY;  // rows past T get P = 0
@@ -240,41 +256,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   load_block(0);
   for (int qb = 0; qb < nqb; ++qb) {
     __syncthreads();  // the previous block's LDS reads are done
-    tq.store(qr, qtr);
-    to.store(dor, dotr);
+    if constexpr (SPLIT) {
+      if (mover_q) tq.store(qr, qtr);
+      else tq.store(dor, dotr);
+    } else {
+      tq.store(qr, qtr);
+      to.store(dor, dotr);
+    }
     if (tid < kAttnBlock) {
       lse_s[tid] = lse_r;
       dv_s[tid] = dv_r;
     }
     __syncthreads();
     if (qb + 1 < nqb) load_block((qb + 1) * kAttnBlock);
-    f16x8 pb[2], dsb[2];
+    // per 32-query half s2: S and dP of its two 16-query blocks, then its share of dV^T, dK^T
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < 2; ++s2) {
+      f16x8 pb, dsb;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const f16x8 aq = *reinterpret_cast<const f16x8*>(qr + (16 * m + l16) * LR + 32 * s + 8 * g);
-        const f16x8 ao = *reinterpret_cast<const f16x8*>(dor + (16 * m + l16) * LR + 32 * s + 8 * g);
-        sc = mfma16h(aq, kf[s], sc);
-        dp = mfma16h(ao, vf[s], dp);
+      for (int mm = 0; mm < 2; ++mm) {
+        const int m = 2 * s2 + mm;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const f16x8 aq = *reinterpret_cast<const f16x8*>(qr + (16 * m + l16) * LR + 32 * s + 8 * g);
+          const f16x8 ao = *reinterpret_cast<const f16x8*>(dor + (16 * m + l16) * LR + 32 * s + 8 * g);
+          sc = mfma16h(aq, kf[s], sc);
+          dp = mfma16h(ao, vf[s], dp);
+        }
+        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_s + 16 * m + 4 * g);
+        const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_s + 16 * m + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
+          pb[4 * mm + i] = (f16)p;
+          dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd[i]));
+        }
       }
-      const f32x4 L = *reinterpret_cast<const f32x4*>(lse_s + 16 * m + 4 * g);
-      const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_s + 16 * m + 4 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
-        pb[m >> 1][4 * (m & 1) + i] = (f16)p;
-        dsb[m >> 1][4 * (m & 1) + i] = (f16)(p * (dp[i] - Dd[i]));
+      for (int mb = 0; mb < NB; ++mb) {
+        dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, s2, g), pb, dvt[mb]);
+        dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, s2, g), dsb, dkt[mb]);
       }
     }
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, s2, g), pb[s2], dvt[mb]);
-        dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, s2, g), dsb[s2], dkt[mb]);
-      }
   }
   // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 w + l % 16
   if (key < T) {
@@ -287,29 +311,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// dQ of 64 queries of one (stream, head), with 32x32x16 MFMAs.  4 waves: wave w owns queries
-// 32 (w % 2) .. +31 and the key half w / 2 of every 64-key block; the halves are added at the
-// end.  Per key block: S^T = K Q^T and dP^T = V dO^T (32x32 C blocks: lane l, register i <-> key
+// dQ of 32 NQG queries of one (stream, head), with 32x32x16 MFMAs.  2 NQG waves: wave w owns
+// queries 32 (w % NQG) .. +31 and the key half w / NQG of every 64-key block; the halves are added
+// at the end.  Every query block reads the head's whole K and V, so wider work-groups cut that
+// stream (and the staging per wave) in proportion.  Per key block: S^T = K Q^T and dP^T = V dO^T (32x32 C blocks: lane l, register i <-> key
 // 8 (i / 4) + 4 (l / 32) + i % 4 of the wave's 32, query l % 32: every lane holds one query, so
 // its lse and Dv are one value each), dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T with dS^T as
 // the B operand straight from the C registers (k-step h: registers 8 h .. 8 h + 7).  A 32x32x16
 // product reads one 1 KB operand from LDS per 32 K multiply-adds, twice the 16x16x32 ratio.  The
 // next block's K and V rows are loaded into registers while the current block is multiplied.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                          const bf16* __restrict__ v, const f16* __restrict__ doh,
-                                                          const float* __restrict__ lse, const float* __restrict__ dvec,
-                                                          float* __restrict__ dq, int T, int H, float scale,
-                                                          float scale_log2) {
+template <int D, int NQG>
+__global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
+    const float* __restrict__ lse, const float* __restrict__ dvec, float* __restrict__ dq, int T, int H, float scale,
+    float scale_log2) {
   using Sh = BwdShape<D>;
   constexpr int K16 = D / 16, FB = D / 32, LR = Sh::LR, LT = Sh::LT;
-  __shared__ __align__(16) f16 lds[2 * kAttnBlock * LR + D * LT];
+  constexpr int STAGE = 2 * kAttnBlock * LR + D * LT;  // f16: K rows, V rows, K transposed
+  constexpr int XCH = NQG * FB * 64 * 32;              // f16: the key halves' exchange (f32x16 per lane)
+  constexpr int NBLK = 16 * (D / 8);                   // 4-row x 8-feature blocks of one tile
+  constexpr bool SPLIT = 128 * NQG >= 2 * NBLK;        // one block of one tile per thread
+  __shared__ __align__(16) f16 lds[STAGE > XCH ? STAGE : XCH];
   f16 *kr = lds, *vr = lds + kAttnBlock * LR, *ktr = lds + 2 * kAttnBlock * LR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int qh = wave & 1, kh = wave >> 1;
+  const int qh = wave % NQG, kh = wave / NQG;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int qi = blockIdx.x * kAttnBlock + 32 * qh + l32;
+  const int qi = blockIdx.x * (32 * NQG) + 32 * qh + l32;
   f16x8 qf[K16], df[K16];  // B operands: lane l holds Q (dO) of query qi, features 16 s + 8 (l / 32) ..
 #pragma unroll
   for (int s = 0; s < K16; ++s) {
@@ -321,22 +349,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 dqt[FB];
 #pragma unroll
   for (int n = 0; n < FB; ++n) dqt[n] = zero16();
-  TileBlock<D> tk, tv;  // every thread moves one block of the K tile (with its transpose) and one of V
-  tk.init(tid, true);
-  tv.init(tid, true);
+  // SPLIT: threads [0, NBLK) move K blocks (with the transpose), [NBLK, 2 NBLK) V blocks, through
+  // one register block (whole waves either way); otherwise every thread moves block tid of both.
+  const bool mover_k = !SPLIT || tid < NBLK;
+  TileBlock<D> tk, tv;
+  if constexpr (SPLIT) {
+    tk.init(mover_k ? tid : tid - NBLK, true);
+  } else {
+    tk.init(tid, true);
+    tv.init(tid, true);
+  }
+  auto load_block = [&](int r0) {
+    if constexpr (SPLIT) {
+      tk.load(mover_k ? k : v, base, rs, r0, T);
+    } else {
+      tk.load(k, base, rs, r0, T);
+      tv.load(v, base, rs, r0, T);
+    }
+  };
   const int nkb = (T + kAttnBlock - 1) / kAttnBlock;
-  tk.load(k, base, rs, 0, T);
-  tv.load(v, base, rs, 0, T);
+  load_block(0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int r0 = kb * kAttnBlock;
     __syncthreads();
-    tk.store(kr, ktr);
-    tv.store(vr, nullptr);
-    __syncthreads();
-    if (kb + 1 < nkb) {
-      tk.load(k, base, rs, r0 + kAttnBlock, T);
-      tv.load(v, base, rs, r0 + kAttnBlock, T);
+    if constexpr (SPLIT) {
+      if (mover_k) tk.store(kr, ktr);
+      else tk.store(vr, nullptr);
+    } else {
+      tk.store(kr, ktr);
+      tv.store(vr, nullptr);
     }
+    __syncthreads();
+    if (kb + 1 < nkb) load_block(r0 + kAttnBlock);
     f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
     for (int s = 0; s < K16; ++s) {
@@ -364,7 +408,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
   f32x16* xs = reinterpret_cast<f32x16*>(lds) + (size_t)qh * FB * 64;
-  static_assert(2 * FB * 64 * 64 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
+  static_assert(NQG * FB * 64 * 64 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
   if (kh) {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) xs[fb * 64 + lane] = dqt[fb];
@@ -907,15 +951,18 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
   const int rows = a.B * a.T * a.H, rpb = 256 / (D / 4);
   hipLaunchKernelGGL(arl2_bwd_rowdot_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, stream, a.d_out, a.o_sm,
                      static_cast<f16*>(a.do_h), a.dvec, rows, a.T, a.H);
-  const int nb = (a.T + kAttnBlock - 1) / kAttnBlock;
   const bf16* q = static_cast<const bf16*>(a.tok.q);
   const bf16* k = static_cast<const bf16*>(a.tok.k);
   const bf16* v = static_cast<const bf16*>(a.tok.v);
   const f16* doh = static_cast<const f16*>(a.do_h);
-  hipLaunchKernelGGL(arl2_bwd_dkdv_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dk,
-                     a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
-  hipLaunchKernelGGL(arl2_bwd_dq_kernel<D>, dim3(nb, BH), dim3(256), 0, stream, q, k, v, doh, a.lse, a.dvec, a.tok.dq,
-                     a.T, a.H, a.scale, a.scale_log2);
+  constexpr int kDkdvWaves = 8;
+  const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
+  hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(nkb, BH), dim3(64 * kDkdvWaves), 0, stream, q, k, v,
+                     doh, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
+  constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
+  const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
+  hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(nqb, BH), dim3(128 * kDqGroups), 0, stream, q, k, v, doh,
+                     a.lse, a.dvec, a.tok.dq, a.T, a.H, a.scale, a.scale_log2);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
   hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(nch * BH), dim3(512), 0, stream, a.tok);
   hipLaunchKernelGGL(arl2_bwd_gsum_kernel, dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, stream, a.tok.part, a.gr,
