@@ -186,3 +186,41 @@ def test_backward_is_bitwise_reproducible():
         for n in range(2):
             for p in range(2):
                 assert np.array_equal(a[key][n][p], b[key][n][p]), (key, n, p)
+
+
+def test_calls_on_alternating_streams_match_one_stream():
+    """Every call of a sweep on a different stream than the one before (the library makes each
+    new stream wait for the previous one): gradients bitwise equal to the one-stream sweep."""
+    w = Workload("bwd_streams", batch=1, heads=2, head_dim=128, tokens=200, frames=3, denoise_steps=1, seed=64)
+    phis = make_phi(w)
+    fr, d_outs = make_stream(w, 3, 2)
+    g_last = make_state_grad(w)
+    states = forward_states(phis[1].astype(np.float64), phis[2].astype(np.float64), fr,
+                            np.zeros((w.batch, w.heads, w.head_dim, w.head_dim)))
+    staged = [([tuple(dev(x, torch.bfloat16) for x in qkv) for qkv in f["passes"]], dev(f["beta"], torch.float32),
+               dev(f["alpha"], torch.float32), dev(states[n], torch.float32)) for n, f in enumerate(fr)]
+    d_dev = [[dev(x, torch.float32) for x in row] for row in d_outs]
+    g_dev = dev(g_last, torch.float32)
+    torch.cuda.synchronize()
+
+    def sweep(streams):
+        pick = iter(streams * 64)
+        bw = Arl2Backward(*[dev(p, torch.bfloat16) for p in phis], batch=w.batch, tokens=w.tokens)
+        bw.begin(g_dev, stream=next(pick))
+        got = []
+        for n in range(len(fr) - 1, -1, -1):
+            passes, beta, alpha, s_prev = staged[n]
+            grads = [bw.pass_(*qkv, s_prev, d_dev[n][p], stream=next(pick)) for p, qkv in enumerate(passes)]
+            _, k, v = passes[-1]
+            db, da = bw.commit(k, v, beta, alpha, s_prev, grads[-1][1], grads[-1][2], stream=next(pick))
+            got += [x for g in grads for x in g] + [db, da]
+        got += list(bw.read(stream=next(pick)))
+        torch.cuda.synchronize()
+        bw.close()
+        return [x.cpu().numpy() for x in got]
+
+    one = sweep([torch.cuda.current_stream()])
+    two = sweep([torch.cuda.Stream(), torch.cuda.Stream()])  # default priority
+    assert len(one) == len(two)
+    for i, (a, b) in enumerate(zip(one, two)):
+        assert np.array_equal(a, b), i
