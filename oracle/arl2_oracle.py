@@ -73,7 +73,7 @@ def inter_read(q_prime: np.ndarray, s: np.ndarray) -> np.ndarray:
 
 def gate_projections(x: np.ndarray, w_gates: np.ndarray, b_gates: np.ndarray, beta_scale: float = 1.0):
     """alpha and beta from the layer's hidden states ([TS] 2.1: the forget gate alpha and the
-    learning rate beta are learned projections of the tokens; [TS] 3: head-wise gates).
+    learning rate beta are learned projections of the tokens; [TS] 4, ablations: head-wise gates).
 
     x [B, T, H d]; w_gates [2H, H d] (row h: beta of head h, row H + h: alpha of head h);
     b_gates [2H].  beta[b, t, h] = beta_scale * sigmoid(x[b, t] . w_gates[h] + b_gates[h]).
@@ -139,19 +139,17 @@ class Arl2Oracle:
         return out
 
     def query_rows(self, q, k, v, rows) -> np.ndarray:
-        """Outputs of the given token rows only ([B, len(rows), H, d]); the same definition as
-        query() restricted to a subset of query tokens (keys and values stay complete)."""
+        """Outputs of the given token rows only ([B, len(rows), H, d]): query() restricted to a
+        subset of query tokens, built from the same functions (softmax attention treats every
+        query row on its own; keys and values stay complete)."""
         q, k, v = self._check(q, "q"), self._check(k, "k"), self._check(v, "v")
         rows = np.asarray(rows)
         out = np.empty((self.batch, len(rows), self.heads, self.head_dim), dtype=self.dtype)
         for b in range(self.batch):
             for h in range(self.heads):
                 qr = q[b, rows, h]
-                a = (qr @ k[b, :, h].T) * self.scale
-                a = a - a.max(axis=1, keepdims=True)
-                p = np.exp(a)
-                p = p / p.sum(axis=1, keepdims=True)
-                out[b, :, h] = p @ v[b, :, h] + feature_map(qr, self.phi_q[h]) @ self.state[b, h]
+                o_intra = softmax_attention(qr, k[b, :, h], v[b, :, h], self.scale)
+                out[b, :, h] = o_intra + inter_read(feature_map(qr, self.phi_q[h]), self.state[b, h])
         return out
 
     denoise_step = query

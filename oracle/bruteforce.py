@@ -63,3 +63,58 @@ def run_stream(phi_q, phi_k, phi_v, frames, scale=None, eps=1e-6):
         outputs.append(outs)
         states.append(s)
     return outputs, states
+
+
+def seq_run_stream(phi_q, phi_k, phi_v, frames, scale=None, eps=1e-6):
+    """The token-level (sequential) access variant for ONE stream and ONE head, by scalar loops
+    (the alternative to frame-level access that [TS] 2.2 rejects: each token reads, and takes its
+    residual against, the state the frame's earlier tokens have written).
+
+    Same frame format as run_stream.  Every pass computes o_t = softmax branch_t + q'_t S^(t-1)
+    with S^(0) = S_{N-1}; the clean pass then writes the frame's state as the decayed previous
+    state plus the sum of the tokens' increments,
+      S_N[i][j] = alpha S_{N-1}[i][j] + sum_t beta_t k'_t[i] (v'_t[j] - sum_l k'_t[l] S^(t-1)[l][j]),
+    the increments being the ones the running state took.  Denoising passes write nothing.
+    Returns (outputs, states) as run_stream."""
+    phi_q, phi_k, phi_v = _lists(phi_q), _lists(phi_k), _lists(phi_v)
+    d = len(phi_q)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+
+    def mapped(x, phi):
+        return [sum(x[a] * phi[a][c] for a in range(d)) for c in range(d)]
+
+    s_prev = [[0.0] * d for _ in range(d)]
+    outputs, states = [], []
+    for fr in frames:
+        beta = _lists(fr["beta"])
+        outs, incr = [], None
+        for p, (q, k, v) in enumerate(fr["passes"]):
+            q, k, v = _lists(q), _lists(k), _lists(v)
+            T = len(q)
+            run = [row[:] for row in s_prev]  # S^(t-1), starting at S_{N-1}
+            incr = [[0.0] * d for _ in range(d)]  # sum of the increments so far
+            out = []
+            for t in range(T):
+                scores = [scale * sum(q[t][i] * k[u][i] for i in range(d)) for u in range(T)]
+                m = max(scores)
+                w = [math.exp(x - m) for x in scores]
+                z = sum(w)
+                qp = mapped(q[t], phi_q)
+                out.append([sum(w[u] * v[u][j] for u in range(T)) / z + sum(qp[i] * run[i][j] for i in range(d))
+                            for j in range(d)])
+                kp = mapped(k[t], phi_k)
+                norm = math.sqrt(sum(x * x for x in kp))
+                kp = [x / max(norm, eps) for x in kp]
+                vp = mapped(v[t], phi_v)
+                resid = [vp[j] - sum(kp[l] * run[l][j] for l in range(d)) for j in range(d)]
+                for i in range(d):
+                    for j in range(d):
+                        dlt = beta[t] * kp[i] * resid[j]
+                        run[i][j] += dlt
+                        incr[i][j] += dlt
+            outs.append(out)
+        alpha = float(fr["alpha"])
+        s_prev = [[alpha * s_prev[i][j] + incr[i][j] for j in range(d)] for i in range(d)]
+        outputs.append(outs)
+        states.append(s_prev)
+    return outputs, states
