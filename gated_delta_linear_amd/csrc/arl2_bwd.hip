@@ -17,9 +17,10 @@
 //                   dphi_k += K^T dU
 //
 // Kernels.  The attention backward runs as two MFMA kernels with no atomics (bitwise
-// reproducible): dK, dV per 64-key block (the keys' fragments stay in registers, query blocks
-// stream through LDS) and dQ per 64-query block (key blocks stream through LDS); the scores
-// are recomputed in each.  Their products run in fp16 with fp32 accumulation: the bf16 inputs
+// reproducible), 8 waves per work-group: dK, dV per 128-key block, 16 keys per wave (the keys'
+// fragments stay in registers, 64-query blocks stream through LDS), and dQ per 128-query block,
+// four 32-query groups times two key halves (64-key blocks stream through LDS); the scores are
+// recomputed in each.  Their products run in fp16 with fp32 accumulation: the bf16 inputs
 // convert exactly, and P, dS and dO round with a relative step of 2^-11.  The
 // token kernels (inter read, state write) work per 128-token chunk with 16x16x32 MFMAs on
 // split-bf16 operands (hi + lo, three products per term), so that their d x d products keep

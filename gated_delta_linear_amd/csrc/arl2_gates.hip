@@ -1,6 +1,6 @@
 // Gate projections of the ARL2 state write ("Attend Locally, Remember Linearly", gist.science
 // technical summary, section 2.1: alpha, the forget gate, and beta, the learning rate, are
-// learned projections of the tokens; section 3: head-wise gates):
+// learned projections of the tokens; section 4, ablations: head-wise gates):
 //   beta[b][t][h] = beta_scale * sigmoid(x[b][t] . w[h] + bias[h])
 //   alpha logit partial[b][blk][h] = sum over tokens t of block blk of x[b][t] . w[H + h]
 // from the layer's input hidden states x [B][T][H d] bf16 and the gate weights w [2H][H d]

@@ -6,7 +6,7 @@
  * Autoregressive Video Diffusion" - the technical summary on gist.science (section 1, the
  * problem: autoregressive video DiTs attend over a key-value cache that grows by one block
  * per generated frame; section 2, the two-stage conversion in which the layers not replaced
- * keep softmax attention; section 3, the memory and speed comparison against that baseline)
+ * keep softmax attention; section 4, the memory and speed comparison against that baseline)
  * and the authors' abstract (fugumt.com page of the same title).
  *
  * One layer object holds, for B independent streams and H heads, a cache of the clean keys

@@ -8,7 +8,7 @@ numpy float64; inputs are the values the GPU receives.
 
 Source.  [TS] technical summary "Attend Locally, Remember Linearly" (gist.science), section 2.2
 (frame-level access: every token of a frame reads the same pre-update state, to avoid an
-information asymmetry inside the frame) and the ablations of section 3; [ABS] the authors'
+information asymmetry inside the frame) and the ablations of section 4 (experimental results); [ABS] the authors'
 abstract, which makes the same choice against updating the state token by token.  This module
 is the alternative those passages reject, built as an A/B of the frame-level design.
 

@@ -11,7 +11,7 @@ Sources.  [TS] is the technical summary "Attend Locally, Remember Linearly: Line
 as Cross-Frame Memory for Autoregressive Video Diffusion" on gist.science: section 1 (the
 problem) describes autoregressive video DiTs whose softmax self-attention keeps a key-value
 cache that grows by one block per generated frame, and section 2 keeps softmax attention in
-the layers the conversion does not replace; section 3 compares the hybrid model's memory and
+the layers the conversion does not replace; section 4 compares the hybrid model's memory and
 speed with that baseline.  [ABS] is the authors' abstract (fugumt.com page of the same title):
 softmax self-attention with key-value caching is what ARL2's fixed-size state replaces.
 

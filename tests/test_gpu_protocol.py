@@ -157,7 +157,7 @@ def test_token_permutation():
                              dev(beta[:, perm], torch.float32), dev(alpha, torch.float32))
     s1, s2 = layer.state().double().cpu().numpy(), layer2.state().double().cpu().numpy()
     o1, o2 = o1.double().cpu().numpy(), o2.double().cpu().numpy()
-    # Reordering changes which keys share a 64-key tile, hence the running max that bf16 P is
+    # Reordering changes which keys share a 32-key unit, hence the running max that fp16 P is
     # rounded against: differences at the 1e-4 level are rounding; a token-sequential write
     # would differ at order 1.
     e_out, e_state = out_err(o2, o1[:, perm]), state_err(s2, s1)
@@ -232,4 +232,43 @@ def test_graph_replays_match_eager():
                 assert scratch == scratch
                 assert torch.equal(out, ref_out[(f + 1) * per - 1]), (rep, f)
                 assert torch.equal(st, ref_st[f]), (rep, f)
+        layer.close()
+
+
+def test_one_frame_graph_replayed_frame_after_frame():
+    """One frame captured once (its denoising passes, the clean pass and the state read, on fixed
+    input buffers) and replayed for every frame of a stream, the buffers refilled eagerly between
+    replays: each replay advances the state exactly as the eager calls do (an odd number of
+    commits per graph, and the same graph every frame)."""
+    frames = 5
+    ref_out, ref_st = _run(_layer(W), W, frames)
+    per = W.denoise_steps + 1
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        layer = _layer(W)
+        slots = [(tuple(torch.empty_like(x) for x in _frame_tensors(W, 0, p)),
+                  tuple(torch.empty_like(x) for x in _gates(W, 0))) for p in range(per)]
+        out = layer.new_output()
+        st = torch.empty(layer.state_shape, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for p in range(per):
+                (q, k, v), (beta, alpha) = slots[p]
+                if p < W.denoise_steps:
+                    layer.denoise_step(q, k, v, out=out, stream=stream)
+                else:
+                    layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
+            layer.state(out=st, stream=stream)
+        torch.cuda.synchronize()
+        layer.load_state(torch.zeros_like(st), 0, stream=stream)
+        for f in range(frames):
+            for p in range(per):
+                for dst, src in zip(slots[p][0] + slots[p][1], _frame_tensors(W, f, p) + _gates(W, f)):
+                    dst.copy_(src)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out[(f + 1) * per - 1]), f
+            assert torch.equal(st, ref_st[f]), f
         layer.close()

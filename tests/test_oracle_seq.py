@@ -4,7 +4,7 @@ orthogonal keys), delta-rule retrieval, dependence on token order (the frame-lev
 permutation equivariance fails here), and planted mistakes.
 
 Sources: "Attend Locally, Remember Linearly" technical summary (gist.science), section 2.2
-(frame-level access) and section 3 (ablations); the authors' abstract.
+(frame-level access) and section 4 (experimental results, ablations); the authors' abstract.
 """
 import numpy as np
 import pytest
