@@ -160,17 +160,21 @@ def _dev_tensor(x: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) ->
 class Arl2Layer:
     """One ARL2 layer on the current GPU (see include/arl2.h for the exact semantics).
 
-    phi_q, phi_k, phi_v: bf16 [H, d, d] device tensors (copied at creation).  Frame tensors
-    q, k, v are bf16 [B, T, H, d]; beta fp32 [B, T, H]; alpha fp32 [B, H]."""
+    phi_q, phi_k, phi_v: [H, d, d] device tensors of io_dtype (copied at creation).  Frame
+    tensors q, k, v are io_dtype [B, T, H, d]; beta fp32 [B, T, H]; alpha fp32 [B, H].
+    io_dtype is torch.bfloat16 or torch.float32 (rounded to bf16, nearest even, on the device)."""
 
     def __init__(self, phi_q: torch.Tensor, phi_k: torch.Tensor, phi_v: torch.Tensor, batch: int, tokens: int,
                  out_dtype: torch.dtype = torch.float32, softmax_scale: float = 0.0, knorm_eps: float = 0.0,
-                 stream=None, access: str = "frame"):
+                 stream=None, access: str = "frame", io_dtype: torch.dtype = torch.bfloat16):
         self._lib = load_library()
         self._handle = c_void_p()
+        if io_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("io_dtype must be torch.bfloat16 or torch.float32")
+        self.io_dtype = io_dtype
         heads, d, _ = phi_q.shape
         for name, t in (("phi_q", phi_q), ("phi_k", phi_k), ("phi_v", phi_v)):
-            _dev_tensor(t, name, torch.bfloat16, (heads, d, d))
+            _dev_tensor(t, name, io_dtype, (heads, d, d))
         if out_dtype not in (torch.float32, torch.bfloat16):
             raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
         self.batch, self.heads, self.head_dim, self.tokens = int(batch), int(heads), int(d), int(tokens)
@@ -179,7 +183,8 @@ class Arl2Layer:
         if access not in ("frame", "token"):
             raise ValueError("access must be 'frame' or 'token'")
         self.access = access
-        cfg = Arl2Config(self.batch, self.heads, self.head_dim, self.tokens, ARL2_BF16,
+        cfg = Arl2Config(self.batch, self.heads, self.head_dim, self.tokens,
+                         ARL2_F32 if io_dtype == torch.float32 else ARL2_BF16,
                          ARL2_F32 if out_dtype == torch.float32 else ARL2_BF16, float(softmax_scale), float(knorm_eps),
                          ARL2_ACCESS_FRAME if access == "frame" else ARL2_ACCESS_TOKEN)
         with torch.cuda.device(self.device):
@@ -207,20 +212,20 @@ class Arl2Layer:
     # --- the protocol -------------------------------------------------------------------
     def denoise_step(self, q, k, v, out=None, stream=None) -> torch.Tensor:
         out = self.new_output() if out is None else out
-        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        args = [_dev_tensor(x, n, self.io_dtype, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
         po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
         _check(self._lib.arl2_denoise_step(self._ptr(), *args, po, _stream_handle(stream)), "arl2_denoise_step")
         return out
 
     def commit_frame(self, q, k, v, beta, alpha, out=None, want_output: bool = True, stream=None):
         B, T, H, _ = self.frame_shape
-        pk = _dev_tensor(k, "k", torch.bfloat16, self.frame_shape)
-        pv = _dev_tensor(v, "v", torch.bfloat16, self.frame_shape)
+        pk = _dev_tensor(k, "k", self.io_dtype, self.frame_shape)
+        pv = _dev_tensor(v, "v", self.io_dtype, self.frame_shape)
         pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
         pa = _dev_tensor(alpha, "alpha", torch.float32, (B, H))
         if want_output or out is not None:
             out = self.new_output() if out is None else out
-            pq = _dev_tensor(q, "q", torch.bfloat16, self.frame_shape)
+            pq = _dev_tensor(q, "q", self.io_dtype, self.frame_shape)
             po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
         else:
             pq, po = (q.data_ptr() if isinstance(q, torch.Tensor) else None), None
@@ -233,14 +238,14 @@ class Arl2Layer:
         """The clean pass with alpha and beta from the gate projections of the hidden states x
         (bf16 [B, T, H d]); w_gates bf16 [2H, H d], b_gates fp32 [2H] (see include/arl2.h)."""
         B, T, H, d = self.frame_shape
-        pk = _dev_tensor(k, "k", torch.bfloat16, self.frame_shape)
-        pv = _dev_tensor(v, "v", torch.bfloat16, self.frame_shape)
+        pk = _dev_tensor(k, "k", self.io_dtype, self.frame_shape)
+        pv = _dev_tensor(v, "v", self.io_dtype, self.frame_shape)
         px = _dev_tensor(x, "x", torch.bfloat16, (B, T, H * d))
         pw = _dev_tensor(w_gates, "w_gates", torch.bfloat16, (2 * H, H * d))
         pb = _dev_tensor(b_gates, "b_gates", torch.float32, (2 * H,))
         if want_output or out is not None:
             out = self.new_output() if out is None else out
-            pq = _dev_tensor(q, "q", torch.bfloat16, self.frame_shape)
+            pq = _dev_tensor(q, "q", self.io_dtype, self.frame_shape)
             po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
         else:
             pq, po = None, None
@@ -252,7 +257,7 @@ class Arl2Layer:
     def denoise_step_seq(self, q, k, v, beta, out=None, stream=None) -> torch.Tensor:
         B, T, H, _ = self.frame_shape
         out = self.new_output() if out is None else out
-        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        args = [_dev_tensor(x, n, self.io_dtype, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
         pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
         po = _dev_tensor(out, "out", self.out_dtype, self.frame_shape)
         _check(self._lib.arl2_denoise_step_seq(self._ptr(), *args, pb, po, _stream_handle(stream)),
@@ -261,7 +266,7 @@ class Arl2Layer:
 
     def commit_frame_seq(self, q, k, v, beta, alpha, out=None, want_output: bool = True, stream=None):
         B, T, H, _ = self.frame_shape
-        args = [_dev_tensor(x, n, torch.bfloat16, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        args = [_dev_tensor(x, n, self.io_dtype, self.frame_shape) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
         pb = _dev_tensor(beta, "beta", torch.float32, (B, T, H))
         pa = _dev_tensor(alpha, "alpha", torch.float32, (B, H))
         po = None

@@ -12,7 +12,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libarl2.so")
-SOURCES = ["arl2_fwd.hip", "arl2_commit.hip", "arl2_kvcache.hip", "arl2_gates.hip", "arl2_seq.hip", "arl2_bwd.hip",
+SOURCES = ["arl2_fwd.hip", "arl2_commit.hip", "arl2_kvcache.hip", "arl2_gates.hip", "arl2_seq.hip", "arl2_bwd.hip", "arl2_convert.hip",
            "arl2_host.cpp", "arl2_softmax_host.cpp", "arl2_bwd_host.cpp"]
 ARCH = "gfx950"
 
@@ -33,20 +33,41 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into libarl2.so; always recompiles."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd: list[str]) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
-    if verbose and msgs.strip():
-        print(msgs)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{msgs}")
+    return msgs
+
+
+def build_library(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every HIP source into libarl2.so; always recompiles (one object per source, in
+    parallel, under _build/, then one link)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    flags = [f for f in compile_flags() if f != "-shared"]
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        cmds.append((obj, [hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]))
+    jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        for (obj, cmd), msgs in zip(cmds, pool.map(lambda c: _run(c[1]), cmds)):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+                if msgs.strip():
+                    print(msgs)
+    tmp = LIB_PATH + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *[o for o, _ in cmds], "-o", tmp]
+    msgs = _run(link)
+    if verbose:
+        print(" ".join(link), flush=True)
+        if msgs.strip():
+            print(msgs)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

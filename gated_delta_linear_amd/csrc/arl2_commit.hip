@@ -32,14 +32,17 @@ struct CommitShape {
 
 constexpr int kReduceThreads = 512;
 
+// s_prev and s_new may be the same buffer (the layer updates S in place): each element of S_new is
+// stored by the thread that loaded the same element of s_prev, and no other thread reads it.
+//
 // One work-group per (stream, head, 16 value columns): a 16-column stripe keeps the chunk sum
 // spread over DP / 16 work-groups per head (the partials are read once, and one CU's load path
 // is what bounds each work-group), and it is one 16x16 MFMA block wide for W.
 template <int D>
 __global__ __launch_bounds__(kReduceThreads) void arl2_commit_reduce_kernel(
-    const float* __restrict__ s_prev, const float* __restrict__ alpha, const float* __restrict__ alpha_part,
+    const float* s_prev, const float* __restrict__ alpha, const float* __restrict__ alpha_part,
     const float* __restrict__ alpha_bias, int n_ablk, int T, const float* __restrict__ partial,
-    int chunks, const bf16* __restrict__ pq, float* __restrict__ s_new, bf16* __restrict__ sneg_hi,
+    int chunks, const bf16* __restrict__ pq, float* s_new, bf16* __restrict__ sneg_hi,
     bf16* __restrict__ sneg_lo, bf16* __restrict__ wt_hi, bf16* __restrict__ wt_lo, int H) {
   using S = CommitShape<D>;
   constexpr int DP = S::DP, FB = S::FB, KS32 = S::KS32;

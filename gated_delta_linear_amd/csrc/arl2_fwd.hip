@@ -43,8 +43,7 @@
 // scale folded in; the running max is only raised when a unit's max exceeds it by more than
 // 8 (in log2 units) in some lane of the wave, so P stays below 2^8 and the rescale of the
 // accumulator is skipped on almost every unit.  Row sums add the rounded P that enters the
-// MFMA in fp16 pairs within a unit (at most 16 terms of at most 2^8, relative rounding 2^-11
-// per add) and in fp32 across units.
+// MFMA, two fp16 values per dot-product instruction with fp32 accumulation.
 #include <type_traits>
 
 #include "arl2_device.h"
@@ -386,9 +385,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Softmax of score registers [v0, v1) of a unit (v1 - v0 a multiple of 4) into fp16 pairs:
   // registers i, i + 1 of the score block become word (i / 2) % 4 of pw[i / 8], the P^T
-  // fragment of k-step i / 8; and the unit's row sum lsum (fp16 pairs of the rounded P that
-  // enters the MFMA).  A fragment is pinned once complete.
-  auto softmax_part = [&](const f32x16& sa, u32x4 (&pw)[2], int v0, int v1, float mc, f16x2& lsum) ARL2_INLINE {
+  // fragment of k-step i / 8; and adds the rounded P that enters the MFMA to the running row sum
+  // (fp32).  A fragment is pinned once complete.
+  const f16x2 ones = {(f16)1.f, (f16)1.f};
+  auto softmax_part = [&](const f32x16& sa, u32x4 (&pw)[2], int v0, int v1, float mc) ARL2_INLINE {
 #pragma unroll
     for (int jj = v0; jj < v1; jj += 4) {
       f16x2 p[2];
@@ -400,10 +400,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         p[e] = __builtin_convertvector(x, f16x2);
         pw[i >> 3][(i >> 1) & 3] = __builtin_bit_cast(unsigned, p[e]);
       }
-      lsum += p[0] + p[1];
+      l_run = __builtin_amdgcn_fdot2(p[0], ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(p[1], ones, l_run, false);
     }
     if (v1 % 8 == 0) pin(pw[(v1 - 1) >> 3]);
-    pin(lsum);
+    pin(l_run);
   };
   // Keys of unit u past the end of this wave's keys do not take part.
   auto mask_unit = [&](int u, f32x16& sc) ARL2_INLINE {
@@ -460,20 +461,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     };
     u32x4 pw[2];
-    f16x2 lsum = {(f16)0.f, (f16)0.f};
     read_stage(0);
     read_stage(1);
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
       hook(t);
       read_stage(t + 2);
-      if (cu) softmax_part(sa, pw, t * 16 / NA, (t + 1) * 16 / NA, mc, lsum);
+      if (cu) softmax_part(sa, pw, t * 16 / NA, (t + 1) * 16 / NA, mc);
       if (nx)
 #pragma unroll
         for (int f = t * FA; f < (t + 1) * FA; ++f) sb = mfma32(kfr[f], qf[f], f ? sb : zero16());
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (cu) l_run += (float)lsum[0] + (float)lsum[1];
     float mp = -INFINITY;
     if (nx) {
       mask_unit(u + 1, sb);

@@ -2,8 +2,10 @@
 //
 // It owns the protocol of "Attend Locally, Remember Linearly" (gist.science technical
 // summary, section 2.2): passes of a frame only read the state, the clean pass writes it
-// once, and every pass of frame N reads S_{N-1}.  S is double-buffered: the write reads one
-// buffer and fills the other, and the buffers swap when the frame index advances.
+// once, and every pass of frame N reads S_{N-1}.  S lives in one buffer that the write updates
+// in place (every element of S_N is written by the thread that read the same element of
+// S_{N-1}, after the pass kernels that read S's derived forms), so the device addresses every
+// call uses are fixed: a captured graph of any number of frames replays the protocol.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -57,8 +59,7 @@ struct arl2_layer {
   // one device slab, carved into the regions below
   void* slab = nullptr;
   size_t bytes = 0;
-  float* s[2] = {nullptr, nullptr};  // S, fp32 [B][H][d][d], ping-pong
-  int cur = 0;                       // index of S_{N-1} (the state every pass reads)
+  float* s = nullptr;                // S, fp32 [B][H][d][d], updated in place by the write
   float* partial = nullptr;          // [B][H][chunks][dp][dp]
   void* sneg_hi = nullptr;           // -S as B fragments, bf16 [B][H][dp/32][dp/16][64][8]
   void* sneg_lo = nullptr;
@@ -72,6 +73,8 @@ struct arl2_layer {
   float* o_inter = nullptr;          // token-level access: inter-frame reads, fp32 [B][T][H][d]
   float* gate_beta = nullptr;        // beta from the gate projection, fp32 [B][T][H]
   float* gate_alpha = nullptr;       // alpha logit sums per 32-token block, fp32 [B][gate_blocks(T)][H]
+  void* stage[3] = {nullptr, nullptr, nullptr};  // io_dtype F32: q, k, v rounded to bf16 [B][T][H][d]
+  int64_t frame_elems = 0;                        // B T H d
   int n_ablk = 0;
   int64_t frame = 0;
   bool poisoned = false;
@@ -148,10 +151,11 @@ arl2_status launch_pass(arl2_layer* L, const void* q, const void* k, const void*
                       w ? "clean pass and state write launch" : "pass kernel launch");
 }
 
-// Derive S_N = alpha S_prev + partials (chunks may be 0) into s[dst], plus its derived forms;
-// alpha from the gate projection's partial sums when alpha_bias is not null.
-arl2_status launch_reduce(arl2_layer* L, const float* s_prev, const float* alpha, int chunks, int dst,
-                          hipStream_t stream, const float* alpha_bias = nullptr) {
+// Derive S_N = alpha S_prev + partials (chunks may be 0) into the layer's S (s_prev may be S
+// itself: the reduce updates it in place), plus its derived forms; alpha from the gate
+// projection's partial sums when alpha_bias is not null.
+arl2_status launch_reduce(arl2_layer* L, const float* s_prev, const float* alpha, int chunks, hipStream_t stream,
+                          const float* alpha_bias = nullptr) {
   arl2::CommitReduceArgs r;
   r.s_prev = s_prev;
   r.alpha = alpha;
@@ -164,7 +168,7 @@ arl2_status launch_reduce(arl2_layer* L, const float* s_prev, const float* alpha
   r.partial = L->partial;
   r.chunks = chunks;
   r.pq = L->pq;
-  r.s_new = L->s[dst];
+  r.s_new = L->s;
   r.sneg_hi = L->sneg_hi;
   r.sneg_lo = L->sneg_lo;
   r.wt_hi = L->wt_hi;
@@ -197,10 +201,27 @@ arl2_status commit(arl2_layer* L, const void* q, const void* k, const void* v, c
   w.knorm_eps = L->eps;
   arl2_status st;
   if ((st = launch_pass(L, q, k, v, out, &w, stream))) return st;
-  if ((st = launch_reduce(L, L->s[L->cur], alpha, L->chunks, L->cur ^ 1, stream, alpha_bias))) return st;
-  L->cur ^= 1;
+  if ((st = launch_reduce(L, L->s, alpha, L->chunks, stream, alpha_bias))) return st;
   L->frame += 1;
   return ARL2_OK;
+}
+
+// io_dtype F32: round the caller's fp32 q, k, v (those not null) to bf16 into the layer's staging
+// copies and point the call at them; io_dtype BF16: nothing to do.
+arl2_status stage_inputs(arl2_layer* L, const void*& q, const void*& k, const void*& v, hipStream_t stream) {
+  if (L->cfg.io_dtype != ARL2_F32) return ARL2_OK;
+  arl2::CvtJobs j{};
+  int n = 0;
+  const void** ptr[3] = {&q, &k, &v};
+  for (int i = 0; i < 3; ++i) {
+    if (!*ptr[i]) continue;
+    j.src[n] = static_cast<const float*>(*ptr[i]);
+    j.dst[n] = L->stage[i];
+    *ptr[i] = L->stage[i];
+    ++n;
+  }
+  if (n == 0) return ARL2_OK;
+  return after_launch(L, arl2::launch_cvt_bf16(j, n, L->frame_elems, stream), stream, "fp32 input conversion launch");
 }
 
 }  // namespace
@@ -234,7 +255,7 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
     return fail(ARL2_E_INVALID_ARG, "tokens_per_frame must be in [1, %d]", ARL2_MAX_TOKENS);
   if (c.head_dim != 16 && c.head_dim != 64 && c.head_dim != 128)
     return fail(ARL2_E_UNSUPPORTED, "head_dim %d not supported (16, 64, 128)", c.head_dim);
-  if (c.io_dtype != ARL2_BF16) return fail(ARL2_E_UNSUPPORTED, "io_dtype must be ARL2_BF16");
+  if (c.io_dtype != ARL2_BF16 && c.io_dtype != ARL2_F32) return fail(ARL2_E_INVALID_ARG, "bad io_dtype");
   if (c.access != ARL2_ACCESS_FRAME && c.access != ARL2_ACCESS_TOKEN) return fail(ARL2_E_INVALID_ARG, "bad access");
   if (c.access == ARL2_ACCESS_TOKEN && c.head_dim == 16)
     return fail(ARL2_E_UNSUPPORTED, "token-level access supports head_dim 64 and 128");
@@ -296,8 +317,12 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   const bool seq = c.access == ARL2_ACCESS_TOKEN;
   const size_t seqws_bytes = seq ? align_up(arl2::seq_workspace_bytes(L->d, c.batch, c.heads, c.tokens_per_frame)) : 0;
   const size_t oint_bytes = seq ? align_up((size_t)c.batch * c.tokens_per_frame * c.heads * d * sizeof(float)) : 0;
-  L->bytes = 2 * s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + gbeta_bytes + galpha_bytes + seqws_bytes +
-             oint_bytes + pq_bytes + 3 * map_bytes;
+  const bool f32 = c.io_dtype == ARL2_F32;
+  L->frame_elems = (int64_t)c.batch * c.tokens_per_frame * c.heads * c.head_dim;
+  const size_t stage_bytes = f32 ? align_up((size_t)L->frame_elems * 2) : 0;
+  const size_t phi_stage_bytes = f32 ? align_up((size_t)c.heads * d * d * 2) : 0;
+  L->bytes = s_bytes + part_bytes + 2 * frag_bytes + 2 * wt_bytes + gbeta_bytes + galpha_bytes + seqws_bytes +
+             oint_bytes + 3 * stage_bytes + 3 * phi_stage_bytes + pq_bytes + 3 * map_bytes;
   if ((e = hipMalloc(&L->slab, L->bytes)) != hipSuccess) {
     (void)hipGetLastError();
     const size_t want = L->bytes;
@@ -305,8 +330,7 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
     return fail(ARL2_E_OUT_OF_MEMORY, "hipMalloc(%zu bytes): %s", want, hipGetErrorString(e));
   }
   char* p = static_cast<char*>(L->slab);
-  L->s[0] = reinterpret_cast<float*>(p); p += s_bytes;
-  L->s[1] = reinterpret_cast<float*>(p); p += s_bytes;
+  L->s = reinterpret_cast<float*>(p); p += s_bytes;
   L->partial = reinterpret_cast<float*>(p); p += part_bytes;
   L->sneg_hi = p; p += frag_bytes;
   L->sneg_lo = p; p += frag_bytes;
@@ -317,6 +341,13 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   if (seq) {
     L->seq_ws = p; p += seqws_bytes;
     L->o_inter = reinterpret_cast<float*>(p); p += oint_bytes;
+  }
+  void* phi_stage[3] = {nullptr, nullptr, nullptr};
+  for (int i = 0; i < 3 && f32; ++i) {
+    L->stage[i] = p; p += stage_bytes;
+  }
+  for (int i = 0; i < 3 && f32; ++i) {
+    phi_stage[i] = p; p += phi_stage_bytes;
   }
   L->pq = p; p += pq_bytes;
   L->pkt = p; p += map_bytes;
@@ -335,6 +366,16 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   // S_0 = 0 and everything derived from it is 0 as well.
   if ((e = hipMemsetAsync(L->slab, 0, L->bytes - pq_bytes - 3 * map_bytes, stream)) != hipSuccess)
     return bail(e, "hipMemsetAsync");
+  if (f32) {  // the maps arrive in fp32: round them to bf16 first
+    arl2::CvtJobs j{{static_cast<const float*>(phi_q), static_cast<const float*>(phi_k),
+                     static_cast<const float*>(phi_v)},
+                    {phi_stage[0], phi_stage[1], phi_stage[2]}};
+    if ((e = arl2::launch_cvt_bf16(j, 3, (int64_t)c.heads * d * d, stream)) != hipSuccess)
+      return bail(e, "fp32 map conversion launch");
+    phi_q = phi_stage[0];
+    phi_k = phi_stage[1];
+    phi_v = phi_stage[2];
+  }
   arl2::PrepMapsArgs pm{phi_q, phi_k, phi_v, L->pq, L->pkt, L->pvt, L->pqt, c.heads};
   if ((e = arl2::launch_prep_maps(L->d, pm, stream)) != hipSuccess) return bail(e, "map preparation launch");
   if (debug_sync() && (e = hipStreamSynchronize(stream)) != hipSuccess) return bail(e, "map preparation");
@@ -350,7 +391,7 @@ arl2_status arl2_denoise_step(arl2_layer* L, const void* q, const void* k, const
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")))
     return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if ((st = use_stream(L, stream))) return st;
+  if ((st = use_stream(L, stream)) || (st = stage_inputs(L, q, k, v, stream))) return st;
   return launch_pass(L, q, k, v, out, nullptr, stream);
 }
 
@@ -368,9 +409,9 @@ static arl2_status seq_pass(arl2_layer* L, const void* q, const void* k, const v
   a.pkt = L->pkt;
   a.pvt = L->pvt;
   a.ws = L->seq_ws;
-  a.s_prev = L->s[L->cur];
+  a.s_prev = L->s;
   a.alpha = alpha;
-  a.s_new = alpha ? L->s[L->cur ^ 1] : nullptr;
+  a.s_new = alpha ? L->s : nullptr;  // in place: each wave reads its columns of S first, writes them last
   a.o_inter = L->o_inter;
   a.B = L->cfg.batch;
   a.H = L->cfg.heads;
@@ -405,7 +446,7 @@ arl2_status arl2_denoise_step_seq(arl2_layer* L, const void* q, const void* k, c
       (st = check_ptr(beta, "beta")) || (st = check_ptr(out, "out")))
     return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if ((st = use_stream(L, stream))) return st;
+  if ((st = use_stream(L, stream)) || (st = stage_inputs(L, q, k, v, stream))) return st;
   return seq_pass(L, q, k, v, beta, nullptr, out, stream);
 }
 
@@ -418,10 +459,9 @@ arl2_status arl2_commit_frame_seq(arl2_layer* L, const void* q, const void* k, c
     return st;
   if (out && !aligned16(out)) return fail(ARL2_E_INVALID_ARG, "out is not 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if ((st = use_stream(L, stream))) return st;
+  if ((st = use_stream(L, stream)) || (st = stage_inputs(L, q, k, v, stream))) return st;
   if ((st = seq_pass(L, q, k, v, beta, alpha, out, stream))) return st;
-  // derived forms of S_N are only read by frame-level passes; the state buffers swap
-  L->cur ^= 1;
+  // (the derived forms of S_N are only read by frame-level passes)
   L->frame += 1;
   return ARL2_OK;
 }
@@ -436,7 +476,8 @@ arl2_status arl2_commit_frame(arl2_layer* L, const void* q, const void* k, const
   if (out && (st = check_ptr(q, "q"))) return st;
   if (out && !aligned16(out)) return fail(ARL2_E_INVALID_ARG, "out is not 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if ((st = use_stream(L, stream))) return st;
+  if (!out) q = nullptr;  // not read without an output
+  if ((st = use_stream(L, stream)) || (st = stage_inputs(L, q, k, v, stream))) return st;
   return commit(L, q, k, v, beta, alpha, nullptr, out, stream);
 }
 
@@ -457,7 +498,8 @@ arl2_status arl2_commit_frame_gated(arl2_layer* L, const void* q, const void* k,
   if ((int64_t)2 * L->cfg.heads * L->cfg.heads * L->d * 2 >= (int64_t(1) << 31))
     return fail(ARL2_E_UNSUPPORTED, "gate weights (2H x H d bf16) must stay below 2 GiB");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if ((st = use_stream(L, stream))) return st;
+  if (!out) q = nullptr;  // not read without an output
+  if ((st = use_stream(L, stream)) || (st = stage_inputs(L, q, k, v, stream))) return st;
   arl2::GateArgs g{x, w_gates, b_gates, beta_scale, L->gate_beta, L->gate_alpha,
                    L->cfg.batch, L->cfg.heads, L->d, L->cfg.tokens_per_frame};
   if ((st = after_launch(L, arl2::launch_gates(g, stream), stream, "gate projection launch"))) return st;
@@ -483,7 +525,7 @@ arl2_status arl2_state_read(arl2_layer* L, float* dst, void* stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if ((st = use_stream(L, stream))) return st;
   const size_t n = (size_t)L->cfg.batch * L->cfg.heads * L->d * L->d * sizeof(float);
-  hipError_t e = hipMemcpyAsync(dst, L->s[L->cur], n, hipMemcpyDeviceToDevice, stream);
+  hipError_t e = hipMemcpyAsync(dst, L->s, n, hipMemcpyDeviceToDevice, stream);
   return after_launch(L, e, stream, "state read copy");
 }
 
@@ -495,8 +537,8 @@ arl2_status arl2_state_write(arl2_layer* L, const float* src, int64_t frame_inde
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   L->poisoned = false;
   if ((st = use_stream(L, stream))) return st;
-  // S = 1 * src with no partials, stored into the buffer the next pass reads.
-  if ((st = launch_reduce(L, src, nullptr, 0, L->cur, stream))) {
+  // S = 1 * src with no partials, and the derived forms the next passes read.
+  if ((st = launch_reduce(L, src, nullptr, 0, stream))) {
     L->poisoned = true;
     return st;
   }

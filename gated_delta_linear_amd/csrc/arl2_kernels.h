@@ -144,6 +144,14 @@ struct PrepMapsArgs {
 };
 hipError_t launch_prep_maps(int d, const PrepMapsArgs& a, hipStream_t stream);
 
+// fp32 -> bf16 (round to nearest even) of up to three tensors of n values each (n % 8 == 0,
+// 16-byte aligned): the staging of fp32 inputs (io_dtype ARL2_F32).
+struct CvtJobs {
+  const float* src[3];
+  void* dst[3];
+};
+hipError_t launch_cvt_bf16(const CvtJobs& jobs, int n_jobs, int64_t n, hipStream_t stream);
+
 // --- backward (arl2_bwd.hip) -------------------------------------------------------------------
 // Per (stream, head) d x d matrices in 16x16x32 B-fragment order ([d/32][d/16][64][8] bf16:
 // lane l of fragment (s, nb) holds M[32 s + 8 (l / 16) + j][16 nb + l % 16]), split into hi + lo

@@ -1,6 +1,6 @@
 // Token-level (sequential) access variant of the ARL2 layer: the alternative to frame-level
 // access that the pages reject ("Attend Locally, Remember Linearly", gist.science technical
-// summary, section 2.2: every token of a frame reads the same pre-update state; section 3:
+// summary, section 2.2: every token of a frame reads the same pre-update state; section 4:
 // ablations), built as an A/B.  Per (stream, head) and frame, with Q' = Q phi_q,
 // K' = unit_rows(K phi_k), V' = V phi_v and the frame's tokens in order:
 //   o_t = softmax branch_t + q'_t S^(t-1),   S^(0) = S_{N-1},
@@ -303,9 +303,9 @@ __global__ __launch_bounds__(256) void arl2_seq_prep_kernel(const bf16* __restri
 
 template <int D>
 __global__ __launch_bounds__(256) void arl2_seq_scan_kernel(const unsigned char* __restrict__ ws,
-                                                            const float* __restrict__ s_prev,
+                                                            const float* s_prev,
                                                             const float* __restrict__ alpha,
-                                                            float* __restrict__ s_new, float* __restrict__ o_inter,
+                                                            float* s_new, float* __restrict__ o_inter,
                                                             int T, int H, int n_chunks) {
   using S = SeqShape<D>;
   constexpr int KS = S::KS, FB = S::FB;
@@ -334,6 +334,7 @@ __global__ __launch_bounds__(256) void arl2_seq_scan_kernel(const unsigned char*
   };
 
   // The slice of S (C blocks [key-feature block fb]: S[16 fb + 4 (l / 16) + i][16 slice + l % 16]).
+  // Only this wave reads or writes these columns, so s_new may be s_prev (S updated in place).
   const float* sp = s_prev + (int64_t)bh * D * D;
   f32x4 s[FB], s0[FB];
 #pragma unroll

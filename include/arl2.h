@@ -31,10 +31,12 @@
  * Tensors (all device memory, contiguous, row-major, 16-byte aligned, owned by the caller
  * and required to stay valid until the work enqueued on the stream has finished):
  *   q, k, v     bf16  [B][T][H][d]        token-major, as a fused QKV projection emits them
+ *                                         (fp32 with io_dtype ARL2_F32)
  *   out         fp32 or bf16 (config) [B][T][H][d]
  *   beta        fp32  [B][T][H]
  *   alpha       fp32  [B][H]
  *   phi_q/k/v   bf16  [H][d][d]           phi[h][i][j], read once by arl2_layer_create
+ *                                         (fp32 with io_dtype ARL2_F32)
  *   state       fp32  [B][H][d][d]        S[b][h][i][j]: i = key feature, j = value feature
  *
  * Arithmetic: Q K^T and the inter-frame read use bf16 products with fp32 accumulation (the
@@ -42,6 +44,12 @@
  * fp32; P V multiplies P rounded to fp16 by V converted to fp16, which is exact for
  * 2^-14 <= |v| <= 65504 (smaller |v| round to fp16 subnormals, larger ones become infinite);
  * the state write uses split-bf16 products (about fp32 accuracy) and keeps S in fp32.
+ * With io_dtype ARL2_F32 the fp32 q, k, v and maps are rounded to bf16 (nearest even) on the
+ * device first, into copies the layer owns; the result is the bf16 path's on those values.
+ *
+ * Graph capture: every call's device addresses are fixed (S is one buffer that the clean pass
+ * updates in place), so calls captured into a HIP graph replay the protocol frame after frame.
+ * The frame index is host state: it counts calls, not replays of captured calls.
  *
  * Streams: every call enqueues its work on `stream` (a hipStream_t; NULL = the null
  * stream) and returns without waiting.  If a call uses a different stream from the
@@ -86,7 +94,8 @@ typedef struct {
   int32_t tokens_per_frame; /* T, 1 <= T <= ARL2_MAX_TOKENS (a chunk of frames counts as one frame);
                                (T + 256) * H * d * 2 bytes must stay below 2 GiB, and
                                ceil(T / 128) * B * H below 2^24 (ARL2_E_UNSUPPORTED) */
-  int32_t io_dtype;         /* dtype of q, k, v and phi: ARL2_BF16 (the only one supported) */
+  int32_t io_dtype;         /* dtype of q, k, v and phi: ARL2_BF16, or ARL2_F32 (rounded to bf16,
+                               nearest even, on the device; the gated call's x stays bf16) */
   int32_t out_dtype;        /* ARL2_F32 (recommended) or ARL2_BF16 (round to nearest even) */
   float softmax_scale;      /* 0 selects 1/sqrt(d) */
   float knorm_eps;          /* 0 selects 1e-6 */
@@ -105,29 +114,35 @@ enum { ARL2_ACCESS_FRAME = 0, ARL2_ACCESS_TOKEN = 1 };
 
 #define ARL2_MAX_TOKENS (1 << 20)
 
-/* Create a layer on the current HIP device: allocates all device memory the layer will
- * ever use (S twice, derived forms of S, per-chunk partial sums of the write, the maps'
- * working layouts), copies phi_q, phi_k, phi_v (device pointers, bf16 [H][d][d]) into it
- * with work enqueued on `stream`, and sets S_0 = 0 and the frame index to 0.  No call
- * after create allocates.  On failure *out_layer is set to NULL. */
+/* Create a layer on the current HIP device (section 2.1: per-head maps phi_q, phi_k, phi_v and
+ * a d x d state per stream and head; S_0 = 0): allocates all device memory the layer will ever
+ * use (S, derived forms of S, per-chunk partial sums of the write, the maps' working layouts,
+ * and with io_dtype ARL2_F32 bf16 copies of a frame's q, k, v), copies phi_q, phi_k, phi_v
+ * (device pointers, [H][d][d] of io_dtype) into it with work enqueued on `stream`, and sets
+ * S_0 = 0 and the frame index to 0.  No call after create allocates.  On failure *out_layer is
+ * set to NULL. */
 arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const void* phi_k,
                               const void* phi_v, void* stream, arl2_layer** out_layer);
 
-/* One denoising pass of the current frame: out = softmax branch + inter-frame read of
- * S_{N-1}.  Reads S, never writes it; the frame index does not change. */
+/* One denoising pass of the current frame (section 2.1: the intra-frame softmax branch plus the
+ * inter-frame read Q' S_{N-1}; section 2.2: frame-level access, and no state write during
+ * denoising): out = softmax branch + inter-frame read of S_{N-1}.  q, k, v [B][T][H][d] of
+ * io_dtype, out [B][T][H][d] of out_dtype.  Reads S, never writes it; the frame index does not
+ * change. */
 arl2_status arl2_denoise_step(arl2_layer* layer, const void* q, const void* k, const void* v,
                               void* out, void* stream);
 
-/* The clean pass of the current frame.  If `out` is not NULL it first computes the pass's
- * output exactly as arl2_denoise_step does (with S_{N-1}; `q` may be NULL when `out` is
- * NULL).  It then writes S_N from k, v, beta [B][T][H] and alpha [B][H] and advances the
- * frame index by one. */
+/* The clean pass of the current frame (section 2.2: the state is written once per frame, after
+ * the final clean pass; section 2.1: the gated update S_N = alpha S_{N-1} + K'^T diag(beta)
+ * (V' - K' S_{N-1})).  If `out` is not NULL it first computes the pass's output exactly as
+ * arl2_denoise_step does (with S_{N-1}; `q` may be NULL when `out` is NULL).  It then writes
+ * S_N from k, v, beta [B][T][H] and alpha [B][H] and advances the frame index by one. */
 arl2_status arl2_commit_frame(arl2_layer* layer, const void* q, const void* k, const void* v,
                               const float* beta, const float* alpha, void* out, void* stream);
 
 /* The clean pass with alpha and beta from the layer's gate projections (section 2.1: the
  * forget gate alpha and the learning rate beta are learned projections of the tokens; section
- * 3: head-wise gates), computed on the device from the frame's hidden states x, bf16
+ * 4, ablations: head-wise gates), computed on the device from the frame's hidden states x, bf16
  * [B][T][H d] (the input of the QKV projection), and the caller's gate weights w_gates, bf16
  * [2H][H d] (row h: beta of head h; row H + h: alpha of head h), and biases b_gates, fp32 [2H]:
  *   beta[b][t][h] = beta_scale * sigmoid(x[b][t] . w_gates[h] + b_gates[h])

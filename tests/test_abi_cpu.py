@@ -81,7 +81,7 @@ FAKE = 0x10000
     (dict(tokens_per_frame=A.ARL2_MAX_TOKENS + 1), A.ARL2_E_INVALID_ARG),
     (dict(head_dim=32), A.ARL2_E_UNSUPPORTED),
     (dict(head_dim=96), A.ARL2_E_UNSUPPORTED),
-    (dict(io_dtype=A.ARL2_F32), A.ARL2_E_UNSUPPORTED),
+    (dict(io_dtype=7), A.ARL2_E_INVALID_ARG),
     (dict(out_dtype=7), A.ARL2_E_INVALID_ARG),
     (dict(softmax_scale=-1.0), A.ARL2_E_INVALID_ARG),
     (dict(softmax_scale=float("nan")), A.ARL2_E_INVALID_ARG),
@@ -113,9 +113,12 @@ def test_create_rejects_bad_pointers(lib):
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path; a GPU is present")
-def test_create_without_device_fails_cleanly(lib):
+@pytest.mark.parametrize("io_dtype", [A.ARL2_BF16, A.ARL2_F32])
+def test_create_without_device_fails_cleanly(lib, io_dtype):
+    """Both input dtypes pass every argument check and stop at the device query."""
     h = ctypes.c_void_p()
-    assert lib.arl2_layer_create(ctypes.byref(_cfg()), FAKE, FAKE, FAKE, None, ctypes.byref(h)) == A.ARL2_E_NO_DEVICE
+    cfg = _cfg(io_dtype=io_dtype)
+    assert lib.arl2_layer_create(ctypes.byref(cfg), FAKE, FAKE, FAKE, None, ctypes.byref(h)) == A.ARL2_E_NO_DEVICE
     assert not h.value
 
 
