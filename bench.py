@@ -6,9 +6,11 @@ Inputs are synthetic (seeded, the shapes and distributions of the workload), pre
 HBM as a ring of 8 unique frames that the timed steps cycle through, so no host work or
 PCIe transfer is inside the timed region and the state keeps evolving.
 
-The value is the rate of frames enqueued launch by launch (eager) after W untimed frames
-(the GPU reaches its steady clock after a few hundred); --graph reports the rate of the same
-frames replayed from captured HIP graphs instead (both are in the breakdown).
+The value is the rate of frames enqueued launch by launch (eager) after W untimed frames;
+before those, frames run untimed for --settle seconds (default 1 s), so that the GPU's clocks
+have ramped up from idle whatever W is (a fresh GPU runs its first few hundred frames about 12 %
+slower).  --graph reports the rate of the same frames replayed from captured HIP graphs instead
+(both are in the breakdown).
 
 Prints one JSON line.  Also reports, for the dominant kernel (the fused per-pass kernel),
 its average duration measured with HIP events around 40 back-to-back pass launches on the
@@ -155,7 +157,7 @@ def capture_frames(layer, ring, w, out, stream, torch):
     """One HIP graph per ring slot, each holding one whole frame (5 pass launches + the
     state write), captured on `stream` (the stream the layer already uses, so no cross-
     stream ordering is recorded).  Replaying graph i % RING for frame i continues the same
-    stream of frames: the state buffers alternate with every frame, and RING is even."""
+    stream of frames (the layer's buffers have fixed addresses)."""
     graphs = []
     for i in range(RING):
         g = torch.cuda.CUDAGraph()
@@ -164,6 +166,17 @@ def capture_frames(layer, ring, w, out, stream, torch):
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
+
+
+def settle_clocks(layer, ring, w, out, stream, torch, seconds):
+    """Run untimed frames for about `seconds` of wall time (batches of 50, each synchronised), so
+    that the GPU leaves its idle clocks before anything is measured.  Returns the frame count."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run_frames(layer, ring, w, 50, out, stream, first=n)
+        torch.cuda.synchronize()
+        n += 50
+    return n
 
 
 def time_region(stream, torch, enqueue):
@@ -424,6 +437,7 @@ def bench(args):
         layer = make_layer(w, torch, access=args.access)
         ring = stage_ring(w, torch, gated=args.gated)
         out = layer.new_output()
+        settle_frames = settle_clocks(layer, ring, w, out, stream, torch, args.settle)
         run_frames(layer, ring, w, args.warmup, out, stream)
         torch.cuda.synchronize()
 
@@ -460,6 +474,8 @@ def bench(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"seconds": args.settle, "frames": settle_frames,
+                         "note": "untimed frames before the warm-up, until the GPU clocks have ramped up"},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -893,6 +909,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=400,
                     help="untimed frames first (the GPU reaches its steady clock after a few hundred)")
     ap.add_argument("--workload", default="dit480p", choices=["dit480p", "long_stream", "chunked"])
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed frames before the warm-up frames (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="report the HIP-graph replay rate as the value")
     ap.add_argument("--access", default="frame", choices=["frame", "token"],
