@@ -38,6 +38,8 @@ SIGNATURES = {
     "arl2_denoise_step_seq": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "arl2_commit_frame_seq": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p]),
+    "arl2_commit_frame_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "arl2_destroy": (c_int, [c_void_p]),
     "arl2_state_read": (c_int, [c_void_p, c_void_p, c_void_p]),
     "arl2_state_write": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
@@ -313,6 +315,37 @@ class Arl2Layer:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def commit_frame_noalloc(phi_q, phi_k, phi_v, state, q, k, v, beta, alpha, out=None, softmax_scale: float = 0.0,
+                         knorm_eps: float = 0.0, stream=None):
+    """arl2_commit_frame_noalloc (include/arl2.h): the clean pass of one frame on the caller's
+    state (fp32 [B, H, d, d], updated in place), with no layer object and no device allocation by
+    the library.  phi_* bf16 [H, d, d]; q, k, v bf16 [B, T, H, d]; beta fp32 [B, T, H]; alpha fp32
+    [B, H]; out fp32 or bf16 [B, T, H, d], or None (state write only)."""
+    lib = load_library()
+    heads, d, _ = phi_q.shape
+    B, T = int(k.shape[0]), int(k.shape[1])
+    frame = (B, T, heads, d)
+    phis = [_dev_tensor(t, n, torch.bfloat16, (heads, d, d)) for t, n in ((phi_q, "phi_q"), (phi_k, "phi_k"),
+                                                                          (phi_v, "phi_v"))]
+    ps = _dev_tensor(state, "state", torch.float32, (B, heads, d, d))
+    pk = _dev_tensor(k, "k", torch.bfloat16, frame)
+    pv = _dev_tensor(v, "v", torch.bfloat16, frame)
+    pb = _dev_tensor(beta, "beta", torch.float32, (B, T, heads))
+    pa = _dev_tensor(alpha, "alpha", torch.float32, (B, heads))
+    pq = po = None
+    out_dtype = ARL2_F32
+    if out is not None:
+        if out.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("out must be float32 or bfloat16")
+        out_dtype = ARL2_F32 if out.dtype == torch.float32 else ARL2_BF16
+        po = _dev_tensor(out, "out", out.dtype, frame)
+        pq = _dev_tensor(q, "q", torch.bfloat16, frame)
+    cfg = Arl2Config(B, heads, d, T, ARL2_BF16, out_dtype, float(softmax_scale), float(knorm_eps), ARL2_ACCESS_FRAME)
+    _check(lib.arl2_commit_frame_noalloc(byref(cfg), *phis, ps, pq, pk, pv, pb, pa, po, _stream_handle(stream)),
+           "arl2_commit_frame_noalloc")
+    return out
 
 
 class SoftmaxLayer:

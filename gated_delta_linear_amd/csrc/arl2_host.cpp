@@ -45,6 +45,54 @@ bool debug_sync() {
 
 const char* last_error() { return g_last_error.c_str(); }
 
+arl2_status check_config(const arl2_config& c) {
+  if (c.batch < 1 || c.heads < 1 || c.batch > 65535 || c.heads > 65535)
+    return fail(ARL2_E_INVALID_ARG, "batch and heads must be in [1, 65535]");
+  if (c.tokens_per_frame < 1 || c.tokens_per_frame > ARL2_MAX_TOKENS)
+    return fail(ARL2_E_INVALID_ARG, "tokens_per_frame must be in [1, %d]", ARL2_MAX_TOKENS);
+  if (c.head_dim != 16 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(ARL2_E_UNSUPPORTED, "head_dim %d not supported (16, 64, 128)", c.head_dim);
+  if (c.io_dtype != ARL2_BF16 && c.io_dtype != ARL2_F32) return fail(ARL2_E_INVALID_ARG, "bad io_dtype");
+  if (c.access != ARL2_ACCESS_FRAME && c.access != ARL2_ACCESS_TOKEN) return fail(ARL2_E_INVALID_ARG, "bad access");
+  if (c.access == ARL2_ACCESS_TOKEN && c.head_dim == 16)
+    return fail(ARL2_E_UNSUPPORTED, "token-level access supports head_dim 64 and 128");
+  // token-level access addresses one stream's fp32 inter-frame reads [T][H][d] with 32-bit byte offsets
+  if (c.access == ARL2_ACCESS_TOKEN && ((int64_t)c.tokens_per_frame + 64) * c.heads * c.head_dim * 4 >= (int64_t(1) << 31))
+    return fail(ARL2_E_UNSUPPORTED, "token-level access: one stream's frame (T x H x d fp32) must stay below 2 GiB");
+  if (c.out_dtype != ARL2_F32 && c.out_dtype != ARL2_BF16) return fail(ARL2_E_INVALID_ARG, "bad out_dtype");
+  if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
+    return fail(ARL2_E_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!(c.knorm_eps >= 0.f) || !std::isfinite(c.knorm_eps))
+    return fail(ARL2_E_INVALID_ARG, "knorm_eps must be finite and >= 0");
+  // the kernels address one stream's frame slice [T][H][d] with 32-bit byte offsets
+  const int64_t slice_bytes = ((int64_t)c.tokens_per_frame + 256) * c.heads * c.head_dim * 2;
+  if (slice_bytes >= (int64_t(1) << 31))
+    return fail(ARL2_E_UNSUPPORTED, "one stream's frame (T x H x d bf16) must stay below 2 GiB");
+  // the clean pass's launch runs ceil(T / 128) x B x H work-groups for the pass and as many for
+  // the state write (each rounded up to 8) in one grid dimension
+  const int64_t pass_wgs = 2 * ((((int64_t)c.tokens_per_frame + 127) / 128) * c.batch * c.heads + 7);
+  if (pass_wgs > (int64_t(1) << 24))
+    return fail(ARL2_E_UNSUPPORTED, "B x H x T too large for one launch (%lld work-groups)", (long long)pass_wgs);
+  return ARL2_OK;
+}
+
+arl2_status current_gfx950(int* dev) {
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(ARL2_E_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+  }
+  if ((e = hipGetDevice(dev)) != hipSuccess) return fail(ARL2_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, *dev)) != hipSuccess)
+    return fail(ARL2_E_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(ARL2_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", *dev, prop.gcnArchName);
+  return ARL2_OK;
+}
+
+
 }  // namespace arl2host
 
 using arl2host::aligned16;
@@ -249,50 +297,14 @@ arl2_status arl2_layer_create(const arl2_config* cfg, const void* phi_q, const v
   *out_layer = nullptr;
   if (!cfg) return fail(ARL2_E_INVALID_ARG, "config is NULL");
   const arl2_config c = *cfg;
-  if (c.batch < 1 || c.heads < 1 || c.batch > 65535 || c.heads > 65535)
-    return fail(ARL2_E_INVALID_ARG, "batch and heads must be in [1, 65535]");
-  if (c.tokens_per_frame < 1 || c.tokens_per_frame > ARL2_MAX_TOKENS)
-    return fail(ARL2_E_INVALID_ARG, "tokens_per_frame must be in [1, %d]", ARL2_MAX_TOKENS);
-  if (c.head_dim != 16 && c.head_dim != 64 && c.head_dim != 128)
-    return fail(ARL2_E_UNSUPPORTED, "head_dim %d not supported (16, 64, 128)", c.head_dim);
-  if (c.io_dtype != ARL2_BF16 && c.io_dtype != ARL2_F32) return fail(ARL2_E_INVALID_ARG, "bad io_dtype");
-  if (c.access != ARL2_ACCESS_FRAME && c.access != ARL2_ACCESS_TOKEN) return fail(ARL2_E_INVALID_ARG, "bad access");
-  if (c.access == ARL2_ACCESS_TOKEN && c.head_dim == 16)
-    return fail(ARL2_E_UNSUPPORTED, "token-level access supports head_dim 64 and 128");
-  // token-level access addresses one stream's fp32 inter-frame reads [T][H][d] with 32-bit byte offsets
-  if (c.access == ARL2_ACCESS_TOKEN && ((int64_t)c.tokens_per_frame + 64) * c.heads * c.head_dim * 4 >= (int64_t(1) << 31))
-    return fail(ARL2_E_UNSUPPORTED, "token-level access: one stream's frame (T x H x d fp32) must stay below 2 GiB");
-  if (c.out_dtype != ARL2_F32 && c.out_dtype != ARL2_BF16) return fail(ARL2_E_INVALID_ARG, "bad out_dtype");
-  if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
-    return fail(ARL2_E_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (!(c.knorm_eps >= 0.f) || !std::isfinite(c.knorm_eps))
-    return fail(ARL2_E_INVALID_ARG, "knorm_eps must be finite and >= 0");
-  // the kernels address one stream's frame slice [T][H][d] with 32-bit byte offsets
-  const int64_t slice_bytes = ((int64_t)c.tokens_per_frame + 256) * c.heads * c.head_dim * 2;
-  if (slice_bytes >= (int64_t(1) << 31))
-    return fail(ARL2_E_UNSUPPORTED, "one stream's frame (T x H x d bf16) must stay below 2 GiB");
-  // the clean pass's launch runs ceil(T / 128) x B x H work-groups for the pass and as many for
-  // the state write (each rounded up to 8) in one grid dimension
-  const int64_t pass_wgs = 2 * ((((int64_t)c.tokens_per_frame + 127) / 128) * c.batch * c.heads + 7);
-  if (pass_wgs > (int64_t(1) << 24))
-    return fail(ARL2_E_UNSUPPORTED, "B x H x T too large for one launch (%lld work-groups)", (long long)pass_wgs);
   arl2_status st;
+  if ((st = arl2host::check_config(c))) return st;
   if ((st = check_ptr(phi_q, "phi_q")) || (st = check_ptr(phi_k, "phi_k")) || (st = check_ptr(phi_v, "phi_v")))
     return st;
 
-  int ndev = 0;
-  hipError_t e = hipGetDeviceCount(&ndev);
-  if (e != hipSuccess || ndev < 1) {
-    (void)hipGetLastError();
-    return fail(ARL2_E_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
-  }
   int dev = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return fail(ARL2_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  hipDeviceProp_t prop;
-  if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
-    return fail(ARL2_E_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(ARL2_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  if ((st = arl2host::current_gfx950(&dev))) return st;
+  hipError_t e;
 
   arl2_layer* L = new arl2_layer();
   L->cfg = c;

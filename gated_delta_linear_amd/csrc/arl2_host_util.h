@@ -12,5 +12,9 @@ const char* last_error();
 bool aligned16(const void* p);
 // ARL2_DEBUG_SYNC=1: synchronise after every launch so that a kernel fault names its call.
 bool debug_sync();
+// Every rule on a layer configuration that does not need the device (sizes, dtypes, access).
+arl2_status check_config(const arl2_config& c);
+// The current HIP device, if there is one and it is a gfx950 (else NO_DEVICE / UNSUPPORTED / HIP).
+arl2_status current_gfx950(int* dev);
 
 }  // namespace arl2host

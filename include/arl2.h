@@ -162,6 +162,25 @@ arl2_status arl2_denoise_step_seq(arl2_layer* layer, const void* q, const void* 
 arl2_status arl2_commit_frame_seq(arl2_layer* layer, const void* q, const void* k, const void* v,
                                   const float* beta, const float* alpha, void* out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the clean pass of one frame without a layer object.
+ * It computes exactly what arl2_commit_frame does on a layer created with cfg, phi_q, phi_k,
+ * phi_v whose state equals `state`: `out` (if not NULL) = the pass's output with S_{N-1} =
+ * state, then state <- S_N, in place.  state: fp32 [B][H][d][d] device memory owned by the
+ * caller (S_0 = 0 is the caller's zero buffer); the other arguments as arl2_layer_create and
+ * arl2_commit_frame (bf16 inputs, frame-level access only: ARL2_E_UNSUPPORTED otherwise).
+ * It allocates nothing: the maps' working layouts, the derived forms of S and the state
+ * write's per-chunk partial sums live in a device array of ARL2_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; a frame needing more is
+ * refused with ARL2_E_UNSUPPORTED (about 13 MB for 12 heads x 1560 tokens x d = 128).  Every
+ * call on a GPU reuses that GPU's array: calls that overlap on one GPU (on different streams,
+ * or from different threads) race and give wrong results; calls on one stream are ordered. */
+#define ARL2_NOALLOC_SCRATCH_BYTES (32u << 20)
+arl2_status arl2_commit_frame_noalloc(const arl2_config* cfg, const void* phi_q, const void* phi_k,
+                                      const void* phi_v, float* state, const void* q, const void* k,
+                                      const void* v, const float* beta, const float* alpha, void* out,
+                                      void* stream);
+
 /* Synchronise the last stream the layer used and free everything.  NULL is accepted. */
 arl2_status arl2_destroy(arl2_layer* layer);
 

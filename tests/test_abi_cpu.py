@@ -194,3 +194,34 @@ def test_bwd_create_rejects_bad_config(lib, kw, status):
     assert lib.arl2_bwd_create(ctypes.byref(A.Arl2Config(**c)), None, None, None, None, ctypes.byref(h)) == status
     assert not h.value
 
+
+
+# --- the allocation-free clean pass (arl2_commit_frame_noalloc) ---------------------------------
+
+def _noalloc(lib, cfg, ptrs=None):
+    p = [FAKE] * 10 if ptrs is None else ptrs
+    return lib.arl2_commit_frame_noalloc(ctypes.byref(cfg) if cfg is not None else None, *p, None)
+
+
+def test_noalloc_rejects_bad_arguments_before_the_device(lib):
+    assert _noalloc(lib, None) == A.ARL2_E_INVALID_ARG
+    assert _noalloc(lib, _cfg(batch=0)) == A.ARL2_E_INVALID_ARG
+    assert _noalloc(lib, _cfg(io_dtype=A.ARL2_F32)) == A.ARL2_E_UNSUPPORTED
+    assert _noalloc(lib, _cfg(access=A.ARL2_ACCESS_TOKEN)) == A.ARL2_E_UNSUPPORTED
+    for i in range(8):  # phi_q, phi_k, phi_v, state, (q), k, v, beta, alpha
+        ptrs = [FAKE] * 10
+        ptrs[i if i < 4 else i + 1] = None
+        assert _noalloc(lib, _cfg(), ptrs) == A.ARL2_E_INVALID_ARG, i
+    ptrs = [FAKE] * 10
+    ptrs[4] = None  # q missing while an output is requested
+    assert _noalloc(lib, _cfg(), ptrs) == A.ARL2_E_INVALID_ARG
+    ptrs = [FAKE] * 10
+    ptrs[5] = FAKE + 4
+    assert _noalloc(lib, _cfg(), ptrs) == A.ARL2_E_INVALID_ARG
+    assert b"aligned" in lib.arl2_last_error()
+
+
+def test_noalloc_refuses_frames_beyond_its_array(lib):
+    # 4 streams x 12 heads x 4680 tokens (d = 128): about 120 MB of per-chunk partial sums
+    assert _noalloc(lib, _cfg(batch=4, heads=12, tokens_per_frame=4680)) == A.ARL2_E_UNSUPPORTED
+    assert b"scratch" in lib.arl2_last_error()
