@@ -13,7 +13,9 @@ from ctypes import POINTER, Structure, byref, c_char_p, c_float, c_int, c_int32,
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
+# ARL2_LIBRARY names another build of the same library (the AddressSanitizer build of the host
+# code, for the CPU interface tests); by default the in-tree libarl2.so
+LIB_PATH = os.environ.get("ARL2_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
 
 ARL2_OK = 0
 ARL2_E_INVALID_ARG = 1

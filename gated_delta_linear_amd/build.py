@@ -1,6 +1,6 @@
 """Build libarl2.so (HIP kernels + C interface) for gfx950 with hipcc, in the package directory.
 
-Usage: python -m gated_delta_linear_amd.build [-v]
+Usage: python -m gated_delta_linear_amd.build [-v] [--asan]
 """
 from __future__ import annotations
 
@@ -42,14 +42,29 @@ def _run(cmd: list[str]) -> str:
     return msgs
 
 
-def build_library(verbose: bool = False, jobs: int | None = None) -> str:
+ASAN_LIB_PATH = os.path.join(PKG_DIR, "_build", "asan", "libarl2.so")
+# host code only: the sanitizer instruments the CPU side of every source (the interface's
+# argument checks, the layer objects), never device code
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime a process must preload to load the sanitized library."""
+    import glob
+
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else None
+
+
+def build_library(verbose: bool = False, jobs: int | None = None, sanitize: bool = False) -> str:
     """Compile every HIP source into libarl2.so; always recompiles (one object per source, in
-    parallel, under _build/, then one link)."""
+    parallel, under _build/, then one link).  sanitize=True builds the AddressSanitizer variant
+    of the host code into _build/asan/libarl2.so instead (for the CPU interface tests)."""
     from concurrent.futures import ThreadPoolExecutor
 
-    obj_dir = os.path.join(PKG_DIR, "_build")
+    obj_dir = os.path.join(PKG_DIR, "_build", "asan") if sanitize else os.path.join(PKG_DIR, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    flags = [f for f in compile_flags() if f != "-shared"]
+    flags = [f for f in compile_flags() if f != "-shared"] + (ASAN_FLAGS if sanitize else [])
     cmds = []
     for src in SOURCES:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
@@ -61,16 +76,18 @@ def build_library(verbose: bool = False, jobs: int | None = None) -> str:
                 print(" ".join(cmd), flush=True)
                 if msgs.strip():
                     print(msgs)
-    tmp = LIB_PATH + ".tmp"
-    link = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *[o for o, _ in cmds], "-o", tmp]
+    lib_path = ASAN_LIB_PATH if sanitize else LIB_PATH
+    tmp = lib_path + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *(ASAN_FLAGS if sanitize else []),
+            *[o for o, _ in cmds], "-o", tmp]
     msgs = _run(link)
     if verbose:
         print(" ".join(link), flush=True)
         if msgs.strip():
             print(msgs)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, sanitize="--asan" in sys.argv))
