@@ -647,16 +647,20 @@ STACK_SOFTMAX = (2, 6, 10, 14, 18, 22, 26)  # the 7 of 30 layers kept as softmax
 
 def stack_bench(args):
     """The pages' 75 % hybrid stack, attention layers only: 30 attention layers of the workload's
-    shape, 23 ARL2 + 7 retained softmax layers (indices STACK_SOFTMAX), each fed by its own Q, K, V
-    projections of the previous layer's output and followed by its output projection (seeded
-    random-init bf16 weights ~ N(0, 1/(H d)), torch.matmul / hipBLASLt; no norms, MLPs or
-    residuals), against the same stack with all 30 layers softmax.  Per-frame time (4 denoising
+    shape, 23 ARL2 + 7 retained softmax layers (indices STACK_SOFTMAX), each fed by its own fused
+    Q, K, V projection of the previous layer's output and followed by its output projection (the
+    library's arl2_linear; seeded random-init bf16 weights ~ N(0, 1/(H d)), query rows x 0.5 and
+    output weights x 2; no norms, MLPs or residuals), every ARL2 layer with its own maps and gates, against the same stack with all 30
+    layers softmax.  Only library kernels run in the timed frames.  Per-frame time (4 denoising
     passes + the clean pass through all 30 layers, launches enqueued back to back; 4 frames timed
-    after warm-up) at frames 1, 21 and 231 (the softmax caches pre-filled with 0, 20 and 230 clean
-    frames), and the layers' device memory."""
+    after warm-up) at frames 1, 21 and 231: the softmax caches are pre-filled with 0, 20 and 230
+    clean frames of keys and values projected from a random frame (timing does not depend on the
+    cached values).  Also the layers' device memory, and the projections alone."""
     import torch
 
     from gated_delta_linear_amd import Arl2Layer, SoftmaxLayer
+    from gated_delta_linear_amd.arl2 import linear
+    from gated_delta_linear_amd.stack import AttentionStack
     from synth import WORKLOADS, make_gates, make_phi
 
     w = WORKLOADS[args.workload]
@@ -666,72 +670,90 @@ def stack_bench(args):
     hd = H * d
     gen = torch.Generator(device="cuda").manual_seed(w.seed + 4242)
     timed, cached = 4, (0, 20, 230)
-    max_frames = max(cached) + timed
+    max_frames = max(cached) + timed + 24
     with torch.cuda.stream(stream):
         def rnd(*shape, scale=1.0):
             return (torch.randn(*shape, device="cuda", generator=gen) * scale).to(torch.bfloat16)
-        wq, wk, wv, wo = ([rnd(hd, hd, scale=hd ** -0.5) for _ in range(STACK_LAYERS)] for _ in range(4))
+
+        def per_layer(i):  # each ARL2 layer's own maps and gates (seeded per layer)
+            lw = w.with_(seed=w.seed * 1000 + i)
+            phis = [torch.from_numpy(p).to("cuda").to(torch.bfloat16) for p in make_phi(lw)]
+            gates = [tuple(torch.from_numpy(g).to("cuda") for g in make_gates(lw, f)) for f in range(RING)]
+            return phis, gates
+
+        def qkv_weights():  # query rows x 0.5 and output weights x 2 keep the random stack's activations O(1)
+            wqkv = torch.randn(3 * hd, hd, device="cuda", generator=gen) * hd ** -0.5
+            wqkv[:hd] *= 0.5
+            return wqkv.to(torch.bfloat16)
+
+        weights = [(qkv_weights(), rnd(hd, hd, scale=2 * hd ** -0.5)) for _ in range(STACK_LAYERS)]
+        own = {i: per_layer(i) for i in range(STACK_LAYERS) if i not in STACK_SOFTMAX}
         x_in = [rnd(B * T, hd) for _ in range(w.denoise_steps + 1)]  # the stack's input per pass
-        beta, alpha = (torch.from_numpy(g).to("cuda") for g in make_gates(w, 0))
-        phis = [torch.from_numpy(p).to("cuda").to(torch.bfloat16) for p in make_phi(w)]
-        arl2 = {i: Arl2Layer(*phis, batch=B, tokens=T, out_dtype=torch.bfloat16) for i in range(STACK_LAYERS)}
-        soft = {i: SoftmaxLayer(B, H, d, T, max_frames, out_dtype=torch.bfloat16) for i in range(STACK_LAYERS)}
-        weight_bytes = 4 * STACK_LAYERS * hd * hd * 2
-        o = torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda")
+
+        def build(hybrid):
+            layers = []
+            for i, (wqkv, wo) in enumerate(weights):
+                kind = "arl2" if hybrid and i not in STACK_SOFTMAX else "softmax"
+                ly = {"kind": kind, "w_qkv_t": wqkv, "w_o_t": wo}
+                if kind == "arl2":
+                    ly["phi"] = own[i][0]
+                layers.append(ly)
+            return AttentionStack(layers, B, H, d, T, max_frames, stream=stream)
+
+        stacks = {True: build(True), False: build(False)}
+        weight_bytes = STACK_LAYERS * 4 * hd * hd * 2
+        frame_no = {True: 0, False: 0}
 
         def frame(hybrid):
+            st = stacks[hybrid]
+            f = frame_no[hybrid]
             for p in range(w.denoise_steps + 1):
-                clean = p == w.denoise_steps
-                x = x_in[p]
-                for i in range(STACK_LAYERS):
-                    q, k, v = (torch.matmul(x, wm[i]).view(B, T, H, d) for wm in (wq, wk, wv))
-                    if hybrid and i not in STACK_SOFTMAX:
-                        if clean:
-                            arl2[i].commit_frame(q, k, v, beta, alpha, out=o, stream=stream)
-                        else:
-                            arl2[i].denoise_step(q, k, v, out=o, stream=stream)
-                    elif clean:
-                        soft[i].commit_frame(q, k, v, out=o, stream=stream)
-                    else:
-                        soft[i].denoise_step(q, k, v, out=o, stream=stream)
-                    x = torch.matmul(o.view(B * T, hd), wo[i])
+                st.run_pass(x_in[p], p == w.denoise_steps, gates=lambda i: own[i][1][f % RING])
+            frame_no[hybrid] += 1
 
-        def prefill(n):
-            q = x_in[0].view(B, T, H, d)
-            for i in range(STACK_LAYERS):
-                soft[i].reset()
-                for _ in range(n):
-                    soft[i].commit_frame(None, q, q, want_output=False, stream=stream)
+        # cache pre-fill: keys and values projected from a random frame, committed n times
+        kv = [torch.empty(B, T, H, d, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+
+        def prefill(hybrid, n):
+            st = stacks[hybrid]
+            for i, att in enumerate(st.attn):
+                if isinstance(att, SoftmaxLayer):
+                    att.reset()
+                    linear(x_in[0], weights[i][0], parts=3, out=[t.view(B * T, hd) for t in kv], stream=stream)
+                    for _ in range(n):
+                        att.commit_frame(None, kv[1], kv[2], want_output=False, stream=stream)
 
         def projections_only():
+            o = stacks[True].o.view(B * T, hd)
+            y = stacks[True].x[0]
             for p in range(w.denoise_steps + 1):
-                x = x_in[p]
                 for i in range(STACK_LAYERS):
-                    for wm in (wq, wk, wv):
-                        torch.matmul(x, wm[i])
-                    x = torch.matmul(o.view(B * T, hd), wo[i])
+                    linear(x_in[p], weights[i][0], parts=3, out=[t.view(B * T, hd) for t in kv], stream=stream)
+                    linear(o, weights[i][1], out=[y], stream=stream)
 
-        prefill(0)
-        for _ in range(20):  # warm-up (the clock settles; every layer's frame count stays small)
-            frame(True)
+        for hybrid in (True, False):
+            prefill(hybrid, 0)
+            for _ in range(8):  # warm-up (the clock settles; every layer's frame count stays small)
+                frame(hybrid)
         points = []
         for n in cached:
             pt = {"frames_cached": n, "frame_index": n + 1}
             for hybrid in (True, False):
-                prefill(n)
+                prefill(hybrid, n)
                 torch.cuda.synchronize()
                 ms, _ = time_region(stream, torch, lambda: [frame(hybrid) for _ in range(timed)])
                 key = "hybrid" if hybrid else "all_softmax"
                 pt[key + "_ms_per_frame"] = ms / timed
                 n_soft = len(STACK_SOFTMAX) if hybrid else STACK_LAYERS
                 cache = 2 * (n + timed) * B * T * H * d * 2  # K and V of one softmax layer after the timed frames
-                pt[key + "_layer_bytes"] = n_soft * cache + (STACK_LAYERS - n_soft) * arl2[0].device_bytes
+                arl2_bytes = next((a.device_bytes for a in stacks[True].attn if isinstance(a, Arl2Layer)), 0)
+                pt[key + "_layer_bytes"] = n_soft * cache + (STACK_LAYERS - n_soft) * arl2_bytes
             pt["speedup"] = pt["all_softmax_ms_per_frame"] / pt["hybrid_ms_per_frame"]
             pt["memory_reduction"] = 1 - pt["hybrid_layer_bytes"] / pt["all_softmax_layer_bytes"]
             points.append(pt)
         proj_ms, _ = time_region(stream, torch, lambda: [projections_only() for _ in range(timed)])
-        for layer in list(arl2.values()) + list(soft.values()):
-            layer.close()
+        for st in stacks.values():
+            st.close()
     # per-frame time grows linearly with the cache; the average over a stream of F = 231 frames
     F = 231
     avg = {}
@@ -742,8 +764,9 @@ def stack_bench(args):
         avg[key] = float(icpt + slope * (F - 1) / 2)
     res = {"metric": "per-frame time and memory of a 30-layer attention stack: 23 ARL2 + 7 softmax layers vs all softmax",
            "workload": f"{w.name}: {B} x {H} heads x {T} tokens/frame, d={d}, {w.denoise_steps} denoising passes + clean "
-                       f"pass per frame; softmax layers {list(STACK_SOFTMAX)}; Q/K/V/output projections of random-init "
-                       f"bf16 weights (torch.matmul); no norms, MLPs or residuals",
+                       f"pass per frame; softmax layers {list(STACK_SOFTMAX)}; fused Q/K/V and output projections "
+                       f"(arl2_linear) of random-init bf16 weights; own maps and gates per ARL2 layer; no norms, MLPs "
+                       f"or residuals",
            "points": points, "projections_ms_per_frame": proj_ms / timed, "weight_bytes": weight_bytes,
            "stream_average_ms_per_frame": avg, "stream_frames": F,
            "stream_average_speedup": avg["all_softmax"] / avg["hybrid"]}

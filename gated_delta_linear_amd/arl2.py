@@ -62,6 +62,12 @@ SOFTMAX_SIGNATURES = {
     "arl2_softmax_device_bytes": (c_size_t, [c_void_p]),
 }
 
+# every function declared in include/arl2_linear.h (the projections around the attention layers)
+LINEAR_SIGNATURES = {
+    "arl2_linear": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_void_p), c_int32,
+                            c_void_p]),
+}
+
 # every function declared in include/arl2_bwd.h (the layer's backward)
 BWD_SIGNATURES = {
     "arl2_bwd_create": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_void_p)]),
@@ -120,7 +126,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_linear_amd.build` "
                            "(the ARL2 layer has no fallback implementation)")
     lib = ctypes.CDLL(path)
-    for name, (res, args) in {**SIGNATURES, **SOFTMAX_SIGNATURES, **BWD_SIGNATURES}.items():
+    for name, (res, args) in {**SIGNATURES, **SOFTMAX_SIGNATURES, **BWD_SIGNATURES, **LINEAR_SIGNATURES}.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
@@ -317,6 +323,31 @@ class Arl2Layer:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def linear(x: torch.Tensor, w_t: torch.Tensor, parts: int = 1, out_dtype: torch.dtype = torch.bfloat16, out=None,
+           stream=None):
+    """arl2_linear (include/arl2_linear.h): y = x W with x bf16 [M, K] and W given transposed,
+    w_t bf16 [N, K]; returns a list of `parts` outputs [M, N / parts] of out_dtype (the N features
+    dealt in order), written into `out` (a list of tensors) when given."""
+    lib = load_library()
+    if x.dim() != 2 or w_t.dim() != 2 or x.shape[1] != w_t.shape[1]:
+        raise ValueError("x must be [M, K] and w_t [N, K]")
+    M, K = int(x.shape[0]), int(x.shape[1])
+    N = int(w_t.shape[0])
+    if out_dtype not in (torch.float32, torch.bfloat16) or parts < 1 or N % parts:
+        raise ValueError("out_dtype must be float32 or bfloat16 and parts must divide N")
+    px = _dev_tensor(x, "x", torch.bfloat16, (M, K))
+    pw = _dev_tensor(w_t, "w_t", torch.bfloat16, (N, K))
+    if out is None:
+        out = [torch.empty((M, N // parts), dtype=out_dtype, device=x.device) for _ in range(parts)]
+    if len(out) != parts:
+        raise ValueError("out must hold `parts` tensors")
+    ptrs = (c_void_p * parts)(*[_dev_tensor(o.view(M, N // parts) if o.is_contiguous() else o, f"out[{i}]", out_dtype,
+                                            (M, N // parts)) for i, o in enumerate(out)])
+    _check(lib.arl2_linear(px, pw, M, N, K, parts, ptrs, ARL2_F32 if out_dtype == torch.float32 else ARL2_BF16,
+                           _stream_handle(stream)), "arl2_linear")
+    return out
 
 
 def commit_frame_noalloc(phi_q, phi_k, phi_v, state, q, k, v, beta, alpha, out=None, softmax_scale: float = 0.0,

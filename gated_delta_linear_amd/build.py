@@ -12,8 +12,8 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libarl2.so")
-SOURCES = ["arl2_fwd.hip", "arl2_commit.hip", "arl2_kvcache.hip", "arl2_gates.hip", "arl2_seq.hip", "arl2_bwd.hip", "arl2_convert.hip", "arl2_noalloc.hip",
-           "arl2_host.cpp", "arl2_softmax_host.cpp", "arl2_bwd_host.cpp"]
+SOURCES = ["arl2_fwd.hip", "arl2_commit.hip", "arl2_kvcache.hip", "arl2_gates.hip", "arl2_seq.hip", "arl2_bwd.hip", "arl2_convert.hip", "arl2_noalloc.hip", "arl2_linear.hip",
+           "arl2_host.cpp", "arl2_softmax_host.cpp", "arl2_bwd_host.cpp", "arl2_linear_host.cpp"]
 ARCH = "gfx950"
 
 

@@ -152,6 +152,24 @@ struct CvtJobs {
 };
 hipError_t launch_cvt_bf16(const CvtJobs& jobs, int n_jobs, int64_t n, hipStream_t stream);
 
+// y = x W with W given as W^T [N][K] (bf16), x [M][K] bf16, y [M][N] fp32 or bf16, the N output
+// features dealt to `parts` row-major outputs of N / parts features each (K % 64 == 0, N % 8 == 0,
+// (N / parts) % 4 == 0; 16-byte aligned pointers).
+constexpr int kLinearMaxParts = 4;
+struct LinearOut {
+  void* ptr[kLinearMaxParts];
+  int parts;
+};
+struct LinearArgs {
+  const void* x;
+  const void* wt;
+  LinearOut y;
+  int M, N, K;
+  bool out_bf16;
+};
+int linear_tile_n(int M, int N);  // feature width of a work-group's tile (64 or 128)
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
 // --- backward (arl2_bwd.hip) -------------------------------------------------------------------
 // Per (stream, head) d x d matrices in 16x16x32 B-fragment order ([d/32][d/16][64][8] bf16:
 // lane l of fragment (s, nb) holds M[32 s + 8 (l / 16) + j][16 nb + l % 16]), split into hi + lo

@@ -13,6 +13,7 @@ from .arl2_oracle import (  # noqa: F401
     unit_rows,
 )
 from .softmax_oracle import SoftmaxOracle, cached_attention  # noqa: F401,E402
+from .stack_oracle import StackOracle, linear, linear_parts, to_bf16  # noqa: F401,E402
 from .seq_oracle import Arl2SeqOracle, sequential_frame, sequential_frame_chunked  # noqa: F401,E402
 from .bwd_oracle import (  # noqa: F401,E402
     layer_backward,

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2.h")
 SOFTMAX_HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2_softmax.h")
 BWD_HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2_bwd.h")
+LINEAR_HEADER = os.path.join(os.path.dirname(HERE), "include", "arl2_linear.h")
 
 
 @pytest.fixture(scope="module")
@@ -34,10 +35,12 @@ def test_header_and_binding_agree():
     assert _declared_functions() == set(A.SIGNATURES)
     assert _declared_functions(SOFTMAX_HEADER) == set(A.SOFTMAX_SIGNATURES)
     assert _declared_functions(BWD_HEADER) == set(A.BWD_SIGNATURES)
+    assert _declared_functions(LINEAR_HEADER) == set(A.LINEAR_SIGNATURES)
 
 
 def test_every_declared_symbol_is_exported(lib):
-    for name in _declared_functions() | _declared_functions(SOFTMAX_HEADER) | _declared_functions(BWD_HEADER):
+    for name in (_declared_functions() | _declared_functions(SOFTMAX_HEADER) | _declared_functions(BWD_HEADER)
+                 | _declared_functions(LINEAR_HEADER)):
         assert hasattr(lib, name), name
 
 
@@ -225,3 +228,30 @@ def test_noalloc_refuses_frames_beyond_its_array(lib):
     # 4 streams x 12 heads x 4680 tokens (d = 128): about 120 MB of per-chunk partial sums
     assert _noalloc(lib, _cfg(batch=4, heads=12, tokens_per_frame=4680)) == A.ARL2_E_UNSUPPORTED
     assert b"scratch" in lib.arl2_last_error()
+
+
+# --- the projections (include/arl2_linear.h) ------------------------------------------------------
+
+def _lin(lib, m=256, n=384, k=128, parts=1, y_dtype=A.ARL2_BF16, x=FAKE, w=FAKE, ys=None):
+    ys = [FAKE] * parts if ys is None else ys
+    arr = (ctypes.c_void_p * max(1, len(ys)))(*ys)
+    return lib.arl2_linear(x, w, m, n, k, parts, arr, y_dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=-1), A.ARL2_E_INVALID_ARG),
+    (dict(k=96), A.ARL2_E_UNSUPPORTED),          # k not a multiple of 64
+    (dict(k=(1 << 20) + 64), A.ARL2_E_UNSUPPORTED),
+    (dict(n=100), A.ARL2_E_UNSUPPORTED),         # n not a multiple of 8
+    (dict(parts=0), A.ARL2_E_INVALID_ARG),
+    (dict(parts=5), A.ARL2_E_INVALID_ARG),
+    (dict(n=24, parts=4), A.ARL2_E_INVALID_ARG),  # n / parts = 6, not a multiple of 4
+    (dict(y_dtype=9), A.ARL2_E_INVALID_ARG),
+    (dict(x=None), A.ARL2_E_INVALID_ARG),
+    (dict(w=FAKE + 8), A.ARL2_E_INVALID_ARG),
+    (dict(parts=2, ys=[FAKE, None]), A.ARL2_E_INVALID_ARG),
+    (dict(parts=2, ys=[FAKE, FAKE + 4]), A.ARL2_E_INVALID_ARG),
+])
+def test_linear_rejects_bad_arguments(lib, kw, status):
+    assert _lin(lib, **kw) == status
+    assert lib.arl2_last_error()
