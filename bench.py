@@ -13,8 +13,9 @@ slower).  --graph reports the rate of the same frames replayed from captured HIP
 (both are in the breakdown).
 
 Prints one JSON line.  Also reports, for the dominant kernel (the fused per-pass kernel),
-its average duration measured with HIP events around 40 back-to-back pass launches on the
-layer's stream, against the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
+its average duration inside the workload's frames (an event pair around the four back-to-back
+denoising passes of each of 60 frames on the layer's stream, inputs from HBM as in the timed
+frames) against the bf16 MFMA peak, and the CPU oracle's rate on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--graph] [--workload dit480p|chunked|long_stream]
   python bench.py --series            per-frame GPU time over the whole stream
@@ -23,6 +24,7 @@ layer's stream, against the bf16 MFMA peak, and the CPU oracle's rate on a bound
   python bench.py --stack             a 30-layer attention stack (23 ARL2 + 7 softmax) vs all softmax
   python bench.py --pmc-target        a short run for rocprofv3 counter passes (kernels + a copy)
   python bench.py --summarize-pmc DIR rocprofv3 counter CSVs -> profiles/ traffic summary
+  python bench.py --summarize-trace CSV  rocprofv3 kernel trace -> kernel-time table
 """
 from __future__ import annotations
 
@@ -101,6 +103,38 @@ def frame_distribution(layer, ring, w, out, stream, torch, n=100, backlog=50):
     t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
     return {"frames": n, "median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
             "p90_us": float(np.percentile(t, 90)), "min_us": float(t.min()), "max_us": float(t.max())}
+
+
+def pass_in_frames_us(layer, ring, w, out, stream, torch, n=60, backlog=30):
+    """Average duration of the pass kernel inside the frames of the workload: one event pair around
+    the denoising passes of each of n frames (back-to-back pass launches, inputs cycling through
+    the ring from HBM, as in the timed frames), enqueued behind a backlog of frames; the frame's
+    span over its denoise_steps launches.  Returns (mean per launch, per-frame means)."""
+    run_frames(layer, ring, w, backlog, out, stream)
+    evs = []
+    for f in range(n):
+        passes, beta, alpha = ring[f % RING]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for p, (q, k, v) in enumerate(passes):
+            if p == 0:
+                a.record(stream)
+            if p < w.denoise_steps:
+                if layer.access == "token":
+                    layer.denoise_step_seq(q, k, v, beta, out=out, stream=stream)
+                else:
+                    layer.denoise_step(q, k, v, out=out, stream=stream)
+                if p + 1 == w.denoise_steps:
+                    b.record(stream)
+                    evs.append((a, b))
+            elif layer.access == "token":
+                layer.commit_frame_seq(q, k, v, beta, alpha, out=out, stream=stream)
+            elif alpha is None:
+                layer.commit_frame_gated(q, k, v, *beta, out=out, stream=stream)
+            else:
+                layer.commit_frame(q, k, v, beta, alpha, out=out, stream=stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 / w.denoise_steps for a, b in evs])
+    return float(t.mean()), t
 
 
 def stage_ring(w, torch, gated=False):
@@ -452,7 +486,8 @@ def bench(args):
         graph_ms, graph_wall = time_region(stream, torch, lambda: [graphs[i % RING].replay() for i in range(args.steps)])
 
         # kernel timing: events around each launch, outside the two timed regions above
-        pass_us = pass_launch_us(layer, ring, w, out, stream, torch)
+        pass_us, pass_all = pass_in_frames_us(layer, ring, w, out, stream, torch)
+        pass_b2b_us = pass_launch_us(layer, ring, w, out, stream, torch)
         write_us = commit_launch_us(layer, ring, w, None, stream, torch, out)
         clean_us = commit_launch_us(layer, ring, w, out, stream, torch, out)
         dist = frame_distribution(layer, ring, w, out, stream, torch)
@@ -502,7 +537,9 @@ def bench(args):
                                    "tflops": gemm_tflops, "frac": achieved / gemm_tflops},
         },
         "breakdown": {
-            "pass_us": pass_us, "clean_pass_with_write_us": clean_us, "state_write_alone_us": write_us,
+            "pass_us": pass_us, "pass_us_p10_p90": [float(np.percentile(pass_all, 10)), float(np.percentile(pass_all, 90))],
+            "pass_us_back_to_back": pass_b2b_us,
+            "clean_pass_with_write_us": clean_us, "state_write_alone_us": write_us,
             "state_write_alone_GBps": state_write_bytes(w) / (write_us * 1e-6) / 1e9,
             "state_write_alone_hbm_frac": state_write_bytes(w) / (write_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
             "per_frame_us": dist,
@@ -925,6 +962,52 @@ def summarize_pmc(args):
     print(json.dumps(out, indent=1))
 
 
+def summarize_trace(args):
+    """A rocprofv3 kernel trace (CSV) of a bench run -> a markdown table of kernel times, with the
+    pass kernel's launches told apart: the denoising passes inside the frames (the four launches
+    of 160 x 8-wave work-groups that precede a clean-pass launch and its reduce), the clean passes
+    (pass and state-write work-groups in one grid), and its other launches (the back-to-back
+    timing and the state write alone)."""
+    import csv
+
+    rows = []
+    with open(args.summarize_trace) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                         int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))))
+    rows.sort()
+    is_fwd = [FWD_KERNEL in r[2] for r in rows]
+    wgs = sorted({r[3] for r, f in zip(rows, is_fwd) if f})
+    small = wgs[0] if wgs else 0
+    label = [None] * len(rows)
+    # frames: four small-grid passes, one larger-grid pass (the clean pass), then the reduce
+    i = 0
+    while i + 5 < len(rows):
+        names = rows[i:i + 6]
+        ok = all(is_fwd[i + j] and names[j][3] == small for j in range(4)) and is_fwd[i + 4] and \
+            names[4][3] > small and "commit_reduce" in names[5][2]
+        if ok:
+            for j in range(4):
+                label[i + j] = "pass in frame"
+            label[i + 4] = "clean pass"
+            label[i + 5] = "reduce in frame"
+            i += 6
+        else:
+            i += 1
+    groups = {}
+    for r, f, lab in zip(rows, is_fwd, label):
+        if lab is None:
+            lab = ("pass kernel, other launches" if f else
+                   "reduce, other launches" if "commit_reduce" in r[2] else r[2][:90])
+        groups.setdefault(lab, []).append((r[1] - r[0]) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|")
+    for lab, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {lab} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} | "
+              f"{100 * sum(v) / total:.1f} % |")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -949,13 +1032,16 @@ def main():
                     help="a 30-layer attention stack, 23 ARL2 + 7 softmax layers, against all softmax")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--summarize-trace", metavar="CSV", help="rocprofv3 kernel trace -> kernel-time table")
     args = ap.parse_args()
     if args.gated and args.access == "token":
         sys.exit("--gated applies to frame-level access only")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         sys.exit("bench.py measures one GPU: this layer runs without sharding or collectives on a "
                  "single MI355X; --gpus must be 1")
-    if args.summarize_pmc:
+    if args.summarize_trace:
+        summarize_trace(args)
+    elif args.summarize_pmc:
         summarize_pmc(args)
     elif args.pmc_target:
         pmc_target(args)
