@@ -893,6 +893,22 @@ def backward_bench(args):
 COPY_BYTES = 2**30  # calibration copy: 1 GiB each way, four times the 256 MB last-level cache
 
 
+def mfma_ceiling():
+    """Runs the sustained-MFMA-rate probe (gated_delta_linear_amd/csrc/probe_mfma_rate.hip, built
+    by build() into the package directory): independent 32x32x16 bf16 MFMA chains on 156 and on
+    256 work-groups, one per CU; one JSON line per grid with the rate and the clock the waves saw."""
+    import subprocess
+
+    from gated_delta_linear_amd.build import PROBE_PATH
+
+    if not os.path.exists(PROBE_PATH):
+        sys.exit(f"{PROBE_PATH} is missing: run __graft_entry__.build() first")
+    res = subprocess.run([PROBE_PATH], capture_output=True, text=True)
+    sys.stdout.write(res.stdout)
+    if res.returncode != 0:
+        sys.exit(f"probe failed ({res.returncode}): {res.stderr.strip()}")
+
+
 def pmc_target(args):
     """A short, fixed run for counter passes: a plain device-to-device copy of known size (the
     calibration of FETCH_SIZE / WRITE_SIZE; before each copy another 1 GiB buffer is written,
@@ -1030,6 +1046,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="the layer's backward (arl2_bwd.h) per frame")
     ap.add_argument("--stack", action="store_true",
                     help="a 30-layer attention stack, 23 ARL2 + 7 softmax layers, against all softmax")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="the chip's sustained dense bf16 MFMA rate (the probe built beside the library)")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="CSV", help="rocprofv3 kernel trace -> kernel-time table")
@@ -1043,6 +1061,8 @@ def main():
         summarize_trace(args)
     elif args.summarize_pmc:
         summarize_pmc(args)
+    elif args.mfma_ceiling:
+        mfma_ceiling()
     elif args.pmc_target:
         pmc_target(args)
     elif args.series:

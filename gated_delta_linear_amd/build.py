@@ -89,5 +89,25 @@ def build_library(verbose: bool = False, jobs: int | None = None, sanitize: bool
     return lib_path
 
 
+PROBE_SRC = os.path.join(CSRC, "probe_mfma_rate.hip")
+PROBE_PATH = os.path.join(PKG_DIR, "probe_mfma_rate")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the sustained-MFMA-rate probe (a standalone measurement program, not part of
+    libarl2.so) into the package directory, beside the library."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE_PATH + ".tmp"]
+    msgs = _run(cmd)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+        if msgs.strip():
+            print(msgs)
+    os.replace(PROBE_PATH + ".tmp", PROBE_PATH)
+    return PROBE_PATH
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv, sanitize="--asan" in sys.argv))
+    if "--asan" not in sys.argv:
+        print(build_probe(verbose="-v" in sys.argv))
