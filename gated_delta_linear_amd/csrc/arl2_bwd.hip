@@ -20,13 +20,16 @@
 // reproducible), 8 waves per work-group: dK, dV per 128-key block, 16 keys per wave (the keys'
 // fragments stay in registers, 64-query blocks stream through LDS), and dQ per 128-query block,
 // four 32-query groups times two key halves (64-key blocks stream through LDS); the scores are
-// recomputed in each.  Their products run in fp16 with fp32 accumulation: the bf16 inputs
-// convert exactly, and P, dS and dO round with a relative step of 2^-11.  The
+// recomputed in each.  Both stage their streamed blocks in two LDS buffers (block b + 1 is
+// written while block b is multiplied, one barrier per block).  Their products run in fp16
+// with fp32 accumulation: the bf16 inputs convert exactly, and P, dS and dO round with a
+// relative step of 2^-11.  The
 // token kernels (inter read, state write) work per 128-token chunk with 16x16x32 MFMAs on
 // split-bf16 operands (hi + lo, three products per term), so that their d x d products keep
 // about fp32 accuracy as the forward's state write does; their sums over tokens leave the chunk
 // as partials that a per-head kernel adds in a fixed order.
 #include <algorithm>
+#include <type_traits>
 
 #include "arl2_device.h"
 #include "arl2_kernels.h"
@@ -199,9 +202,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // per wave) in proportion.  Per query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l,
 // register i <-> query 16 m + 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS =
 // P (dP - Dv); then dV^T += dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from
-// the C registers.  The next block's Q and dO rows are loaded into registers while the current
-// block is multiplied: with 64 NW >= 2 x the tile's blocks each thread moves one block of one
-// tile, otherwise one block of each.
+// the C registers.  Block qb + 1 is staged into the other LDS buffer while block qb is
+// multiplied, and block qb + 2's Q and dO rows are loaded into registers meanwhile: with
+// 64 NW >= 2 x the tile's blocks each thread moves one block of one tile, otherwise one block of
+// each.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
@@ -212,9 +216,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int TILE = kAttnBlock * LR + D * Sh::LT;  // f16 elements of one staged tile (rows + transposed)
   constexpr int NBLK = 16 * (D / 8);                  // 4-row x 8-feature blocks of one tile
   constexpr bool SPLIT = 64 * NW >= 2 * NBLK;         // one block of one tile per thread
-  __shared__ __align__(16) f16 lds[2 * TILE];
-  __shared__ __align__(16) float lse_s[kAttnBlock], dv_s[kAttnBlock];
-  f16 *qr = lds, *qtr = lds + kAttnBlock * LR, *dor = lds + TILE, *dotr = lds + TILE + kAttnBlock * LR;
+  // two buffers of (Q rows, Q^T, dO rows, dO^T): block qb is read from buffer qb % 2 while block
+  // qb + 1 is staged into the other one
+  __shared__ __align__(16) f16 lds[2][2 * TILE];
+  __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
@@ -254,22 +259,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
   const int nqb = (T + kAttnBlock - 1) / kAttnBlock;
-  load_block(0);
-  for (int qb = 0; qb < nqb; ++qb) {
-    __syncthreads();  // the previous block's LDS reads are done
+  auto stage_block = [&](int buf) {
+    f16* L = lds[buf];
     if constexpr (SPLIT) {
-      if (mover_q) tq.store(qr, qtr);
-      else tq.store(dor, dotr);
+      if (mover_q) tq.store(L, L + kAttnBlock * LR);
+      else tq.store(L + TILE, L + TILE + kAttnBlock * LR);
     } else {
-      tq.store(qr, qtr);
-      to.store(dor, dotr);
+      tq.store(L, L + kAttnBlock * LR);
+      to.store(L + TILE, L + TILE + kAttnBlock * LR);
     }
     if (tid < kAttnBlock) {
-      lse_s[tid] = lse_r;
-      dv_s[tid] = dv_r;
+      lse_s[buf][tid] = lse_r;
+      dv_s[buf][tid] = dv_r;
     }
+  };
+  load_block(0);
+  stage_block(0);
+  if (nqb > 1) load_block(kAttnBlock);
+  for (int qb = 0; qb < nqb; ++qb) {
+    // block qb is staged (everyone's stores are done) and block qb - 1's reads of the other
+    // buffer are done: block qb + 1 goes there while block qb is multiplied
     __syncthreads();
-    if (qb + 1 < nqb) load_block((qb + 1) * kAttnBlock);
+    const int cur = qb & 1;
+    if (qb + 1 < nqb) stage_block(cur ^ 1);
+    if (qb + 2 < nqb) load_block((qb + 2) * kAttnBlock);
+    const f16 *qr = lds[cur], *qtr = lds[cur] + kAttnBlock * LR, *dor = lds[cur] + TILE,
+              *dotr = lds[cur] + TILE + kAttnBlock * LR;
+    const float* lse_c = lse_s[cur];
+    const float* dv_c = dv_s[cur];
     // per 32-query half s2: S and dP of its two 16-query blocks, then its share of dV^T, dK^T
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -285,8 +302,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           sc = mfma16h(aq, kf[s], sc);
           dp = mfma16h(ao, vf[s], dp);
         }
-        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_s + 16 * m + 4 * g);
-        const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_s + 16 * m + 4 * g);
+        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_c + 16 * m + 4 * g);
+        const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_c + 16 * m + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
@@ -319,8 +336,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // 8 (i / 4) + 4 (l / 32) + i % 4 of the wave's 32, query l % 32: every lane holds one query, so
 // its lse and Dv are one value each), dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T with dS^T as
 // the B operand straight from the C registers (k-step h: registers 8 h .. 8 h + 7).  A 32x32x16
-// product reads one 1 KB operand from LDS per 32 K multiply-adds, twice the 16x16x32 ratio.  The
-// next block's K and V rows are loaded into registers while the current block is multiplied.
+// product reads one 1 KB operand from LDS per 32 K multiply-adds, twice the 16x16x32 ratio.
+// Block kb + 1 is staged into the other LDS stage while block kb is multiplied, from registers
+// loaded two blocks earlier (two register sets; the dK/dV kernel keeps one, as a second one
+// there costs more in its schedule than it hides).
 template <int D, int NQG>
 __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
@@ -332,8 +351,9 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
   constexpr int XCH = NQG * FB * 64 * 32;              // f16: the key halves' exchange (f32x16 per lane)
   constexpr int NBLK = 16 * (D / 8);                   // 4-row x 8-feature blocks of one tile
   constexpr bool SPLIT = 128 * NQG >= 2 * NBLK;        // one block of one tile per thread
-  __shared__ __align__(16) f16 lds[STAGE > XCH ? STAGE : XCH];
-  f16 *kr = lds, *vr = lds + kAttnBlock * LR, *ktr = lds + 2 * kAttnBlock * LR;
+  // two stages (K rows, V rows, K^T): block kb is read from stage kb % 2 while block kb + 1 is
+  // staged into the other one; the exchange at the end reuses them
+  __shared__ __align__(16) f16 lds[2 * STAGE > XCH ? 2 * STAGE : XCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int qh = wave % NQG, kh = wave / NQG;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -352,36 +372,56 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
   for (int n = 0; n < FB; ++n) dqt[n] = zero16();
   // SPLIT: threads [0, NBLK) move K blocks (with the transpose), [NBLK, 2 NBLK) V blocks, through
   // one register block (whole waves either way); otherwise every thread moves block tid of both.
+  // Two register sets: block j's rows come into set j % 2 two blocks before they are staged.
   const bool mover_k = !SPLIT || tid < NBLK;
-  TileBlock<D> tk, tv;
-  if constexpr (SPLIT) {
-    tk.init(mover_k ? tid : tid - NBLK, true);
-  } else {
-    tk.init(tid, true);
-    tv.init(tid, true);
-  }
-  auto load_block = [&](int r0) {
+  TileBlock<D> tk[2], tv[2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
     if constexpr (SPLIT) {
-      tk.load(mover_k ? k : v, base, rs, r0, T);
+      tk[sl].init(mover_k ? tid : tid - NBLK, true);
     } else {
-      tk.load(k, base, rs, r0, T);
-      tv.load(v, base, rs, r0, T);
+      tk[sl].init(tid, true);
+      tv[sl].init(tid, true);
+    }
+  }
+  auto load_block = [&](int r0, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    if constexpr (SPLIT) {
+      tk[sl].load(mover_k ? k : v, base, rs, r0, T);
+    } else {
+      tk[sl].load(k, base, rs, r0, T);
+      tv[sl].load(v, base, rs, r0, T);
     }
   };
   const int nkb = (T + kAttnBlock - 1) / kAttnBlock;
-  load_block(0);
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto stage_block = [&](int buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    f16* L = lds + buf * STAGE;
+    if constexpr (SPLIT) {
+      if (mover_k) tk[sl].store(L, L + 2 * kAttnBlock * LR);
+      else tk[sl].store(L + kAttnBlock * LR, nullptr);
+    } else {
+      tk[sl].store(L, L + 2 * kAttnBlock * LR);
+      tv[sl].store(L + kAttnBlock * LR, nullptr);
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load_block(0, S0());
+  if (nkb > 1) load_block(kAttnBlock, S1());
+  stage_block(0, S0());
+  if (nkb > 2) load_block(2 * kAttnBlock, S0());
+  // block kb (odd_c: kb % 2, a compile-time constant): it is staged in stage kb % 2, and block
+  // kb - 1's reads of the other stage are done, so block kb + 1 (register set (kb + 1) % 2) goes
+  // there while block kb is multiplied; that set then takes block kb + 3
+  auto kblock = [&](int kb, auto odd_c) {
+    constexpr int odd = decltype(odd_c)::value;
+    using Next = std::integral_constant<int, 1 - odd>;
     const int r0 = kb * kAttnBlock;
     __syncthreads();
-    if constexpr (SPLIT) {
-      if (mover_k) tk.store(kr, ktr);
-      else tk.store(vr, nullptr);
-    } else {
-      tk.store(kr, ktr);
-      tv.store(vr, nullptr);
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) load_block(r0 + kAttnBlock);
+    if (kb + 1 < nkb) stage_block(1 - odd, Next());
+    if (kb + 3 < nkb) load_block(r0 + 3 * kAttnBlock, Next());
+    const f16 *kr = lds + odd * STAGE, *vr = kr + kAttnBlock * LR, *ktr = kr + 2 * kAttnBlock * LR;
     f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
     for (int s = 0; s < K16; ++s) {
@@ -406,7 +446,13 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
         const f16x4 a0 = *reinterpret_cast<const f16x4*>(pa), a1 = *reinterpret_cast<const f16x4*>(pa + 8);
         dqt[fb] = mfma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, dsb[hh], dqt[fb]);
       }
+  };
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    kblock(kb, S0());
+    kblock(kb + 1, S1());
   }
+  if (kb < nkb) kblock(kb, S0());
   __syncthreads();
   f32x16* xs = reinterpret_cast<f32x16*>(lds) + (size_t)qh * FB * 64;
   static_assert(NQG * FB * 64 * 64 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
