@@ -65,6 +65,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def pass_grid(w) -> int:
+    """Work-groups of one denoising-pass launch: one per (stream, head, 128-query tile)."""
+    return w.batch * w.heads * ((w.tokens + 127) // 128)
+
+
 def pass_flops(w) -> float:
     """Algorithmic FLOPs of one pass: per (stream, head) 4 T^2 d (scores and P V) + 2 T d^2
     (the inter-frame read as Q (phi_q S))."""
@@ -307,6 +312,26 @@ def gemm_reference_tflops(torch, n=8192, reps=10) -> float:
     return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
+def probe_ceiling(iters: int = 10000):
+    """The chip's sustained dense bf16 MFMA rate from the probe built beside the library (independent
+    MFMA chains only; one work-group per CU on 156 and on 256 CUs): {grid: {tflops, clock_ghz}}, or
+    None when the probe has not been built."""
+    import subprocess
+
+    from gated_delta_linear_amd.build import PROBE_PATH
+
+    if not os.path.exists(PROBE_PATH):
+        return None
+    res = subprocess.run([PROBE_PATH, str(iters)], capture_output=True, text=True)
+    if res.returncode != 0:
+        return None
+    out = {}
+    for line in res.stdout.splitlines():
+        r = json.loads(line)
+        out[str(r["work_groups"])] = {"tflops": r["tflops"], "clock_ghz": r["clock_ghz"]}
+    return out
+
+
 def cpu_env():
     """BLAS threads the oracle uses, the BLAS build and the CPU model."""
     blas = "unknown"
@@ -494,6 +519,7 @@ def bench(args):
         torch.cuda.synchronize()
         device_bytes = layer.device_bytes
         layer.close()
+        ceiling = probe_ceiling()  # before the GEMM, which heats the GPU
         gemm_tflops = gemm_reference_tflops(torch)  # last: a long GEMM heats the GPU
 
     use_graph = args.graph
@@ -535,6 +561,12 @@ def bench(args):
             "flops_per_launch": pass_flops(w), "avg_launch_us": pass_us,
             "measured_reference": {"what": "torch.matmul bf16 8192^3 (hipBLASLt) on the same GPU",
                                    "tflops": gemm_tflops, "frac": achieved / gemm_tflops},
+            # what the chip sustains with nothing but MFMAs on the pass's grid (its clock drops
+            # below the 2.4 GHz of the nominal peak when every CU is busy)
+            "sustained_mfma_ceiling": None if ceiling is None else {
+                "what": "bench.py --mfma-ceiling probe: independent bf16 MFMA chains, one work-group per CU",
+                "by_work_groups": ceiling, "pass_work_groups": pass_grid(w),
+                "frac_of_ceiling": achieved / ceiling["156" if pass_grid(w) <= 156 else "256"]["tflops"]},
         },
         "breakdown": {
             "pass_us": pass_us, "pass_us_p10_p90": [float(np.percentile(pass_all, 10)), float(np.percentile(pass_all, 90))],
