@@ -125,6 +125,8 @@ SMALL = [  # (batch, heads, d, T, frames, passes)
     (1, 2, 64, 37, 3, 2),
     (2, 2, 64, 200, 2, 3),
     (1, 2, 128, 64, 2, 2),
+    (1, 2, 128, 100, 2, 2),  # two 64-row blocks: the staging loops' tail without a third block
+    (1, 1, 64, 128, 2, 2),   # two full blocks
     (1, 1, 128, 129, 3, 2),
     (2, 3, 128, 200, 2, 2),
     (1, 2, 128, 333, 2, 2),
