@@ -40,6 +40,9 @@
  * Status codes, arl2_last_error() and the stream rule (a call on a different stream than the
  * previous one waits for it) are those of arl2.h.  A failed launch poisons the object
  * (ARL2_E_PROTOCOL) until arl2_bwd_begin.
+ * Graph capture: unlike the forward's calls, these are meant for eager launch.  Each
+ * arl2_bwd_commit reads dL/dS from one of two device buffers and writes the other, chosen on the
+ * host, so a captured commit would replay with the buffers it was captured with.
  */
 #ifndef ARL2_BWD_H
 #define ARL2_BWD_H
