@@ -31,6 +31,9 @@
  * Status codes, the stream rule (a call on a different stream than the previous one waits
  * for it) and arl2_last_error() are those of arl2.h.  A failed launch poisons the layer
  * (later calls return ARL2_E_PROTOCOL) until arl2_softmax_reset.
+ * Graph capture: the number of cached frames is host state, and every call's launch is shaped
+ * by it (keys attended, the cache slot a commit writes), so a captured call replays as the call
+ * it was: capture the passes of one frame and replay them only while that frame is current.
  */
 #ifndef ARL2_SOFTMAX_H
 #define ARL2_SOFTMAX_H
