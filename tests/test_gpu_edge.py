@@ -230,7 +230,8 @@ def test_fp32_inputs_tiny_workload():
     assert worst_o <= OUT_TOL and worst_s <= STATE_TOL, (worst_o, worst_s)
 
 
-@pytest.mark.parametrize("B,H,d,T", [(1, 1, 16, 16), (2, 3, 64, 129), (1, 2, 128, 300)])
+@pytest.mark.parametrize("B,H,d,T", [(1, 1, 16, 16), (2, 3, 64, 129), (1, 2, 128, 300),
+                                     (1, 12, 128, 1560)])  # the last: the 12-head, 1560-token layer
 def test_fp32_inputs_equal_bf16_path_bitwise(B, H, d, T):
     """Device rounding of fp32 inputs = the host's round-to-nearest-even: outputs and state equal
     the bf16 layer's, bitwise, over two frames (denoising, clean pass with and without output)."""
