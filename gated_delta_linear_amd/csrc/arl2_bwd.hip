@@ -138,6 +138,11 @@ __device__ __forceinline__ f16x8 load_f16x8(const T* p) {
   else return to_f16(ld_bf16x8(p));
 }
 
+// Row-major staged tiles keep 16-byte chunk c of row r at chunk c ^ ((r >> 4) & 3): with the
+// 272-byte row pitch (4 banks per row), the 16 lanes of a staging store (rows 4 apart) and the 16
+// lanes of a fragment read (16 consecutive rows) then both land on 16 distinct 4-bank groups.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 4) & 3); }
+
 // One 4-row x 8-feature block of a 64-row tile of a [.][T][H][D] bf16 or fp16 tensor, staged
 // through registers into LDS as fp16: row-major (pitch LR) and, when tr is not null, transposed
 // (pitch LT: tr[f][r]).  Rows past T are zeros.  Block i of a tile is (row group i % 16, feature
@@ -170,7 +175,7 @@ struct TileBlock {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x[e] = from_bf16 ? to_f16(__builtin_bit_cast(bf16x8, raw[e])) : __builtin_bit_cast(f16x8, raw[e]);
-      *reinterpret_cast<f16x8*>(rowm + (4 * rg + e) * Sh::LR + 8 * cc) = x[e];
+      *reinterpret_cast<f16x8*>(rowm + (4 * rg + e) * Sh::LR + 8 * swz_chunk(4 * rg + e, cc)) = x[e];
     }
     if (tr) {
 #pragma unroll
@@ -297,8 +302,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const f16x8 aq = *reinterpret_cast<const f16x8*>(qr + (16 * m + l16) * LR + 32 * s + 8 * g);
-          const f16x8 ao = *reinterpret_cast<const f16x8*>(dor + (16 * m + l16) * LR + 32 * s + 8 * g);
+          const int ro = (16 * m + l16) * LR + 8 * swz_chunk(16 * m + l16, 4 * s + g);
+          const f16x8 aq = *reinterpret_cast<const f16x8*>(qr + ro);
+          const f16x8 ao = *reinterpret_cast<const f16x8*>(dor + ro);
           sc = mfma16h(aq, kf[s], sc);
           dp = mfma16h(ao, vf[s], dp);
         }
@@ -425,8 +431,9 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
     f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
     for (int s = 0; s < K16; ++s) {
-      const f16x8 ak = *reinterpret_cast<const f16x8*>(kr + (32 * kh + l32) * LR + 16 * s + 8 * hi);
-      const f16x8 av = *reinterpret_cast<const f16x8*>(vr + (32 * kh + l32) * LR + 16 * s + 8 * hi);
+      const int ro = (32 * kh + l32) * LR + 8 * swz_chunk(32 * kh + l32, 2 * s + hi);
+      const f16x8 ak = *reinterpret_cast<const f16x8*>(kr + ro);
+      const f16x8 av = *reinterpret_cast<const f16x8*>(vr + ro);
       sc = mfma32(ak, qf[s], sc);
       dp = mfma32(av, df[s], dp);
     }
