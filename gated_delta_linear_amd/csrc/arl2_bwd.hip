@@ -335,40 +335,103 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// V and K^T of a pass in fp16 for the dQ kernel's direct-to-LDS staging: v16 in the [B][T][H][d]
+// layout of v (rows past T not written); kt16 [B][H][d][tp], each head's keys as rows of 64-key
+// blocks per feature (keys past T zero).  One work-group per (stream, head, 64-key block); thread
+// j moves rows 4 (j % 16) .. + 3 of 8-feature chunk j / 16, K transposed through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                           f16* __restrict__ v16, f16* __restrict__ kt16, int T, int H,
+                                                           int tp) {
+  constexpr int CPR = D / 8, TPITCH = kAttnBlock + 8;  // chunks per row; transposing tile's pitch (f16)
+  __shared__ __align__(16) f16 tr[D * TPITCH];
+  const int tid = threadIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, k0 = blockIdx.x * kAttnBlock;
+  const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
+  for (int j = tid; j < 16 * CPR; j += 256) {
+    const int rg = j % 16, cc = j / 16;
+    f16x8 kx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = k0 + 4 * rg + e;
+      kx[e] = f16x8{};
+      if (key < T) {
+        const int64_t o = base + (int64_t)key * rs + 8 * cc;
+        kx[e] = to_f16(ld_bf16x8(k + o));
+        *reinterpret_cast<f16x8*>(v16 + o) = to_f16(ld_bf16x8(v + o));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<f16x4*>(tr + (8 * cc + c) * TPITCH + 4 * rg) = f16x4{kx[0][c], kx[1][c], kx[2][c], kx[3][c]};
+  }
+  __syncthreads();
+  for (int j = tid; j < D * (kAttnBlock / 8); j += 256) {
+    const int f = j / (kAttnBlock / 8), c = j % (kAttnBlock / 8);
+    *reinterpret_cast<f16x8*>(kt16 + ((int64_t)bh * D + f) * tp + k0 + 8 * c) =
+        *reinterpret_cast<const f16x8*>(tr + f * TPITCH + 8 * c);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_b;
+
+// 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_b*)lds, 16, voff, soff, 0, 0);
+}
+
+// Buffer resource over rows [first_row, T) of one (stream, head) slice of a [B][T][H][d] fp16
+// tensor: rows past the frame lie outside num_records and load as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc16(const f16* base, int T, int64_t rs, int d,
+                                                              int first_row) {
+  const int64_t start = (int64_t)first_row * rs;
+  const int64_t left = (int64_t)(T - 1) * rs + d - start;
+  const bool any = left > 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(any ? base + start : base), (short)0,
+                                           any ? (int)(left * 2) : 0, 0x00020000);
+}
+
 // dQ of 32 NQG queries of one (stream, head), with 32x32x16 MFMAs.  2 NQG waves: wave w owns
 // queries 32 (w % NQG) .. +31 and the key half w / NQG of every 64-key block; the halves are added
 // at the end.  Every query block reads the head's whole K and V, so wider work-groups cut that
-// stream (and the staging per wave) in proportion.  Per key block: S^T = K Q^T and dP^T = V dO^T (32x32 C blocks: lane l, register i <-> key
-// 8 (i / 4) + 4 (l / 32) + i % 4 of the wave's 32, query l % 32: every lane holds one query, so
-// its lse and Dv are one value each), dS^T = P^T (dP^T - Dv), then dQ^T += K^T dS^T with dS^T as
-// the B operand straight from the C registers (k-step h: registers 8 h .. 8 h + 7).  A 32x32x16
-// product reads one 1 KB operand from LDS per 32 K multiply-adds, twice the 16x16x32 ratio.
-// Block kb + 1 is staged into the other LDS stage while block kb is multiplied, from registers
-// loaded two blocks earlier (two register sets; the dK/dV kernel keeps one, as a second one
-// there costs more in its schedule than it hides).
+// stream in proportion.  Per key block: S^T = K Q^T and dP^T = V dO^T (32x32 C blocks: lane l,
+// register i <-> key 8 (i / 4) + 4 (l / 32) + i % 4 of the wave's 32, query l % 32: every lane
+// holds one query, so its lse and Dv are one value each), dS^T = P^T (dP^T - Dv), then
+// dQ^T += K^T dS^T with dS^T as the B operand straight from the C registers (k-step h: registers
+// 8 h .. 8 h + 7).  A 32x32x16 product reads one 1 KB operand from LDS per 32 K multiply-adds,
+// twice the 16x16x32 ratio.
+// Staging: each block's K rows (bf16, as given), V rows (the fp16 copy v16) and K^T (kt16, 64
+// keys per feature row, fp16) come straight into LDS with direct-to-LDS loads, in two stages: block kb + 1's
+// loads fly while block kb is multiplied, and no thread converts or transposes anything.  A row
+// tile keeps 16-byte chunk c of key row r at chunk c ^ (r mod d/8), the K^T tile 8-key chunk c of
+// feature row f at c ^ ((f >> 1) & 7): every load brings whole rows, the row fragments' reads hit
+// distinct banks and the K^T fragments' reads at most two lanes per bank.
 template <int D, int NQG>
 __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
-    const float* __restrict__ lse, const float* __restrict__ dvec, float* __restrict__ dq, int T, int H, float scale,
-    float scale_log2) {
-  using Sh = BwdShape<D>;
-  constexpr int K16 = D / 16, FB = D / 32, LR = Sh::LR, LT = Sh::LT;
-  constexpr int STAGE = 2 * kAttnBlock * LR + D * LT;  // f16: K rows, V rows, K transposed
-  constexpr int XCH = NQG * FB * 64 * 32;              // f16: the key halves' exchange (f32x16 per lane)
-  constexpr int NBLK = 16 * (D / 8);                   // 4-row x 8-feature blocks of one tile
-  constexpr bool SPLIT = 128 * NQG >= 2 * NBLK;        // one block of one tile per thread
-  // two stages (K rows, V rows, K^T): block kb is read from stage kb % 2 while block kb + 1 is
-  // staged into the other one; the exchange at the end reuses them
-  __shared__ __align__(16) f16 lds[2 * STAGE > XCH ? 2 * STAGE : XCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const f16* __restrict__ v16,
+    const f16* __restrict__ kt16, const f16* __restrict__ doh, const float* __restrict__ lse,
+    const float* __restrict__ dvec, float* __restrict__ dq, int T, int H, int tp, float scale, float scale_log2) {
+  constexpr int K16 = D / 16, FB = D / 32, NW = 2 * NQG;
+  constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per key row, 16-byte chunks per row, rows per 1-KB load
+  constexpr int TILE = kAttnBlock * RB;                    // bytes of a 64-row tile; the K^T tile (d rows of 128 bytes) too
+  constexpr int LD = TILE / 1024;                          // 1-KB loads per tile
+  constexpr int LPT = LD / NW;                             // of them per wave
+  static_assert(LD % NW == 0, "every wave issues the same number of loads per tile");
+  // Separate arrays per stage and tile, addressed with compile-time stage numbers, so that the
+  // compiler tells the loads in flight into one stage from the reads of the other.
+  __shared__ __align__(16) unsigned char kr0[TILE], kr1[TILE], vr0[TILE], vr1[TILE], kt0[TILE], kt1[TILE];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qh = wave % NQG, kh = wave / NQG;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
   const int qi = blockIdx.x * (32 * NQG) + 32 * qh + l32;
-  f16x8 qf[K16], df[K16];  // B operands: lane l holds Q (dO) of query qi, features 16 s + 8 (l / 32) ..
+  // B operands: lane l holds Q (bf16, as given: S^T = K Q^T runs on the bf16 inputs) and dO (fp16)
+  // of query qi, features 16 s + 8 (l / 32) ..
+  bf16x8 qf[K16];
+  f16x8 df[K16];
 #pragma unroll
   for (int s = 0; s < K16; ++s) {
-    qf[s] = qi < T ? load_f16x8(q + base + (int64_t)qi * rs + 16 * s + 8 * hi) : f16x8{};
+    qf[s] = qi < T ? ld_bf16x8(q + base + (int64_t)qi * rs + 16 * s + 8 * hi) : zero_bf16x8();
     df[s] = qi < T ? load_f16x8(doh + base + (int64_t)qi * rs + 16 * s + 8 * hi) : f16x8{};
   }
   const float L = qi < T ? lse[(int64_t)bh * T + qi] : 0.f;
@@ -376,64 +439,58 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
   f32x16 dqt[FB];
 #pragma unroll
   for (int n = 0; n < FB; ++n) dqt[n] = zero16();
-  // SPLIT: threads [0, NBLK) move K blocks (with the transpose), [NBLK, 2 NBLK) V blocks, through
-  // one register block (whole waves either way); otherwise every thread moves block tid of both.
-  // Two register sets: block j's rows come into set j % 2 two blocks before they are staged.
-  const bool mover_k = !SPLIT || tid < NBLK;
-  TileBlock<D> tk[2], tv[2];
+
+  // Loads of block kb: a wave's loads i = wave + NW m of each tile (row tiles: rows RPI i ..,
+  // lane l row RPI i + l / CPR, chunk (l % CPR) ^ (row % CPR); K^T: feature rows 8 i .., lane l row
+  // 8 i + l / 8, key chunk (l % 8) ^ ((row >> 1) & 7)).
+  auto issue = [&](int kb, unsigned char* kd, unsigned char* vd, unsigned char* td) {
+    const int r0 = kb * kAttnBlock;
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc16(reinterpret_cast<const f16*>(k) + base, T, rs, D, r0);  // bf16 bits
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc16(v16 + base, T, rs, D, r0);
+    // (base and size made explicitly wave-uniform, so that the descriptor lives in scalar registers)
+    const uint64_t kt_addr = reinterpret_cast<uint64_t>(kt16 + ((int64_t)bh * D * tp + r0));
+    const uint32_t kt_lo = __builtin_amdgcn_readfirstlane((uint32_t)kt_addr);
+    const uint32_t kt_hi = __builtin_amdgcn_readfirstlane((uint32_t)(kt_addr >> 32));
+    const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(((uint64_t)kt_hi << 32) | kt_lo), (short)0,
+        __builtin_amdgcn_readfirstlane(D * tp * 2 - r0 * 2), 0x00020000);
 #pragma unroll
-  for (int sl = 0; sl < 2; ++sl) {
-    if constexpr (SPLIT) {
-      tk[sl].init(mover_k ? tid : tid - NBLK, true);
-    } else {
-      tk[sl].init(tid, true);
-      tv[sl].init(tid, true);
+    for (int m = 0; m < LPT; ++m) {
+      const int i = wave + NW * m, row = RPI * i + lane / CPR;
+      const int vo = (lane / CPR) * (int)(rs * 2) + 16 * ((lane % CPR) ^ (row % CPR));
+      dma16b(rk, kd + i * 1024, vo, RPI * i * (int)(rs * 2));
+      dma16b(rv, vd + i * 1024, vo, RPI * i * (int)(rs * 2));
     }
-  }
-  auto load_block = [&](int r0, auto slot_c) {
-    constexpr int sl = decltype(slot_c)::value;
-    if constexpr (SPLIT) {
-      tk[sl].load(mover_k ? k : v, base, rs, r0, T);
-    } else {
-      tk[sl].load(k, base, rs, r0, T);
-      tv[sl].load(v, base, rs, r0, T);
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int i = wave + NW * m, row = 8 * i + lane / 8;
+      dma16b(rkt, td + i * 1024, (lane / 8) * tp * 2 + 16 * ((lane % 8) ^ ((row >> 1) & 7)), 8 * i * tp * 2);
     }
   };
   const int nkb = (T + kAttnBlock - 1) / kAttnBlock;
-  auto stage_block = [&](int buf, auto slot_c) {
-    constexpr int sl = decltype(slot_c)::value;
-    f16* L = lds + buf * STAGE;
-    if constexpr (SPLIT) {
-      if (mover_k) tk[sl].store(L, L + 2 * kAttnBlock * LR);
-      else tk[sl].store(L + kAttnBlock * LR, nullptr);
-    } else {
-      tk[sl].store(L, L + 2 * kAttnBlock * LR);
-      tv[sl].store(L + kAttnBlock * LR, nullptr);
-    }
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  load_block(0, S0());
-  if (nkb > 1) load_block(kAttnBlock, S1());
-  stage_block(0, S0());
-  if (nkb > 2) load_block(2 * kAttnBlock, S0());
-  // block kb (odd_c: kb % 2, a compile-time constant): it is staged in stage kb % 2, and block
-  // kb - 1's reads of the other stage are done, so block kb + 1 (register set (kb + 1) % 2) goes
-  // there while block kb is multiplied; that set then takes block kb + 3
+  issue(0, kr0, vr0, kt0);
+  // block kb (odd_c: kb % 2): this wave's loads of it have landed and its reads of block kb - 1
+  // are done; after the barrier everyone's are, so block kb + 1 goes into the other stage while
+  // block kb is multiplied
   auto kblock = [&](int kb, auto odd_c) {
     constexpr int odd = decltype(odd_c)::value;
-    using Next = std::integral_constant<int, 1 - odd>;
+    const unsigned char* kc = odd ? kr1 : kr0;
+    const unsigned char* vc = odd ? vr1 : vr0;
+    const unsigned char* tc = odd ? kt1 : kt0;
     const int r0 = kb * kAttnBlock;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    if (kb + 1 < nkb) stage_block(1 - odd, Next());
-    if (kb + 3 < nkb) load_block(r0 + 3 * kAttnBlock, Next());
-    const f16 *kr = lds + odd * STAGE, *vr = kr + kAttnBlock * LR, *ktr = kr + 2 * kAttnBlock * LR;
+    if (kb + 1 < nkb) {
+      if constexpr (odd) issue(kb + 1, kr0, vr0, kt0);
+      else issue(kb + 1, kr1, vr1, kt1);
+    }
     f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
     for (int s = 0; s < K16; ++s) {
-      const int ro = (32 * kh + l32) * LR + 8 * swz_chunk(32 * kh + l32, 2 * s + hi);
-      const f16x8 ak = *reinterpret_cast<const f16x8*>(kr + ro);
-      const f16x8 av = *reinterpret_cast<const f16x8*>(vr + ro);
+      const int r = 32 * kh + l32;
+      const int ro = r * RB + 16 * ((2 * s + hi) ^ (r % CPR));
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kc + ro);
+      const f16x8 av = *reinterpret_cast<const f16x8*>(vc + ro);
       sc = mfma32(ak, qf[s], sc);
       dp = mfma32(av, df[s], dp);
     }
@@ -449,30 +506,37 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         // A: K^T rows 32 fb + l % 32, keys 32 kh + 16 hh + 8 (j / 4) + 4 (l / 32) + j % 4
-        const f16* pa = ktr + (32 * fb + l32) * LT + 32 * kh + 16 * hh + 4 * hi;
-        const f16x4 a0 = *reinterpret_cast<const f16x4*>(pa), a1 = *reinterpret_cast<const f16x4*>(pa + 8);
+        const int f = 32 * fb + l32, sw = (f >> 1) & 7, c0 = 4 * kh + 2 * hh;
+        const f16x4 a0 = *reinterpret_cast<const f16x4*>(tc + f * 128 + 16 * (c0 ^ sw) + 8 * hi);
+        const f16x4 a1 = *reinterpret_cast<const f16x4*>(tc + f * 128 + 16 * ((c0 + 1) ^ sw) + 8 * hi);
         dqt[fb] = mfma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, dsb[hh], dqt[fb]);
       }
   };
   int kb = 0;
   for (; kb + 1 < nkb; kb += 2) {
-    kblock(kb, S0());
-    kblock(kb + 1, S1());
+    kblock(kb, std::integral_constant<int, 0>());
+    kblock(kb + 1, std::integral_constant<int, 1>());
   }
-  if (kb < nkb) kblock(kb, S0());
+  if (kb < nkb) kblock(kb, std::integral_constant<int, 0>());
+  // the key halves' exchange, in the row tiles (4 KB per wave and feature block)
+  constexpr int PER = TILE / 4096;
+  static_assert(NQG * FB <= 4 * PER, "the exchange must fit in the row tiles");
+  auto xslot = [&](int i) -> f32x16* {
+    const int a = i / PER;
+    unsigned char* p = a == 0 ? kr0 : a == 1 ? kr1 : a == 2 ? vr0 : vr1;
+    return reinterpret_cast<f32x16*>(p + (i % PER) * 4096);
+  };
   __syncthreads();
-  f32x16* xs = reinterpret_cast<f32x16*>(lds) + (size_t)qh * FB * 64;
-  static_assert(NQG * FB * 64 * 64 <= (int)sizeof(lds), "the exchange must fit in the staging tiles");
   if (kh) {
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) xs[fb * 64 + lane] = dqt[fb];
+    for (int fb = 0; fb < FB; ++fb) xslot(qh * FB + fb)[lane] = dqt[fb];
   }
   __syncthreads();
   // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of query qi
   if (!kh && qi < T) {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
-      const f32x16 x = dqt[fb] + xs[fb * 64 + lane];
+      const f32x16 x = dqt[fb] + xslot(qh * FB + fb)[lane];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi) =
@@ -1013,10 +1077,14 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
   const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
   hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(nkb, BH), dim3(64 * kDkdvWaves), 0, stream, q, k, v,
                      doh, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
+  f16* v16 = static_cast<f16*>(a.v16);
+  f16* kt16 = static_cast<f16*>(a.kt16);
+  hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, k, v, v16, kt16, a.T,
+                     a.H, a.tp);
   constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
   const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
-  hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(nqb, BH), dim3(128 * kDqGroups), 0, stream, q, k, v, doh,
-                     a.lse, a.dvec, a.tok.dq, a.T, a.H, a.scale, a.scale_log2);
+  hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(nqb, BH), dim3(128 * kDqGroups), 0, stream, q, k, v16,
+                     kt16, doh, a.lse, a.dvec, a.tok.dq, a.T, a.H, a.tp, a.scale, a.scale_log2);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
   hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(nch * BH), dim3(512), 0, stream, a.tok);
   hipLaunchKernelGGL(arl2_bwd_gsum_kernel, dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, stream, a.tok.part, a.gr,
@@ -1056,6 +1124,8 @@ hipError_t launch_bwd_fill(float* dst, const float* src, size_t n, hipStream_t s
   if (blocks > 0) hipLaunchKernelGGL(arl2_bwd_fill_kernel, dim3(blocks), dim3(256), 0, stream, dst, src, n4);
   return hipGetLastError();
 }
+
+int bwd_key_pitch(int T) { return (T + kAttnBlock - 1) / kAttnBlock * kAttnBlock; }
 
 hipError_t launch_bwd_pass(int d, const BwdPassArgs& a, hipStream_t stream) {
   switch (d) {

@@ -216,10 +216,14 @@ struct BwdPassArgs {
   float* dvec;            // workspace: dO . O per row, [B][H][T]
   float* gr;              // sum over the frame's passes of Q^T dO, [B][H][d][d]
   bool gr_first;          // first pass of the frame: gr is overwritten
+  void* v16;              // workspace: v in fp16, [B][T][H][d]
+  void* kt16;             // workspace: k^T in fp16, [B][H][d][tp] (keys past T zero)
+  int tp;                 // T rounded up to whole 64-key blocks
   int B, H, T;
   float scale, scale_log2;
 };
 hipError_t launch_bwd_pass(int d, const BwdPassArgs& a, hipStream_t stream);
+int bwd_key_pitch(int T);  // tp: T rounded up to a multiple of 64
 
 struct BwdFragJobs {
   struct Job {
