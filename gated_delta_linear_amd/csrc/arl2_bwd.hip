@@ -44,8 +44,6 @@ template <int D>
 struct BwdShape {
   static constexpr int KS = D / 32;          // 32-deep k-steps over features
   static constexpr int NB = D / 16;          // 16-wide blocks over features
-  static constexpr int LR = D + 8;           // bf16 row pitch of staged row-major tiles
-  static constexpr int LT = kAttnBlock + 8;  // bf16 row pitch of staged transposed tiles
   static constexpr int LF = D + 4;           // fp32 row pitch of the token kernels' row buffers
   static constexpr int BPW = NB * NB / 8;    // 16x16 blocks of a d x d sum per wave (8 waves)
 };
@@ -138,239 +136,8 @@ __device__ __forceinline__ f16x8 load_f16x8(const T* p) {
   else return to_f16(ld_bf16x8(p));
 }
 
-// Row-major staged tiles keep 16-byte chunk c of row r at chunk c ^ ((r >> 4) & 3): with the
-// 272-byte row pitch (4 banks per row), the 16 lanes of a staging store (rows 4 apart) and the 16
-// lanes of a fragment read (16 consecutive rows) then both land on 16 distinct 4-bank groups.
-__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 4) & 3); }
-
-// One 4-row x 8-feature block of a 64-row tile of a [.][T][H][D] bf16 or fp16 tensor, staged
-// through registers into LDS as fp16: row-major (pitch LR) and, when tr is not null, transposed
-// (pitch LT: tr[f][r]).  Rows past T are zeros.  Block i of a tile is (row group i % 16, feature
-// chunk i / 16): the 16 lanes of a group take the 16 row groups of one feature chunk, so that every
-// transposed write instruction fills whole 128-byte rows of the tile.
-template <int D>
-struct TileBlock {
-  uint4 raw[4];  // the rows' bits as loaded (bf16 or fp16): converted only when stored, so that a
-                 // load issued before the current block's products is not waited for until then
-  int rg, cc;
-  bool on, from_bf16;
-  __device__ __forceinline__ void init(int i, bool bf) {
-    on = i >= 0 && i < 16 * (D / 8);
-    rg = i % 16;
-    cc = i / 16;
-    from_bf16 = bf;
-  }
-  __device__ __forceinline__ void load(const void* __restrict__ src, int64_t base, int64_t rs, int r0, int T) {
-    const uint16_t* p = static_cast<const uint16_t*>(src);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * rg + e;
-      raw[e] = on && r < T ? *reinterpret_cast<const uint4*>(p + base + (int64_t)r * rs + 8 * cc) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(f16* rowm, f16* tr) const {
-    if (!on) return;
-    using Sh = BwdShape<D>;
-    f16x8 x[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = from_bf16 ? to_f16(__builtin_bit_cast(bf16x8, raw[e])) : __builtin_bit_cast(f16x8, raw[e]);
-      *reinterpret_cast<f16x8*>(rowm + (4 * rg + e) * Sh::LR + 8 * swz_chunk(4 * rg + e, cc)) = x[e];
-    }
-    if (tr) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        f16x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = x[e][c];
-        *reinterpret_cast<f16x4*>(tr + (8 * cc + c) * Sh::LT + 4 * rg) = t;
-      }
-    }
-  }
-};
-
-// A fragment of a contraction over 32 staged rows (k-step s2 of a 64-row block) from a transposed
-// tile, in the row order of two stacked 16x16 C blocks: element j <-> row 32 s2 + 16 (j / 4) +
-// 4 g + j % 4, feature row f of the tile.
-template <int D>
-__device__ __forceinline__ f16x8 tr_frag(const f16* tr, int f, int s2, int g) {
-  const f16* p = tr + f * BwdShape<D>::LT + 32 * s2 + 4 * g;
-  const f16x4 a = *reinterpret_cast<const f16x4*>(p), b = *reinterpret_cast<const f16x4*>(p + 16);
-  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
 // exp2 on the transcendental unit (arguments are at most about 0 here: lse bounds every score)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// dK, dV of 16 NW keys of one (stream, head).  NW waves, wave w owning keys 16 w .. 16 w + 15; every
-// key block reads the head's whole Q and dO, so wider work-groups cut that stream (and the staging
-// per wave) in proportion.  Per query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l,
-// register i <-> query 16 m + 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS =
-// P (dP - Dv); then dV^T += dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from
-// the C registers.  Block qb + 1 is staged into the other LDS buffer while block qb is
-// multiplied, and block qb + 2's Q and dO rows are loaded into registers meanwhile: with
-// 64 NW >= 2 x the tile's blocks each thread moves one block of one tile, otherwise one block of
-// each.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
-    const float* __restrict__ lse, const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv,
-    int T, int H, float scale, float scale_log2) {
-  using Sh = BwdShape<D>;
-  constexpr int KS = Sh::KS, NB = Sh::NB, LR = Sh::LR;
-  constexpr int TILE = kAttnBlock * LR + D * Sh::LT;  // f16 elements of one staged tile (rows + transposed)
-  constexpr int NBLK = 16 * (D / 8);                  // 4-row x 8-feature blocks of one tile
-  constexpr bool SPLIT = 64 * NW >= 2 * NBLK;         // one block of one tile per thread
-  // two buffers of (Q rows, Q^T, dO rows, dO^T): block qb is read from buffer qb % 2 while block
-  // qb + 1 is staged into the other one
-  __shared__ __align__(16) f16 lds[2][2 * TILE];
-  __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
-  const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int key = blockIdx.x * (16 * NW) + 16 * wave + l16;
-  f16x8 kf[KS], vf[KS];  // B operands: K^T, V^T columns of this wave's keys
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    kf[s] = key < T ? load_f16x8(k + base + (int64_t)key * rs + 32 * s + 8 * g) : f16x8{};
-    vf[s] = key < T ? load_f16x8(v + base + (int64_t)key * rs + 32 * s + 8 * g) : f16x8{};
-  }
-  f32x4 dkt[NB], dvt[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) dkt[n] = dvt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // SPLIT: threads [0, NBLK) move Q blocks and [NBLK, 2 NBLK) dO blocks (whole waves either way),
-  // through one register block; otherwise every thread moves block tid of both tiles.
-  const bool mover_q = !SPLIT || tid < NBLK;
-  TileBlock<D> tq, to;
-  if constexpr (SPLIT) {
-    tq.init(mover_q ? tid : tid - NBLK, mover_q);
-  } else {
-    tq.init(tid, true);
-    to.init(tid, false);
-  }
-  float lse_r = 0.f, dv_r = 0.f;
-  auto load_block = [&](int r0) {
-    if constexpr (SPLIT) {
-      if (mover_q) tq.load(q, base, rs, r0, T);
-      else tq.load(doh, base, rs, r0, T);
-    } else {
-      tq.load(q, base, rs, r0, T);
-      to.load(doh, base, rs, r0, T);
-    }
-    if (tid < kAttnBlock) {
-      const int r = r0 + tid;
-      lse_r = r < T ? lse[(int64_t)bh * T + r] : INFINITY;  // rows past T get P = 0
-      dv_r = r < T ? dvec[(int64_t)bh * T + r] : 0.f;
-    }
-  };
-  const int nqb = (T + kAttnBlock - 1) / kAttnBlock;
-  auto stage_block = [&](int buf) {
-    f16* L = lds[buf];
-    if constexpr (SPLIT) {
-      if (mover_q) tq.store(L, L + kAttnBlock * LR);
-      else tq.store(L + TILE, L + TILE + kAttnBlock * LR);
-    } else {
-      tq.store(L, L + kAttnBlock * LR);
-      to.store(L + TILE, L + TILE + kAttnBlock * LR);
-    }
-    if (tid < kAttnBlock) {
-      lse_s[buf][tid] = lse_r;
-      dv_s[buf][tid] = dv_r;
-    }
-  };
-  load_block(0);
-  stage_block(0);
-  if (nqb > 1) load_block(kAttnBlock);
-  for (int qb = 0; qb < nqb; ++qb) {
-    // block qb is staged (everyone's stores are done) and block qb - 1's reads of the other
-    // buffer are done: block qb + 1 goes there while block qb is multiplied
-    __syncthreads();
-    const int cur = qb & 1;
-    if (qb + 1 < nqb) stage_block(cur ^ 1);
-    if (qb + 2 < nqb) load_block((qb + 2) * kAttnBlock);
-    const f16 *qr = lds[cur], *qtr = lds[cur] + kAttnBlock * LR, *dor = lds[cur] + TILE,
-              *dotr = lds[cur] + TILE + kAttnBlock * LR;
-    const float* lse_c = lse_s[cur];
-    const float* dv_c = dv_s[cur];
-    // per 32-query half s2: S and dP of its two 16-query blocks, then its share of dV^T, dK^T
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f16x8 pb, dsb;
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int m = 2 * s2 + mm;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int ro = (16 * m + l16) * LR + 8 * swz_chunk(16 * m + l16, 4 * s + g);
-          const f16x8 aq = *reinterpret_cast<const f16x8*>(qr + ro);
-          const f16x8 ao = *reinterpret_cast<const f16x8*>(dor + ro);
-          sc = mfma16h(aq, kf[s], sc);
-          dp = mfma16h(ao, vf[s], dp);
-        }
-        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_c + 16 * m + 4 * g);
-        const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_c + 16 * m + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
-          pb[4 * mm + i] = (f16)p;
-          dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd[i]));
-        }
-      }
-#pragma unroll
-      for (int mb = 0; mb < NB; ++mb) {
-        dvt[mb] = mfma16h(tr_frag<D>(dotr, 16 * mb + l16, s2, g), pb, dvt[mb]);
-        dkt[mb] = mfma16h(tr_frag<D>(qtr, 16 * mb + l16, s2, g), dsb, dkt[mb]);
-      }
-    }
-  }
-  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 w + l % 16
-  if (key < T) {
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-      const int64_t o = base + (int64_t)key * rs + 16 * mb + 4 * g;
-      *reinterpret_cast<f32x4*>(dk + o) = dkt[mb] * scale;
-      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb];
-    }
-  }
-}
-
-// V and K^T of a pass in fp16 for the dQ kernel's direct-to-LDS staging: v16 in the [B][T][H][d]
-// layout of v (rows past T not written); kt16 [B][H][d][tp], each head's keys as rows of 64-key
-// blocks per feature (keys past T zero).  One work-group per (stream, head, 64-key block); thread
-// j moves rows 4 (j % 16) .. + 3 of 8-feature chunk j / 16, K transposed through LDS.
-template <int D>
-__global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
-                                                           f16* __restrict__ v16, f16* __restrict__ kt16, int T, int H,
-                                                           int tp) {
-  constexpr int CPR = D / 8, TPITCH = kAttnBlock + 8;  // chunks per row; transposing tile's pitch (f16)
-  __shared__ __align__(16) f16 tr[D * TPITCH];
-  const int tid = threadIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, k0 = blockIdx.x * kAttnBlock;
-  const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  for (int j = tid; j < 16 * CPR; j += 256) {
-    const int rg = j % 16, cc = j / 16;
-    f16x8 kx[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = k0 + 4 * rg + e;
-      kx[e] = f16x8{};
-      if (key < T) {
-        const int64_t o = base + (int64_t)key * rs + 8 * cc;
-        kx[e] = to_f16(ld_bf16x8(k + o));
-        *reinterpret_cast<f16x8*>(v16 + o) = to_f16(ld_bf16x8(v + o));
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      *reinterpret_cast<f16x4*>(tr + (8 * cc + c) * TPITCH + 4 * rg) = f16x4{kx[0][c], kx[1][c], kx[2][c], kx[3][c]};
-  }
-  __syncthreads();
-  for (int j = tid; j < D * (kAttnBlock / 8); j += 256) {
-    const int f = j / (kAttnBlock / 8), c = j % (kAttnBlock / 8);
-    *reinterpret_cast<f16x8*>(kt16 + ((int64_t)bh * D + f) * tp + k0 + 8 * c) =
-        *reinterpret_cast<const f16x8*>(tr + f * TPITCH + 8 * c);
-  }
-}
 
 typedef __attribute__((address_space(3))) void lds_void_b;
 
@@ -388,6 +155,222 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc16(const f16* base, i
   const bool any = left > 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(any ? base + start : base), (short)0,
                                            any ? (int)(left * 2) : 0, 0x00020000);
+}
+
+// dK, dV of 16 NW keys of one (stream, head).  NW waves, wave w owning keys 16 w .. 16 w + 15; every
+// key block reads the head's whole Q and dO, so wider work-groups cut that stream in proportion.
+// Per query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l, register i <-> query
+// 16 m + 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS = P (dP - Dv); then
+// dV^T += dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from the C registers.
+// Staging: each 64-query block's Q rows (bf16, as given: S = Q K^T runs on the bf16 inputs), dO
+// rows (the fp16 dO) and the transposed fp16 copies Q^T and dO^T (64 queries per feature row)
+// come straight into LDS with direct-to-LDS loads, in two stages: block qb + 1's loads fly while
+// block qb is multiplied.  Row tiles keep 16-byte chunk c of query row r at c ^ (r mod d/8), the
+// transposed tiles 8-query chunk c of feature row f at c ^ ((f >> 1) & 7): every load brings
+// whole rows and the fragment reads hit distinct banks.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
+    const f16* __restrict__ qt16, const f16* __restrict__ dot16, const float* __restrict__ lse,
+    const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv, int T, int H, int tp, float scale,
+    float scale_log2) {
+  using Sh = BwdShape<D>;
+  constexpr int KS = Sh::KS, NB = Sh::NB;
+  constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per query row, 16-byte chunks per row, rows per 1-KB load
+  constexpr int TILE = kAttnBlock * RB;                    // bytes of a 64-row tile; a transposed tile (d rows of 128 bytes) too
+  constexpr int LD = TILE / 1024, LPT = LD / NW;           // 1-KB loads per tile, of them per wave
+  static_assert(LD % NW == 0, "every wave issues the same number of loads per tile");
+  // separate arrays per stage and tile, addressed with compile-time stage numbers
+  __shared__ __align__(16) unsigned char qr0[TILE], qr1[TILE], or0[TILE], or1[TILE], qt0[TILE], qt1[TILE],
+      ot0[TILE], ot1[TILE];
+  __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
+  const int key = blockIdx.x * (16 * NW) + 16 * wave + l16;
+  bf16x8 kf[KS];  // B operands: K^T columns of this wave's keys (bf16, as given)
+  f16x8 vf[KS];   // V^T columns in fp16
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = key < T ? ld_bf16x8(k + base + (int64_t)key * rs + 32 * s + 8 * g) : zero_bf16x8();
+    vf[s] = key < T ? load_f16x8(v + base + (int64_t)key * rs + 32 * s + 8 * g) : f16x8{};
+  }
+  f32x4 dkt[NB], dvt[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) dkt[n] = dvt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Loads of block qb (a wave's loads i = wave + NW m of each tile; see the dQ kernel's).
+  auto issue = [&](int qb, unsigned char* qd, unsigned char* od, unsigned char* qtd, unsigned char* otd) {
+    const int r0 = qb * kAttnBlock;
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc16(reinterpret_cast<const f16*>(q) + base, T, rs, D, r0);  // bf16 bits
+    const __amdgpu_buffer_rsrc_t ro = rows_rsrc16(doh + base, T, rs, D, r0);
+    const int64_t toff = (int64_t)bh * D * tp + r0;
+    const uint64_t qa = reinterpret_cast<uint64_t>(qt16 + toff), oa = reinterpret_cast<uint64_t>(dot16 + toff);
+    const int tbytes = __builtin_amdgcn_readfirstlane(D * tp * 2 - r0 * 2);
+    auto uni = [](uint64_t a) {  // wave-uniform address, so that the descriptor lives in scalar registers
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+      return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    };
+    const __amdgpu_buffer_rsrc_t rqt = __builtin_amdgcn_make_buffer_rsrc(uni(qa), (short)0, tbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rot = __builtin_amdgcn_make_buffer_rsrc(uni(oa), (short)0, tbytes, 0x00020000);
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int i = wave + NW * m, row = RPI * i + lane / CPR;
+      const int vo = (lane / CPR) * (int)(rs * 2) + 16 * ((lane % CPR) ^ (row % CPR));
+      dma16b(rq, qd + i * 1024, vo, RPI * i * (int)(rs * 2));
+      dma16b(ro, od + i * 1024, vo, RPI * i * (int)(rs * 2));
+    }
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int i = wave + NW * m, row = 8 * i + lane / 8;
+      const int vo = (lane / 8) * tp * 2 + 16 * ((lane % 8) ^ ((row >> 1) & 7));
+      dma16b(rqt, qtd + i * 1024, vo, 8 * i * tp * 2);
+      dma16b(rot, otd + i * 1024, vo, 8 * i * tp * 2);
+    }
+  };
+  // lse and Dv of a block's rows: loaded into registers (threads < 64) one block ahead of their
+  // store into LDS, and before that block's tile loads, so that waiting for them waits for nothing
+  // else
+  float lse_r = 0.f, dv_r = 0.f;
+  auto load_ld = [&](int qb) {
+    if (tid < kAttnBlock) {
+      const int r = qb * kAttnBlock + tid;
+      lse_r = r < T ? lse[(int64_t)bh * T + r] : INFINITY;  // rows past T get P = 0
+      dv_r = r < T ? dvec[(int64_t)bh * T + r] : 0.f;
+    }
+  };
+  auto store_ld = [&](int buf) {
+    if (tid < kAttnBlock) {
+      lse_s[buf][tid] = lse_r;
+      dv_s[buf][tid] = dv_r;
+    }
+  };
+  const int nqb = (T + kAttnBlock - 1) / kAttnBlock;
+  load_ld(0);
+  store_ld(0);
+  if (nqb > 1) load_ld(1);
+  issue(0, qr0, or0, qt0, ot0);
+  // block qb (odd_c: qb % 2): this wave's loads of it have landed and its reads of block qb - 1
+  // are done; after the barrier everyone's are, so block qb + 1 goes into the other stage while
+  // block qb is multiplied
+  auto qblock = [&](int qb, auto odd_c) {
+    constexpr int odd = decltype(odd_c)::value;
+    const unsigned char* qc = odd ? qr1 : qr0;
+    const unsigned char* oc = odd ? or1 : or0;
+    const unsigned char* qtc = odd ? qt1 : qt0;
+    const unsigned char* otc = odd ? ot1 : ot0;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    if (qb + 1 < nqb) {
+      store_ld(1 - odd);
+      if (qb + 2 < nqb) load_ld(qb + 2);
+      if constexpr (odd) issue(qb + 1, qr0, or0, qt0, ot0);
+      else issue(qb + 1, qr1, or1, qt1, ot1);
+    }
+    const float* lse_c = lse_s[odd];
+    const float* dv_c = dv_s[odd];
+    // per 32-query half s2: S and dP of its two 16-query blocks, then its share of dV^T, dK^T
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      f16x8 pb, dsb;
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int m = 2 * s2 + mm;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int r = 16 * m + l16;
+          const int ro = r * RB + 16 * ((4 * s + g) ^ (r % CPR));
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qc + ro);
+          const f16x8 ao = *reinterpret_cast<const f16x8*>(oc + ro);
+          sc = mfma16(aq, kf[s], sc);
+          dp = mfma16h(ao, vf[s], dp);
+        }
+        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_c + 16 * m + 4 * g);
+        const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_c + 16 * m + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
+          pb[4 * mm + i] = (f16)p;
+          dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd[i]));
+        }
+      }
+      // A fragments of the transposed tiles: feature row f = 16 mb + l % 16, queries
+      // 32 s2 + 16 (j / 4) + 4 (l / 16) + j % 4 (the stacked-C row order of P and dS)
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        const int f = 16 * mb + l16, sw = (f >> 1) & 7, c0 = 4 * s2 + (g >> 1), o8 = 8 * (g & 1);
+        const int t0 = f * 128 + 16 * (c0 ^ sw) + o8, t1 = f * 128 + 16 * ((c0 + 2) ^ sw) + o8;
+        const f16x4 a0 = *reinterpret_cast<const f16x4*>(otc + t0), a1 = *reinterpret_cast<const f16x4*>(otc + t1);
+        const f16x4 b0 = *reinterpret_cast<const f16x4*>(qtc + t0), b1 = *reinterpret_cast<const f16x4*>(qtc + t1);
+        dvt[mb] = mfma16h(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, pb, dvt[mb]);
+        dkt[mb] = mfma16h(f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, dsb, dkt[mb]);
+      }
+    }
+  };
+  int qb = 0;
+  for (; qb + 1 < nqb; qb += 2) {
+    qblock(qb, std::integral_constant<int, 0>());
+    qblock(qb + 1, std::integral_constant<int, 1>());
+  }
+  if (qb < nqb) qblock(qb, std::integral_constant<int, 0>());
+  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 w + l % 16
+  if (key < T) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      const int64_t o = base + (int64_t)key * rs + 16 * mb + 4 * g;
+      *reinterpret_cast<f32x4*>(dk + o) = dkt[mb] * scale;
+      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb];
+    }
+  }
+}
+
+// A pass's operands in fp16 for the attention backward's direct-to-LDS staging: v16 in the
+// [B][T][H][d] layout of v (rows past T not written), and the transposes kt16, qt16, dot16
+// [B][H][d][tp] of k, q and the fp16 dO: each head's features as rows of its tokens, 64-token
+// blocks (tokens past T zero).  One work-group per (stream, head, 64-token block); thread j moves
+// rows 4 (j % 16) .. + 3 of 8-feature chunk j / 16, transposing through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                           const bf16* __restrict__ v, const f16* __restrict__ doh,
+                                                           f16* __restrict__ v16, f16* __restrict__ kt16,
+                                                           f16* __restrict__ qt16, f16* __restrict__ dot16, int T,
+                                                           int H, int tp) {
+  constexpr int CPR = D / 8, TPITCH = kAttnBlock + 8;  // chunks per row; transposing tiles' pitch (f16)
+  __shared__ __align__(16) f16 tr[3][D * TPITCH];     // K^T, Q^T, dO^T of the block
+  const int tid = threadIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, k0 = blockIdx.x * kAttnBlock;
+  const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
+  for (int j = tid; j < 16 * CPR; j += 256) {
+    const int rg = j % 16, cc = j / 16;
+    f16x8 x[3][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = k0 + 4 * rg + e;
+      x[0][e] = x[1][e] = x[2][e] = f16x8{};
+      if (t < T) {
+        const int64_t o = base + (int64_t)t * rs + 8 * cc;
+        x[0][e] = to_f16(ld_bf16x8(k + o));
+        x[1][e] = to_f16(ld_bf16x8(q + o));
+        x[2][e] = ld_f16x8(doh + o);
+        *reinterpret_cast<f16x8*>(v16 + o) = to_f16(ld_bf16x8(v + o));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<f16x4*>(tr[m] + (8 * cc + c) * TPITCH + 4 * rg) =
+            f16x4{x[m][0][c], x[m][1][c], x[m][2][c], x[m][3][c]};
+  }
+  __syncthreads();
+  f16* const dst[3] = {kt16, qt16, dot16};
+  for (int j = tid; j < 3 * D * (kAttnBlock / 8); j += 256) {
+    const int m = j / (D * (kAttnBlock / 8)), jj = j % (D * (kAttnBlock / 8));
+    const int f = jj / (kAttnBlock / 8), c = jj % (kAttnBlock / 8);
+    *reinterpret_cast<f16x8*>(dst[m] + ((int64_t)bh * D + f) * tp + k0 + 8 * c) =
+        *reinterpret_cast<const f16x8*>(tr[m] + f * TPITCH + 8 * c);
+  }
 }
 
 // dQ of 32 NQG queries of one (stream, head), with 32x32x16 MFMAs.  2 NQG waves: wave w owns
@@ -1073,14 +1056,16 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
   const bf16* k = static_cast<const bf16*>(a.tok.k);
   const bf16* v = static_cast<const bf16*>(a.tok.v);
   const f16* doh = static_cast<const f16*>(a.do_h);
+  f16* v16 = static_cast<f16*>(a.v16);
+  f16* kt16 = static_cast<f16*>(a.kt16);
+  f16* qt16 = static_cast<f16*>(a.qt16);
+  f16* dot16 = static_cast<f16*>(a.dot16);
+  hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, q, k, v, doh, v16, kt16,
+                     qt16, dot16, a.T, a.H, a.tp);
   constexpr int kDkdvWaves = 8;
   const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
   hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(nkb, BH), dim3(64 * kDkdvWaves), 0, stream, q, k, v,
-                     doh, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, a.scale, a.scale_log2);
-  f16* v16 = static_cast<f16*>(a.v16);
-  f16* kt16 = static_cast<f16*>(a.kt16);
-  hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, k, v, v16, kt16, a.T,
-                     a.H, a.tp);
+                     doh, qt16, dot16, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, a.tp, a.scale, a.scale_log2);
   constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
   const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
   hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(nqb, BH), dim3(128 * kDqGroups), 0, stream, q, k, v16,

@@ -29,8 +29,10 @@ struct arl2_bwd {
   float* lse = nullptr;        // its rows' log-sum-exp, [B][H][T]
   float* dvec = nullptr;       // dO . O per row, [B][H][T]
   void* do_h = nullptr;        // d_out in fp16
-  void* v16 = nullptr;         // the pass's v in fp16, [B][T][H][d], and k^T in fp16, [B][H][d][tp]
+  void* v16 = nullptr;         // the pass's v in fp16, [B][T][H][d]; k^T, q^T, dO^T in fp16, [B][H][d][tp]
   void* kt16 = nullptr;
+  void* qt16 = nullptr;
+  void* dot16 = nullptr;
   float* ds[2] = {nullptr, nullptr};  // dL/dS, [B][H][d][d], ping-pong
   int cur = 0;
   float* gr = nullptr;         // sum over the frame's passes of Q^T dO
@@ -180,7 +182,7 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
   const size_t hmat = align_up(H * d * d * 4), hmatbf = align_up(H * d * d * 2);
   const size_t rpart = align_up(BH * g->nch * d * d * 4), wpart = align_up(BH * g->nch * 3 * d * d * 4);
   const size_t kt_bf = align_up(BH * d * (size_t)arl2::bwd_key_pitch(c.tokens_per_frame) * 2);
-  g->bytes = tok_f32 + 2 * row_f32 + 2 * tok_bf + kt_bf + 3 * mat + rpart + wpart + 8 * matbf + 6 * hmatbf + 3 * hmat;
+  g->bytes = tok_f32 + 2 * row_f32 + 2 * tok_bf + 3 * kt_bf + 3 * mat + rpart + wpart + 8 * matbf + 6 * hmatbf + 3 * hmat;
   if ((e = hipMalloc(&g->slab, g->bytes)) != hipSuccess) {
     (void)hipGetLastError();
     const size_t want = g->bytes;
@@ -194,6 +196,8 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
   g->do_h = p; p += tok_bf;
   g->v16 = p; p += tok_bf;
   g->kt16 = p; p += kt_bf;
+  g->qt16 = p; p += kt_bf;
+  g->dot16 = p; p += kt_bf;
   g->ds[0] = reinterpret_cast<float*>(p); p += mat;
   g->ds[1] = reinterpret_cast<float*>(p); p += mat;
   g->gr = reinterpret_cast<float*>(p); p += mat;
@@ -291,6 +295,8 @@ arl2_status arl2_bwd_pass(arl2_bwd* g, const void* q, const void* k, const void*
   a.do_h = g->do_h;
   a.v16 = g->v16;
   a.kt16 = g->kt16;
+  a.qt16 = g->qt16;
+  a.dot16 = g->dot16;
   a.tp = arl2::bwd_key_pitch(g->cfg.tokens_per_frame);
   a.dvec = g->dvec;
   a.gr = g->gr;

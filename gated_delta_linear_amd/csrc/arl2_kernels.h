@@ -217,7 +217,9 @@ struct BwdPassArgs {
   float* gr;              // sum over the frame's passes of Q^T dO, [B][H][d][d]
   bool gr_first;          // first pass of the frame: gr is overwritten
   void* v16;              // workspace: v in fp16, [B][T][H][d]
-  void* kt16;             // workspace: k^T in fp16, [B][H][d][tp] (keys past T zero)
+  void* kt16;             // workspace: k^T, q^T, dO^T in fp16, [B][H][d][tp] (tokens past T zero)
+  void* qt16;
+  void* dot16;
   int tp;                 // T rounded up to whole 64-key blocks
   int B, H, T;
   float scale, scale_log2;
