@@ -20,10 +20,14 @@
 // reproducible), 8 waves per work-group: dK, dV per 128-key block, 16 keys per wave (the keys'
 // fragments stay in registers, 64-query blocks stream through LDS), and dQ per 128-query block,
 // four 32-query groups times two key halves (64-key blocks stream through LDS); the scores are
-// recomputed in each.  Both stage their streamed blocks in two LDS buffers (block b + 1 is
-// written while block b is multiplied, one barrier per block).  Their products run in fp16
-// with fp32 accumulation: the bf16 inputs convert exactly, and P, dS and dO round with a
-// relative step of 2^-11.  The
+// recomputed in each.  Every streamed tile reaches LDS by direct-to-LDS buffer loads, two
+// stages deep (block b + 1 is in flight while block b is multiplied, one barrier per block),
+// with rows chunk-swizzled so that the fragment reads hit distinct banks; no thread converts or
+// transposes anything on the way.  The operands those loads need in another type or layout (V
+// in fp16, and K^T, Q^T, dO^T in fp16) are written once per pass by a conversion kernel.  The
+// score products S = Q K^T run in bf16 on the inputs as given; the others (dP = dO V^T, dV,
+// dK, dQ) in fp16, where P, dS and dO round with a relative step of 2^-11; all accumulate in
+// fp32.  The
 // token kernels (inter read, state write) work per 128-token chunk with 16x16x32 MFMAs on
 // split-bf16 operands (hi + lo, three products per term), so that their d x d products keep
 // about fp32 accuracy as the forward's state write does; their sums over tokens leave the chunk
@@ -127,8 +131,9 @@ __global__ __launch_bounds__(256) void arl2_bwd_rowdot_kernel(const float* __res
 }
 
 // --- attention backward ---------------------------------------------------------------------
-// All products in fp16 with fp32 accumulation (P, dS and dO round with a relative step of 2^-11,
-// four times finer than bf16; the bf16 inputs convert exactly), at the bf16 MFMA rate.
+// S = Q K^T in bf16 on the inputs as given; every other product in fp16 (P, dS and dO round with
+// a relative step of 2^-11, four times finer than bf16; the bf16 inputs convert exactly when
+// they lie in fp16's normal range); all with fp32 accumulation, at the bf16 MFMA rate.
 
 template <typename T>
 __device__ __forceinline__ f16x8 load_f16x8(const T* p) {
