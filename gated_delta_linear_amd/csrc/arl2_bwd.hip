@@ -44,6 +44,17 @@ namespace {
 constexpr int kAttnBlock = 64;  // queries or keys per work-group of the attention backward
 constexpr int kTokChunk = 128;  // tokens per work-group of the token kernels (8 waves x 16)
 
+// XCD-aware order of a 1-D grid of 8 ceil(n / 8) work-groups over n items (blocks of rows of
+// one (stream, head) after another): the hardware deals work-group i to XCD i % 8, and item
+// x ceil(n / 8) + j goes to work-group 8 j + x, so each XCD takes a contiguous run of items, one
+// or two heads, and a head's operands fill one or two L2 caches instead of all eight.  Returns
+// -1 for the padding work-groups.
+__device__ __forceinline__ int xcd_item(int n) {
+  const int per = (n + 7) / 8, item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  return item < n ? item : -1;
+}
+inline int xcd_grid(int n) { return 8 * ((n + 7) / 8); }
+
 template <int D>
 struct BwdShape {
   static constexpr int KS = D / 32;          // 32-deep k-steps over features
@@ -177,8 +188,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
     const f16* __restrict__ qt16, const f16* __restrict__ dot16, const float* __restrict__ lse,
-    const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv, int T, int H, int tp, float scale,
-    float scale_log2) {
+    const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv, int T, int H, int BH, int tp,
+    float scale, float scale_log2) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NB = Sh::NB;
   constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per query row, 16-byte chunks per row, rows per 1-KB load
@@ -191,9 +202,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int nkb = (T + 16 * NW - 1) / (16 * NW), item = xcd_item(nkb * BH);
+  if (item < 0) return;
+  const int bh = item / nkb, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int key = blockIdx.x * (16 * NW) + 16 * wave + l16;
+  const int key = (item % nkb) * (16 * NW) + 16 * wave + l16;
   bf16x8 kf[KS];  // B operands: K^T columns of this wave's keys (bf16, as given)
   f16x8 vf[KS];   // V^T columns in fp16
 #pragma unroll
@@ -397,7 +410,8 @@ template <int D, int NQG>
 __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const f16* __restrict__ v16,
     const f16* __restrict__ kt16, const f16* __restrict__ doh, const float* __restrict__ lse,
-    const float* __restrict__ dvec, float* __restrict__ dq, int T, int H, int tp, float scale, float scale_log2) {
+    const float* __restrict__ dvec, float* __restrict__ dq, int T, int H, int BH, int tp, float scale,
+    float scale_log2) {
   constexpr int K16 = D / 16, FB = D / 32, NW = 2 * NQG;
   constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per key row, 16-byte chunks per row, rows per 1-KB load
   constexpr int TILE = kAttnBlock * RB;                    // bytes of a 64-row tile; the K^T tile (d rows of 128 bytes) too
@@ -410,9 +424,11 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qh = wave % NQG, kh = wave / NQG;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int nqb = (T + 32 * NQG - 1) / (32 * NQG), item = xcd_item(nqb * BH);
+  if (item < 0) return;
+  const int bh = item / nqb, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int qi = blockIdx.x * (32 * NQG) + 32 * qh + l32;
+  const int qi = (item % nqb) * (32 * NQG) + 32 * qh + l32;
   // B operands: lane l holds Q (bf16, as given: S^T = K Q^T runs on the bf16 inputs) and dO (fp16)
   // of query qi, features 16 s + 8 (l / 32) ..
   bf16x8 qf[K16];
@@ -628,7 +644,9 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
   __shared__ __align__(16) float dbuf[kTokChunk * LF];  // the chunk's dO rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int T = a.T, H = a.H, nch = (T + kTokChunk - 1) / kTokChunk;
-  const int chunk = blockIdx.x % nch, bh = blockIdx.x / nch, b = bh / H, h = bh % H;
+  const int item = xcd_item(nch * a.B * H);
+  if (item < 0) return;
+  const int chunk = item % nch, bh = item / nch, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D, mat = (int64_t)bh * D * D;
   const int t0 = chunk * kTokChunk, r0 = 16 * wave, ta = t0 + r0 + l16;
   const bf16* st_hi = static_cast<const bf16*>(a.st_hi) + mat;
@@ -714,7 +732,9 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
   __shared__ __align__(16) float bbuf[kTokChunk * LF];  // R rows, later dR rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int T = a.T, H = a.H, nch = (T + kTokChunk - 1) / kTokChunk;
-  const int chunk = blockIdx.x % nch, bh = blockIdx.x / nch, b = bh / H, h = bh % H;
+  const int item = xcd_item(nch * a.B * H);
+  if (item < 0) return;
+  const int chunk = item % nch, bh = item / nch, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D, mat = (int64_t)bh * D * D;
   const int64_t hmat = (int64_t)h * D * D;
   const int t0 = chunk * kTokChunk, r0 = 16 * wave, ta = t0 + r0 + l16;
@@ -1069,14 +1089,15 @@ hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
                      qt16, dot16, a.T, a.H, a.tp);
   constexpr int kDkdvWaves = 8;
   const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
-  hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(nkb, BH), dim3(64 * kDkdvWaves), 0, stream, q, k, v,
-                     doh, qt16, dot16, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, a.tp, a.scale, a.scale_log2);
+  hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(xcd_grid(nkb * BH)), dim3(64 * kDkdvWaves), 0, stream,
+                     q, k, v, doh, qt16, dot16, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, BH, a.tp, a.scale,
+                     a.scale_log2);
   constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
   const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
-  hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(nqb, BH), dim3(128 * kDqGroups), 0, stream, q, k, v16,
-                     kt16, doh, a.lse, a.dvec, a.tok.dq, a.T, a.H, a.tp, a.scale, a.scale_log2);
+  hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(xcd_grid(nqb * BH)), dim3(128 * kDqGroups), 0, stream, q,
+                     k, v16, kt16, doh, a.lse, a.dvec, a.tok.dq, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
-  hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(nch * BH), dim3(512), 0, stream, a.tok);
+  hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(xcd_grid(nch * BH)), dim3(512), 0, stream, a.tok);
   hipLaunchKernelGGL(arl2_bwd_gsum_kernel, dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, stream, a.tok.part, a.gr,
                      D * D, nch, a.gr_first ? 1 : 0);
   return hipGetLastError();
@@ -1091,7 +1112,7 @@ hipError_t launch_bwd_frags_d(const BwdFragJobs& j, int BH, int n_jobs, hipStrea
 template <int D>
 hipError_t launch_bwd_commit_d(const BwdTokArgs& t, const BwdFrameArgs& f, hipStream_t stream) {
   const int nch = (t.T + kTokChunk - 1) / kTokChunk;
-  hipLaunchKernelGGL(arl2_bwd_write_kernel<D>, dim3(nch * t.B * t.H), dim3(512), 0, stream, t);
+  hipLaunchKernelGGL(arl2_bwd_write_kernel<D>, dim3(xcd_grid(nch * t.B * t.H)), dim3(512), 0, stream, t);
   hipLaunchKernelGGL(arl2_bwd_frame_kernel<D>, dim3(D / 16, D / 16, t.H), dim3(256), 0, stream, f);
   return hipGetLastError();
 }
