@@ -543,8 +543,10 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
       const f32x16 x = dqt[fb] + xslot(qh * FB + fb)[lane];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi) =
-            f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
+      {
+        f32x4* o = reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi);
+        *o = *o + f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
+      }
     }
   }
 }
@@ -635,7 +637,8 @@ __device__ __forceinline__ float group16_sum(float x) {
 }
 
 // Inter-frame read of one pass, per (stream, head, 128-token chunk); wave w owns tokens 16 w ..
-// 16 w + 15 of the chunk.  dq += (dO S^T) phi_q^T, and the chunk's partial of Gr = Q^T dO.
+// 16 w + 15 of the chunk.  dq = (dO S^T) phi_q^T (the dQ kernel adds the softmax branch's part
+// later), and the chunk's partial of Gr = Q^T dO.
 template <int D>
 __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) {
   using Sh = BwdShape<D>;
@@ -691,7 +694,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + r0 + 4 * g + i;
-      if (t < T) a.dq[base + (int64_t)t * rs + 16 * nb + l16] += c[i];
+      if (t < T) a.dq[base + (int64_t)t * rs + 16 * nb + l16] = c[i];
     }
     if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
@@ -1072,34 +1075,49 @@ __global__ __launch_bounds__(256) void arl2_bwd_fill_kernel(float* __restrict__ 
 }
 
 template <int D>
-hipError_t launch_bwd_pass_d(const BwdPassArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_stage_d(BwdStage stage, const BwdPassArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
-  const int rows = a.B * a.T * a.H, rpb = 256 / (D / 4);
-  hipLaunchKernelGGL(arl2_bwd_rowdot_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, stream, a.d_out, a.o_sm,
-                     static_cast<f16*>(a.do_h), a.dvec, rows, a.T, a.H);
   const bf16* q = static_cast<const bf16*>(a.tok.q);
   const bf16* k = static_cast<const bf16*>(a.tok.k);
   const bf16* v = static_cast<const bf16*>(a.tok.v);
   const f16* doh = static_cast<const f16*>(a.do_h);
-  f16* v16 = static_cast<f16*>(a.v16);
-  f16* kt16 = static_cast<f16*>(a.kt16);
-  f16* qt16 = static_cast<f16*>(a.qt16);
-  f16* dot16 = static_cast<f16*>(a.dot16);
-  hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, q, k, v, doh, v16, kt16,
-                     qt16, dot16, a.T, a.H, a.tp);
-  constexpr int kDkdvWaves = 8;
-  const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
-  hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(xcd_grid(nkb * BH)), dim3(64 * kDkdvWaves), 0, stream,
-                     q, k, v, doh, qt16, dot16, a.lse, a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, BH, a.tp, a.scale,
-                     a.scale_log2);
-  constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
-  const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
-  hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(xcd_grid(nqb * BH)), dim3(128 * kDqGroups), 0, stream, q,
-                     k, v16, kt16, doh, a.lse, a.dvec, a.tok.dq, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
-  hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(xcd_grid(nch * BH)), dim3(512), 0, stream, a.tok);
-  hipLaunchKernelGGL(arl2_bwd_gsum_kernel, dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, stream, a.tok.part, a.gr,
-                     D * D, nch, a.gr_first ? 1 : 0);
+  switch (stage) {
+    case BwdStage::kRead:
+      hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(xcd_grid(nch * BH)), dim3(512), 0, stream, a.tok);
+      break;
+    case BwdStage::kPrep: {
+      const int rows = a.B * a.T * a.H, rpb = 256 / (D / 4);
+      hipLaunchKernelGGL(arl2_bwd_rowdot_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, stream, a.d_out,
+                         a.o_sm, static_cast<f16*>(a.do_h), a.dvec, rows, a.T, a.H);
+      hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, q, k, v, doh,
+                         static_cast<f16*>(a.v16), static_cast<f16*>(a.kt16), static_cast<f16*>(a.qt16),
+                         static_cast<f16*>(a.dot16), a.T, a.H, a.tp);
+      break;
+    }
+    case BwdStage::kDkdv: {
+      constexpr int kDkdvWaves = 8;
+      const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
+      hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(xcd_grid(nkb * BH)), dim3(64 * kDkdvWaves), 0,
+                         stream, q, k, v, doh, static_cast<const f16*>(a.qt16), static_cast<const f16*>(a.dot16), a.lse,
+                         a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
+      break;
+    }
+    case BwdStage::kDq: {
+      constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
+      const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
+      hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(xcd_grid(nqb * BH)), dim3(128 * kDqGroups), 0,
+                         stream, q, k, static_cast<const f16*>(a.v16), static_cast<const f16*>(a.kt16), doh, a.lse,
+                         a.dvec, a.tok.dq, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
+      break;
+    }
+    case BwdStage::kGsum:
+      hipLaunchKernelGGL(arl2_bwd_gsum_kernel, dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, stream, a.tok.part,
+                         a.gr, D * D, nch, a.gr_first ? 1 : 0);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1138,10 +1156,10 @@ hipError_t launch_bwd_fill(float* dst, const float* src, size_t n, hipStream_t s
 
 int bwd_key_pitch(int T) { return (T + kAttnBlock - 1) / kAttnBlock * kAttnBlock; }
 
-hipError_t launch_bwd_pass(int d, const BwdPassArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_stage(int d, BwdStage stage, const BwdPassArgs& a, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_bwd_pass_d<64>(a, stream);
-    case 128: return launch_bwd_pass_d<128>(a, stream);
+    case 64: return launch_bwd_stage_d<64>(stage, a, stream);
+    case 128: return launch_bwd_stage_d<128>(stage, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

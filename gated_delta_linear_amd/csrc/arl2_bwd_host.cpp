@@ -47,11 +47,32 @@ struct arl2_bwd {
   hipStream_t last_stream = nullptr;
   bool have_last_stream = false;
   hipEvent_t handoff = nullptr;
+  // A second stream of the object's own (default priority, not blocking with the null stream):
+  // a pass's inter-frame read and its dQ kernel run there, beside the softmax recompute and the
+  // dK/dV kernel on the caller's stream, on the CUs those leave idle.  Forked from and joined
+  // back into the caller's stream within each call.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_prep = nullptr, ev_join = nullptr;
 };
 
 namespace {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+void release_sync_objects(arl2_bwd* g) {
+  if (g->side) (void)hipStreamDestroy(g->side);
+  for (hipEvent_t ev : {g->handoff, g->ev_fork, g->ev_prep, g->ev_join})
+    if (ev) (void)hipEventDestroy(ev);
+  g->side = nullptr;
+  g->handoff = g->ev_fork = g->ev_prep = g->ev_join = nullptr;
+}
+
+// `waiter` waits for what `signaller` has enqueued so far
+hipError_t order_after(hipEvent_t ev, hipStream_t signaller, hipStream_t waiter) {
+  hipError_t e = hipEventRecord(ev, signaller);
+  if (e == hipSuccess) e = hipStreamWaitEvent(waiter, ev, 0);
+  return e;
+}
 
 arl2_status hip_fail(arl2_bwd* g, hipError_t e, const char* what) {
   if (g) g->poisoned = true;
@@ -211,12 +232,15 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   auto bail = [&](hipError_t err, const char* what) {
     (void)hipStreamSynchronize(stream);
+    if (g->side) (void)hipStreamSynchronize(g->side);
     (void)hipFree(g->slab);
-    if (g->handoff) (void)hipEventDestroy(g->handoff);
+    release_sync_objects(g);
     delete g;
     return fail(ARL2_E_HIP, "%s: %s", what, hipGetErrorString(err));
   };
-  if ((e = hipEventCreateWithFlags(&g->handoff, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
+  for (hipEvent_t* ev : {&g->handoff, &g->ev_fork, &g->ev_prep, &g->ev_join})
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
+  if ((e = hipStreamCreateWithFlags(&g->side, hipStreamNonBlocking)) != hipSuccess) return bail(e, "hipStreamCreate");
   if ((e = hipMemcpyAsync(g->phi_q, phi_q, H * d * d * 2, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
     return bail(e, "phi_q copy");
   const void* src[5] = {phi_k, phi_v, phi_k, phi_v, phi_q};
@@ -228,7 +252,7 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
   if ((st = arl2_bwd_begin(g, nullptr, stream_)) != ARL2_OK) {
     (void)hipStreamSynchronize(stream);
     (void)hipFree(g->slab);
-    (void)hipEventDestroy(g->handoff);
+    release_sync_objects(g);
     delete g;
     return st;
   }
@@ -277,8 +301,6 @@ arl2_status arl2_bwd_pass(arl2_bwd* g, const void* q, const void* k, const void*
   f.Tk = f.T;
   f.kv_rows = f.T;
   f.lse = g->lse;
-  if ((st = after_launch(g, arl2::launch_fwd(g->d, f, nullptr, stream), stream, "softmax recompute"))) return st;
-  if ((st = frags(g, s_prev, false, stream))) return st;
   arl2::BwdPassArgs a;
   a.tok = tok_args(g);
   a.tok.q = q;
@@ -306,7 +328,25 @@ arl2_status arl2_bwd_pass(arl2_bwd* g, const void* q, const void* k, const void*
   a.T = g->cfg.tokens_per_frame;
   a.scale = g->scale;
   a.scale_log2 = g->scale_log2;
-  if ((st = after_launch(g, arl2::launch_bwd_pass(g->d, a, stream), stream, "pass backward"))) return st;
+  // Caller's stream: S fragments | recompute, prep ........ | dK/dV | (join) gsum
+  // side stream:                  (fork) read | (prep done) dQ |
+  // The read overwrites dq and the dQ kernel adds to it (one fp32 sum of two terms, the same in
+  // either order).  Each wait is enqueued after the record it waits for.
+  using arl2::BwdStage;
+  hipError_t e;
+  if ((st = frags(g, s_prev, false, stream))) return st;
+  if ((e = order_after(g->ev_fork, stream, g->side)) != hipSuccess) return hip_fail(g, e, "stream fork");
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kRead, a, g->side), g->side, "inter-frame read backward")))
+    return st;
+  if ((st = after_launch(g, arl2::launch_fwd(g->d, f, nullptr, stream), stream, "softmax recompute"))) return st;
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kPrep, a, stream), stream, "attention backward prep")))
+    return st;
+  if ((e = order_after(g->ev_prep, stream, g->side)) != hipSuccess) return hip_fail(g, e, "stream fork");
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kDq, a, g->side), g->side, "dQ backward"))) return st;
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kDkdv, a, stream), stream, "dK/dV backward")))
+    return st;
+  if ((e = order_after(g->ev_join, g->side, stream)) != hipSuccess) return hip_fail(g, e, "stream join");
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kGsum, a, stream), stream, "Q^T dO sums"))) return st;
   g->gr_valid = true;
   return ARL2_OK;
 }
@@ -373,8 +413,9 @@ arl2_status arl2_bwd_read(arl2_bwd* g, float* ds, float* dphi_q, float* dphi_k, 
 arl2_status arl2_bwd_destroy(arl2_bwd* g) {
   if (!g) return ARL2_OK;
   hipError_t e = g->have_last_stream ? hipStreamSynchronize(g->last_stream) : hipSuccess;
+  if (e == hipSuccess && g->side) e = hipStreamSynchronize(g->side);
   const hipError_t e2 = hipFree(g->slab);
-  if (g->handoff) (void)hipEventDestroy(g->handoff);
+  release_sync_objects(g);
   delete g;
   if (e == hipSuccess) e = e2;
   return e == hipSuccess ? ARL2_OK : fail(ARL2_E_HIP, "destroy: %s", hipGetErrorString(e));

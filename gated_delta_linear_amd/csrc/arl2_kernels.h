@@ -224,7 +224,15 @@ struct BwdPassArgs {
   int B, H, T;
   float scale, scale_log2;
 };
-hipError_t launch_bwd_pass(int d, const BwdPassArgs& a, hipStream_t stream);
+// The pass backward in stages, which the host orders on two streams:
+//   kRead: the inter-frame read (needs the S fragments): dq = its part, and the chunk partials of Q^T dO;
+//   kPrep: dO . O per row and dO in fp16, then the fp16 operands of the attention kernels (needs
+//          the recomputed softmax output and log-sum-exp);
+//   kDkdv: dK, dV of the softmax branch (needs kPrep; overwrites dk, dv);
+//   kDq:   dQ of the softmax branch, added to dq (needs kPrep and kRead);
+//   kGsum: the chunk partials summed into gr (needs kRead).
+enum class BwdStage { kRead, kPrep, kDkdv, kDq, kGsum };
+hipError_t launch_bwd_stage(int d, BwdStage stage, const BwdPassArgs& a, hipStream_t stream);
 int bwd_key_pitch(int T);  // tp: T rounded up to a multiple of 64
 
 struct BwdFragJobs {

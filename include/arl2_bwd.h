@@ -33,13 +33,18 @@
  *   dbeta, dalpha     fp32 [B][T][H], [B][H] (4-byte aligned), written by arl2_bwd_commit
  *   ds_last, ds0      fp32 [B][H][d][d]   dL/dS after the last frame (in), dL/dS_0 (out)
  *   dphi_q/k/v        fp32 [H][d][d]      accumulated over the frames since arl2_bwd_begin
- * Precision: the softmax branch's backward multiplies fp16 operands with fp32 accumulation (q,
- * k, v converted from bf16, exact for 2^-14 <= |x| <= 65504; P, dS and dO rounded to fp16); the
- * inter-frame read and the state write use split-bf16 products (about fp32 accuracy).  Results
- * are bitwise reproducible (no atomics).
+ * Precision: the softmax branch's backward forms the scores Q K^T from the bf16 inputs as given
+ * and multiplies fp16 operands elsewhere, all with fp32 accumulation (q, k, v converted from
+ * bf16, exact for 2^-14 <= |x| <= 65504; P, dS and dO rounded to fp16); the inter-frame read and
+ * the state write use split-bf16 products (about fp32 accuracy).  Results are bitwise
+ * reproducible (no atomics).
  * Status codes, arl2_last_error() and the stream rule (a call on a different stream than the
  * previous one waits for it) are those of arl2.h.  A failed launch poisons the object
  * (ARL2_E_PROTOCOL) until arl2_bwd_begin.
+ * Streams: arl2_bwd_pass also runs part of its work on a second stream that the object creates
+ * (default priority, not synchronising with the null stream), forked from and joined back into
+ * the caller's stream inside the call: work the caller enqueues afterwards on its stream sees
+ * every result of the call.
  * Graph capture: unlike the forward's calls, these are meant for eager launch.  Each
  * arl2_bwd_commit reads dL/dS from one of two device buffers and writes the other, chosen on the
  * host, so a captured commit would replay with the buffers it was captured with.
