@@ -173,25 +173,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc16(const f16* base, i
                                            any ? (int)(left * 2) : 0, 0x00020000);
 }
 
-// dK, dV of 16 NW keys of one (stream, head).  NW waves, wave w owning keys 16 w .. 16 w + 15; every
-// key block reads the head's whole Q and dO, so wider work-groups cut that stream in proportion.
-// Per query block: S = Q K^T and dP = dO V^T (16x16 C blocks: lane l, register i <-> query
-// 16 m + 4 (l / 16) + i, key l % 16), P = exp2(S scale log2 e - lse), dS = P (dP - Dv); then
-// dV^T += dO^T P and dK^T += Q^T dS with P, dS as the B operands straight from the C registers.
+// dK, dV of 32 NKG keys of one (stream, head), with 32x32x16 MFMAs.  2 NKG waves in two roles
+// that share each 32-key group kg: wave kg (role P) forms S = Q K^T and P = exp2(S scale log2 e
+// - lse) and accumulates dV^T += dO^T P; wave NKG + kg (role dS) forms dP = dO V^T, takes P
+// from role P through LDS, dS = P (dP - Dv), and accumulates dK^T += Q^T dS.  Per 64-query block
+// and 32-query half, C blocks of S and dP hold lane l, register i <-> query
+// 8 (i / 4) + 4 (l / 32) + i % 4, key l % 32: every lane holds one key, so P and dS go straight
+// from the C registers into the B operands of the dV, dK products (k-step h: registers
+// 8 h .. 8 h + 7), and the P handed over is the producer lane's registers as they are.  A block
+// runs in two phases split by a barrier: role P's scores and exponentials beside role dS's dP
+// products, then role P's dV products beside role dS's dS and dK products; the two waves of a
+// key group share a SIMD, so one's vector work overlaps the other's MFMAs.  Each 32x32x16
+// product reads one 1 KB operand from LDS.  Every key block reads the head's whole Q and dO.
 // Staging: each 64-query block's Q rows (bf16, as given: S = Q K^T runs on the bf16 inputs), dO
 // rows (the fp16 dO) and the transposed fp16 copies Q^T and dO^T (64 queries per feature row)
 // come straight into LDS with direct-to-LDS loads, in two stages: block qb + 1's loads fly while
 // block qb is multiplied.  Row tiles keep 16-byte chunk c of query row r at c ^ (r mod d/8), the
-// transposed tiles 8-query chunk c of feature row f at c ^ ((f >> 1) & 7): every load brings
-// whole rows and the fragment reads hit distinct banks.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
+// transposed tiles stored chunk c of feature row f at c ^ (f mod 8): every load brings whole
+// rows, and every fragment read (one 16-byte chunk per lane) hits distinct banks.
+template <int D, int NKG>
+__global__ __launch_bounds__(128 * NKG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
     const f16* __restrict__ qt16, const f16* __restrict__ dot16, const float* __restrict__ lse,
     const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv, int T, int H, int BH, int tp,
     float scale, float scale_log2) {
-  using Sh = BwdShape<D>;
-  constexpr int KS = Sh::KS, NB = Sh::NB;
+  constexpr int K16 = D / 16, FB = D / 32, NW = 2 * NKG;
   constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per query row, 16-byte chunks per row, rows per 1-KB load
   constexpr int TILE = kAttnBlock * RB;                    // bytes of a 64-row tile; a transposed tile (d rows of 128 bytes) too
   constexpr int LD = TILE / 1024, LPT = LD / NW;           // 1-KB loads per tile, of them per wave
@@ -200,23 +206,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __align__(16) unsigned char qr0[TILE], qr1[TILE], or0[TILE], or1[TILE], qt0[TILE], qt1[TILE],
       ot0[TILE], ot1[TILE];
   __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  // P handed from role P to role dS: [key group][32-query half][k-step][lane] 16 bytes
+  __shared__ __align__(16) f16x8 p_x[NKG][2][2][64];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nkb = (T + 16 * NW - 1) / (16 * NW), item = xcd_item(nkb * BH);
+  const int kg = wave % NKG, role = wave / NKG;
+  const int nkb = (T + 32 * NKG - 1) / (32 * NKG), item = xcd_item(nkb * BH);
   if (item < 0) return;
   const int bh = item / nkb, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
-  const int key = (item % nkb) * (16 * NW) + 16 * wave + l16;
-  bf16x8 kf[KS];  // B operands: K^T columns of this wave's keys (bf16, as given)
-  f16x8 vf[KS];   // V^T columns in fp16
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    kf[s] = key < T ? ld_bf16x8(k + base + (int64_t)key * rs + 32 * s + 8 * g) : zero_bf16x8();
-    vf[s] = key < T ? load_f16x8(v + base + (int64_t)key * rs + 32 * s + 8 * g) : f16x8{};
-  }
-  f32x4 dkt[NB], dvt[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) dkt[n] = dvt[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int key = (item % nkb) * (32 * NKG) + 32 * kg + l32;
 
   // Loads of block qb (a wave's loads i = wave + NW m of each tile; see the dQ kernel's).
   auto issue = [&](int qb, unsigned char* qd, unsigned char* od, unsigned char* qtd, unsigned char* otd) {
@@ -242,7 +241,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int m = 0; m < LPT; ++m) {
       const int i = wave + NW * m, row = 8 * i + lane / 8;
-      const int vo = (lane / 8) * tp * 2 + 16 * ((lane % 8) ^ ((row >> 1) & 7));
+      const int vo = (lane / 8) * tp * 2 + 16 * ((lane % 8) ^ (row & 7));
       dma16b(rqt, qtd + i * 1024, vo, 8 * i * tp * 2);
       dma16b(rot, otd + i * 1024, vo, 8 * i * tp * 2);
     }
@@ -264,20 +263,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       dv_s[buf][tid] = dv_r;
     }
   };
+  // A fragment of a transposed tile: feature row 32 fb + l % 32, queries 32 h2 + 16 hh +
+  // 8 (j / 4) + 4 (l / 32) + j % 4 (the stacked-C row order of P and dS), which the quad order of
+  // the copies puts in stored chunk 4 h2 + 2 hh + l / 32
+  auto tfrag = [&](const unsigned char* t, int fb, int h2, int hh) {
+    const int f = 32 * fb + l32;
+    return *reinterpret_cast<const f16x8*>(t + f * 128 + 16 * ((4 * h2 + 2 * hh + hi) ^ (f & 7)));
+  };
+  // A fragment of a row tile: query row 32 h2 + l % 32, features 16 s + 8 (l / 32) ..
+  auto rfrag_off = [&](int h2, int s) {
+    const int r = 32 * h2 + l32;
+    return r * RB + 16 * ((2 * s + hi) ^ (r % CPR));
+  };
+  // the phase barrier: role P's stores of P are done (lgkmcnt(0)); the block's tile loads stay in
+  // flight (no vmcnt wait), and the compiler keeps LDS accesses on their side of it
+  auto phase_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   const int nqb = (T + kAttnBlock - 1) / kAttnBlock;
-  load_ld(0);
-  store_ld(0);
-  if (nqb > 1) load_ld(1);
-  issue(0, qr0, or0, qt0, ot0);
   // block qb (odd_c: qb % 2): this wave's loads of it have landed and its reads of block qb - 1
   // are done; after the barrier everyone's are, so block qb + 1 goes into the other stage while
   // block qb is multiplied
-  auto qblock = [&](int qb, auto odd_c) {
+  auto begin_block = [&](int qb, auto odd_c) {
     constexpr int odd = decltype(odd_c)::value;
-    const unsigned char* qc = odd ? qr1 : qr0;
-    const unsigned char* oc = odd ? or1 : or0;
-    const unsigned char* qtc = odd ? qt1 : qt0;
-    const unsigned char* otc = odd ? ot1 : ot0;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     if (qb + 1 < nqb) {
@@ -286,60 +292,170 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if constexpr (odd) issue(qb + 1, qr0, or0, qt0, ot0);
       else issue(qb + 1, qr1, or1, qt1, ot1);
     }
-    const float* lse_c = lse_s[odd];
-    const float* dv_c = dv_s[odd];
-    // per 32-query half s2: S and dP of its two 16-query blocks, then its share of dV^T, dK^T
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f16x8 pb, dsb;
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int m = 2 * s2 + mm;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int r = 16 * m + l16;
-          const int ro = r * RB + 16 * ((4 * s + g) ^ (r % CPR));
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qc + ro);
-          const f16x8 ao = *reinterpret_cast<const f16x8*>(oc + ro);
-          sc = mfma16(aq, kf[s], sc);
-          dp = mfma16h(ao, vf[s], dp);
-        }
-        const f32x4 L = *reinterpret_cast<const f32x4*>(lse_c + 16 * m + 4 * g);
-        const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_c + 16 * m + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(sc[i] * scale_log2 - L[i]);
-          pb[4 * mm + i] = (f16)p;
-          dsb[4 * mm + i] = (f16)(p * (dp[i] - Dd[i]));
-        }
-      }
-      // A fragments of the transposed tiles: feature row f = 16 mb + l % 16, queries
-      // 32 s2 + 16 (j / 4) + 4 (l / 16) + j % 4 (the stacked-C row order of P and dS)
-#pragma unroll
-      for (int mb = 0; mb < NB; ++mb) {
-        const int f = 16 * mb + l16, sw = (f >> 1) & 7, c0 = 4 * s2 + (g >> 1), o8 = 8 * (g & 1);
-        const int t0 = f * 128 + 16 * (c0 ^ sw) + o8, t1 = f * 128 + 16 * ((c0 + 2) ^ sw) + o8;
-        const f16x4 a0 = *reinterpret_cast<const f16x4*>(otc + t0), a1 = *reinterpret_cast<const f16x4*>(otc + t1);
-        const f16x4 b0 = *reinterpret_cast<const f16x4*>(qtc + t0), b1 = *reinterpret_cast<const f16x4*>(qtc + t1);
-        dvt[mb] = mfma16h(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, pb, dvt[mb]);
-        dkt[mb] = mfma16h(f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]}, dsb, dkt[mb]);
-      }
-    }
   };
-  int qb = 0;
-  for (; qb + 1 < nqb; qb += 2) {
-    qblock(qb, std::integral_constant<int, 0>());
-    qblock(qb + 1, std::integral_constant<int, 1>());
-  }
-  if (qb < nqb) qblock(qb, std::integral_constant<int, 0>());
-  // lane l, register i: feature 16 mb + 4 (l / 16) + i of key 16 w + l % 16
-  if (key < T) {
+  load_ld(0);
+  store_ld(0);
+  if (nqb > 1) load_ld(1);
+  issue(0, qr0, or0, qt0, ot0);
+
+  if (role == 0) {
+    // role P: B operands K^T (lane l: key, features 16 s + 8 (l / 32) ..; bf16, as given)
+    bf16x8 kf[K16];
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-      const int64_t o = base + (int64_t)key * rs + 16 * mb + 4 * g;
-      *reinterpret_cast<f32x4*>(dk + o) = dkt[mb] * scale;
-      *reinterpret_cast<f32x4*>(dv + o) = dvt[mb];
+    for (int s = 0; s < K16; ++s)
+      kf[s] = key < T ? ld_bf16x8(k + base + (int64_t)key * rs + 16 * s + 8 * hi) : zero_bf16x8();
+    f32x16 dvt[FB];
+#pragma unroll
+    for (int n = 0; n < FB; ++n) dvt[n] = zero16();
+    auto qblock = [&](int qb, auto odd_c) {
+      constexpr int odd = decltype(odd_c)::value;
+      const unsigned char* qc = odd ? qr1 : qr0;
+      const unsigned char* otc = odd ? ot1 : ot0;
+      const float* lse_c = lse_s[odd];
+      begin_block(qb, odd_c);
+      // every fragment of a product group is read before its MFMAs, and the dV operands before
+      // the exponentials, so that LDS latency hides behind MFMA and vector work
+      bf16x8 fa[2][K16];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int s = 0; s < K16; ++s) fa[h2][s] = *reinterpret_cast<const bf16x8*>(qc + rfrag_off(h2, s));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sc[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int s = 0; s < K16; ++s)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) sc[h2] = mfma32(fa[h2][s], kf[s], sc[h2]);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 ta[FB][2];  // dO^T operands of the first 32-query half
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) ta[fb][hh] = tfrag(otc, fb, 0, hh);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 pb[2][2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 L = *reinterpret_cast<const f32x4*>(lse_c + 32 * h2 + 8 * j + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pb[h2][j / 2][4 * (j % 2) + e] = (f16)fast_exp2(sc[h2][4 * j + e] * scale_log2 - L[e]);
+        }
+        p_x[kg][h2][0][lane] = pb[h2][0];
+        p_x[kg][h2][1][lane] = pb[h2][1];
+      }
+      phase_barrier();
+      f16x8 tb[FB][2];  // the second half's, read while the first half's products run
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) tb[fb][hh] = tfrag(otc, fb, 1, hh);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) dvt[fb] = mfma32(ta[fb][hh], pb[0][hh], dvt[fb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) dvt[fb] = mfma32(tb[fb][hh], pb[1][hh], dvt[fb]);
+    };
+    int qb = 0;
+    for (; qb + 1 < nqb; qb += 2) {
+      qblock(qb, std::integral_constant<int, 0>());
+      qblock(qb + 1, std::integral_constant<int, 1>());
+    }
+    if (qb < nqb) qblock(qb, std::integral_constant<int, 0>());
+    // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of key l % 32
+    if (key < T) {
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(dv + base + (int64_t)key * rs + 32 * fb + 8 * g4 + 4 * hi) =
+              f32x4{dvt[fb][4 * g4], dvt[fb][4 * g4 + 1], dvt[fb][4 * g4 + 2], dvt[fb][4 * g4 + 3]};
+    }
+  } else {
+    // role dS: B operands V^T in fp16 (lane l: key, features 16 s + 8 (l / 32) ..)
+    f16x8 vf[K16];
+#pragma unroll
+    for (int s = 0; s < K16; ++s)
+      vf[s] = key < T ? load_f16x8(v + base + (int64_t)key * rs + 16 * s + 8 * hi) : f16x8{};
+    f32x16 dkt[FB];
+#pragma unroll
+    for (int n = 0; n < FB; ++n) dkt[n] = zero16();
+    auto qblock = [&](int qb, auto odd_c) {
+      constexpr int odd = decltype(odd_c)::value;
+      const unsigned char* oc = odd ? or1 : or0;
+      const unsigned char* qtc = odd ? qt1 : qt0;
+      const float* dv_c = dv_s[odd];
+      begin_block(qb, odd_c);
+      // as in role P: fragment reads ahead of their MFMAs, the dK operands before the barrier
+      f16x8 fa[2][K16];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int s = 0; s < K16; ++s) fa[h2][s] = *reinterpret_cast<const f16x8*>(oc + rfrag_off(h2, s));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 dp[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int s = 0; s < K16; ++s)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) dp[h2] = mfma32(fa[h2][s], vf[s], dp[h2]);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 ta[FB][2];  // Q^T operands of the first 32-query half
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) ta[fb][hh] = tfrag(qtc, fb, 0, hh);
+      phase_barrier();
+      // dS of a 32-query half from role P's P (this lane's registers there) and dP
+      auto ds_half = [&](int h2, f16x8 (&dsb)[2]) {
+        const f16x8 p0 = p_x[kg][h2][0][lane], p1 = p_x[kg][h2][1][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 Dd = *reinterpret_cast<const f32x4*>(dv_c + 32 * h2 + 8 * j + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * j + e;
+            const float p = (float)(i < 8 ? p0[i] : p1[i - 8]);
+            dsb[i / 8][i % 8] = (f16)(p * (dp[h2][i] - Dd[e]));
+          }
+        }
+      };
+      f16x8 d0[2], d1[2];
+      ds_half(0, d0);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x8 tb[FB][2];  // the second half's, read while the first half's products run
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) tb[fb][hh] = tfrag(qtc, fb, 1, hh);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) dkt[fb] = mfma32(ta[fb][hh], d0[hh], dkt[fb]);
+      ds_half(1, d1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) dkt[fb] = mfma32(tb[fb][hh], d1[hh], dkt[fb]);
+    };
+    int qb = 0;
+    for (; qb + 1 < nqb; qb += 2) {
+      qblock(qb, std::integral_constant<int, 0>());
+      qblock(qb + 1, std::integral_constant<int, 1>());
+    }
+    if (qb < nqb) qblock(qb, std::integral_constant<int, 0>());
+    if (key < T) {
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(dk + base + (int64_t)key * rs + 32 * fb + 8 * g4 + 4 * hi) =
+              f32x4{dkt[fb][4 * g4], dkt[fb][4 * g4 + 1], dkt[fb][4 * g4 + 2], dkt[fb][4 * g4 + 3]} * scale;
     }
   }
 }
@@ -347,7 +463,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // A pass's operands in fp16 for the attention backward's direct-to-LDS staging: v16 in the
 // [B][T][H][d] layout of v (rows past T not written), and the transposes kt16, qt16, dot16
 // [B][H][d][tp] of k, q and the fp16 dO: each head's features as rows of its tokens, 64-token
-// blocks (tokens past T zero).  One work-group per (stream, head, 64-token block); thread j moves
+// blocks (tokens past T zero), each 16-token group stored as its 4-token quads 0, 2, 1, 3 (the
+// order in which a 32x32x16 MFMA lane takes its 8 k-values when P or dS come straight from C
+// registers, so that a lane's A fragment is one 16-byte chunk).  One work-group per (stream, head, 64-token block); thread j moves
 // rows 4 (j % 16) .. + 3 of 8-feature chunk j / 16, transposing through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -386,8 +504,11 @@ __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restr
   for (int j = tid; j < 3 * D * (kAttnBlock / 8); j += 256) {
     const int m = j / (D * (kAttnBlock / 8)), jj = j % (D * (kAttnBlock / 8));
     const int f = jj / (kAttnBlock / 8), c = jj % (kAttnBlock / 8);
+    // stored chunk c = 2 g + e of a row: tokens 16 g + 4 e .. + 3, then 16 g + 8 + 4 e .. + 3
+    const f16* src = tr[m] + f * TPITCH + 16 * (c / 2) + 4 * (c % 2);
+    const f16x4 lo = *reinterpret_cast<const f16x4*>(src), hi = *reinterpret_cast<const f16x4*>(src + 8);
     *reinterpret_cast<f16x8*>(dst[m] + ((int64_t)bh * D + f) * tp + k0 + 8 * c) =
-        *reinterpret_cast<const f16x8*>(tr[m] + f * TPITCH + 8 * c);
+        f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 }
 
@@ -403,9 +524,9 @@ __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restr
 // Staging: each block's K rows (bf16, as given), V rows (the fp16 copy v16) and K^T (kt16, 64
 // keys per feature row, fp16) come straight into LDS with direct-to-LDS loads, in two stages: block kb + 1's
 // loads fly while block kb is multiplied, and no thread converts or transposes anything.  A row
-// tile keeps 16-byte chunk c of key row r at chunk c ^ (r mod d/8), the K^T tile 8-key chunk c of
-// feature row f at c ^ ((f >> 1) & 7): every load brings whole rows, the row fragments' reads hit
-// distinct banks and the K^T fragments' reads at most two lanes per bank.
+// tile keeps 16-byte chunk c of key row r at chunk c ^ (r mod d/8), the K^T tile stored chunk c
+// of feature row f at c ^ (f mod 8): every load brings whole rows, and every fragment read (one
+// 16-byte chunk per lane) hits distinct banks.
 template <int D, int NQG>
 __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const f16* __restrict__ v16,
@@ -446,7 +567,7 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // Loads of block kb: a wave's loads i = wave + NW m of each tile (row tiles: rows RPI i ..,
   // lane l row RPI i + l / CPR, chunk (l % CPR) ^ (row % CPR); K^T: feature rows 8 i .., lane l row
-  // 8 i + l / 8, key chunk (l % 8) ^ ((row >> 1) & 7)).
+  // 8 i + l / 8, key chunk (l % 8) ^ (row % 8)).
   auto issue = [&](int kb, unsigned char* kd, unsigned char* vd, unsigned char* td) {
     const int r0 = kb * kAttnBlock;
     const __amdgpu_buffer_rsrc_t rk = rows_rsrc16(reinterpret_cast<const f16*>(k) + base, T, rs, D, r0);  // bf16 bits
@@ -468,7 +589,7 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
     for (int m = 0; m < LPT; ++m) {
       const int i = wave + NW * m, row = 8 * i + lane / 8;
-      dma16b(rkt, td + i * 1024, (lane / 8) * tp * 2 + 16 * ((lane % 8) ^ ((row >> 1) & 7)), 8 * i * tp * 2);
+      dma16b(rkt, td + i * 1024, (lane / 8) * tp * 2 + 16 * ((lane % 8) ^ (row & 7)), 8 * i * tp * 2);
     }
   };
   const int nkb = (T + kAttnBlock - 1) / kAttnBlock;
@@ -509,11 +630,11 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        // A: K^T rows 32 fb + l % 32, keys 32 kh + 16 hh + 8 (j / 4) + 4 (l / 32) + j % 4
-        const int f = 32 * fb + l32, sw = (f >> 1) & 7, c0 = 4 * kh + 2 * hh;
-        const f16x4 a0 = *reinterpret_cast<const f16x4*>(tc + f * 128 + 16 * (c0 ^ sw) + 8 * hi);
-        const f16x4 a1 = *reinterpret_cast<const f16x4*>(tc + f * 128 + 16 * ((c0 + 1) ^ sw) + 8 * hi);
-        dqt[fb] = mfma32(f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, dsb[hh], dqt[fb]);
+        // A: K^T rows 32 fb + l % 32, keys 32 kh + 16 hh + 8 (j / 4) + 4 (l / 32) + j % 4: stored
+        // chunk 4 kh + 2 hh + l / 32 of the row (the copies' quad order)
+        const int f = 32 * fb + l32;
+        dqt[fb] = mfma32(*reinterpret_cast<const f16x8*>(tc + f * 128 + 16 * ((4 * kh + 2 * hh + hi) ^ (f & 7))),
+                         dsb[hh], dqt[fb]);
       }
   };
   int kb = 0;
@@ -1096,9 +1217,9 @@ hipError_t launch_bwd_stage_d(BwdStage stage, const BwdPassArgs& a, hipStream_t 
       break;
     }
     case BwdStage::kDkdv: {
-      constexpr int kDkdvWaves = 8;
-      const int nkb = (a.T + 16 * kDkdvWaves - 1) / (16 * kDkdvWaves);
-      hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kDkdvWaves>), dim3(xcd_grid(nkb * BH)), dim3(64 * kDkdvWaves), 0,
+      constexpr int kKeyGroups = 4;  // 32-key groups per work-group (times two roles: 8 waves)
+      const int nkb = (a.T + 32 * kKeyGroups - 1) / (32 * kKeyGroups);
+      hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kKeyGroups>), dim3(xcd_grid(nkb * BH)), dim3(128 * kKeyGroups), 0,
                          stream, q, k, v, doh, static_cast<const f16*>(a.qt16), static_cast<const f16*>(a.dot16), a.lse,
                          a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
       break;
