@@ -602,40 +602,54 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
     const unsigned char* kc = odd ? kr1 : kr0;
     const unsigned char* vc = odd ? vr1 : vr0;
     const unsigned char* tc = odd ? kt1 : kt0;
-    const int r0 = kb * kAttnBlock;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     if (kb + 1 < nkb) {
       if constexpr (odd) issue(kb + 1, kr0, vr0, kt0);
       else issue(kb + 1, kr1, vr1, kt1);
     }
-    f32x16 sc = zero16(), dp = zero16();
+    // every row fragment is read before the score and dP products, and the K^T fragments
+    // before dS^T is formed, so that LDS latency hides behind MFMA and vector work
+    bf16x8 ak[K16];
+    f16x8 av[K16];
 #pragma unroll
     for (int s = 0; s < K16; ++s) {
       const int r = 32 * kh + l32;
       const int ro = r * RB + 16 * ((2 * s + hi) ^ (r % CPR));
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kc + ro);
-      const f16x8 av = *reinterpret_cast<const f16x8*>(vc + ro);
-      sc = mfma32(ak, qf[s], sc);
-      dp = mfma32(av, df[s], dp);
+      ak[s] = *reinterpret_cast<const bf16x8*>(kc + ro);
+      av[s] = *reinterpret_cast<const f16x8*>(vc + ro);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+    for (int s = 0; s < K16; ++s) {
+      sc = mfma32(ak[s], qf[s], sc);
+      dp = mfma32(av[s], df[s], dp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // A: K^T rows 32 fb + l % 32, keys 32 kh + 16 hh + 8 (j / 4) + 4 (l / 32) + j % 4: stored
+    // chunk 4 kh + 2 hh + l / 32 of the row (the copies' quad order)
+    f16x8 at[FB][2];
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int f = 32 * fb + l32;
+        at[fb][hh] = *reinterpret_cast<const f16x8*>(tc + f * 128 + 16 * ((4 * kh + 2 * hh + hi) ^ (f & 7)));
+      }
     f16x8 dsb[2];
+    // Keys past T need no mask: their K^T columns are zero in the copy, so their dS adds nothing,
+    // provided it is finite; the exponent is clamped at 0 (a key of the frame has S scale log2 e
+    // <= lse up to rounding, so P <= 1), which keeps every P finite.
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = r0 + 32 * kh + 8 * (i / 4) + 4 * hi + i % 4;
-      const float p = key < T ? fast_exp2(sc[i] * scale_log2 - L) : 0.f;
+      const float p = fast_exp2(fminf(sc[i] * scale_log2 - L, 0.f));
       dsb[i / 8][i % 8] = (f16)(p * (dp[i] - Dd));
     }
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        // A: K^T rows 32 fb + l % 32, keys 32 kh + 16 hh + 8 (j / 4) + 4 (l / 32) + j % 4: stored
-        // chunk 4 kh + 2 hh + l / 32 of the row (the copies' quad order)
-        const int f = 32 * fb + l32;
-        dqt[fb] = mfma32(*reinterpret_cast<const f16x8*>(tc + f * 128 + 16 * ((4 * kh + 2 * hh + hi) ^ (f & 7))),
-                         dsb[hh], dqt[fb]);
-      }
+      for (int hh = 0; hh < 2; ++hh) dqt[fb] = mfma32(at[fb][hh], dsb[hh], dqt[fb]);
   };
   int kb = 0;
   for (; kb + 1 < nkb; kb += 2) {
@@ -651,23 +665,31 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
     unsigned char* p = a == 0 ? kr0 : a == 1 ? kr1 : a == 2 ? vr0 : vr1;
     return reinterpret_cast<f32x16*>(p + (i % PER) * 4096);
   };
+  // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of query qi; the inter-frame
+  // read's part of dq is loaded before the exchange, to be added to
+  f32x4 prior[FB][4];
+  const bool out = !kh && qi < T;
+  if (out) {
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        prior[fb][g4] = *reinterpret_cast<const f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi);
+  }
   __syncthreads();
   if (kh) {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) xslot(qh * FB + fb)[lane] = dqt[fb];
   }
   __syncthreads();
-  // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of query qi
-  if (!kh && qi < T) {
+  if (out) {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
       const f32x16 x = dqt[fb] + xslot(qh * FB + fb)[lane];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-      {
-        f32x4* o = reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi);
-        *o = *o + f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
-      }
+        *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi) =
+            prior[fb][g4] + f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
     }
   }
 }
