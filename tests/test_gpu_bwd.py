@@ -18,7 +18,8 @@ import torch
 from gated_delta_linear_amd import Arl2Backward
 from oracle import layer_backward
 from oracle.bwd_oracle import forward_states
-from synth import WORKLOADS, Workload, make_gates, make_out_grad, make_pass_inputs, make_phi, make_state_grad
+from synth import (WORKLOADS, Workload, make_gates, make_out_grad, make_pass_inputs, make_phi, make_state_grad,
+                   round_bf16)
 from tests.arl2_harness import dev, log, out_err, state_err
 
 pytestmark = pytest.mark.gpu
@@ -154,6 +155,31 @@ def test_key_norm_below_eps():
     sqrt(d) / 16) take the constant branch of max(|u|, eps)."""
     w = Workload("bwd_eps", batch=1, heads=2, head_dim=64, tokens=96, frames=2, denoise_steps=1, seed=62)
     tok, prec = run_case(w, 2, 2, knorm_eps=4.0, k_scale_rows=(1.0 / 16, 3))
+    assert tok <= TOK_TOL and prec <= PRECISE_TOL, (tok, prec)
+
+
+@pytest.mark.parametrize("d,T", [(128, 100), (64, 257)])
+def test_strongly_negative_scores(d, T):
+    """Every score far below zero: q = -16 u + noise, k = u + noise with u of +-1 entries per
+    head, so scores sit near -16 d (log-sum-exp near -260 in log2 units at d = 128).  At a ragged
+    T the keys that pad the last 64-key block score 0, and exp2(score scale log2 e - lse) there
+    would be about 2^260, infinite in fp32: the attention backward must keep such keys from
+    reaching any gradient.  (The keys' shared part u is kept small: dq sums dS over keys, whose
+    exact sum is zero, so a large shared key part would magnify dS's fp16 rounding.)"""
+    w = Workload(f"bwd_neg_{d}_{T}", batch=1, heads=2, head_dim=d, tokens=T, frames=2, denoise_steps=1, seed=70 + T)
+    rng = np.random.default_rng(71 + T)
+    u = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=(1, 1, w.heads, d))
+    fr, d_outs = make_stream(w, 2, 2)
+    for f in fr:
+        f["passes"] = [(round_bf16(-16 * u + 0.5 * q), round_bf16(u + 0.25 * k), v) for q, k, v in f["passes"]]
+    phis = make_phi(w)
+    g_last = make_state_grad(w)
+    got = gpu_backward(w, phis, fr, d_outs, g_last)
+    for key in ("dq", "dk", "dv"):
+        assert all(np.isfinite(x).all() for row in got[key] for x in row), key
+    want = layer_backward(*(p.astype(np.float64) for p in phis), fr, d_outs, g_last=g_last, eps=1e-6)
+    tok, prec = compare(got, want, d_outs)
+    log(f"bwd negative scores d={d} T={T}: token grads {tok:.3e}, state / map / gate grads {prec:.3e}")
     assert tok <= TOK_TOL and prec <= PRECISE_TOL, (tok, prec)
 
 
