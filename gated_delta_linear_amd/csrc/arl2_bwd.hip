@@ -50,11 +50,12 @@ constexpr int kTokChunk = 128;  // tokens per work-group of the token kernels (8
 // x ceil(n / 8) + j goes to work-group 8 j + x, so each XCD takes a contiguous run of items, one
 // or two heads, and a head's operands fill one or two L2 caches instead of all eight.  Returns
 // -1 for the padding work-groups.
-__device__ __forceinline__ int xcd_item(int n) {
-  const int per = (n + 7) / 8, item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+__device__ __forceinline__ int xcd_item_at(int wg, int n) {
+  const int per = (n + 7) / 8, item = (wg & 7) * per + (wg >> 3);
   return item < n ? item : -1;
 }
-inline int xcd_grid(int n) { return 8 * ((n + 7) / 8); }
+__device__ __forceinline__ int xcd_item(int n) { return xcd_item_at((int)blockIdx.x, n); }
+__host__ __device__ inline int xcd_grid(int n) { return 8 * ((n + 7) / 8); }
 
 template <int D>
 struct BwdShape {
@@ -192,28 +193,44 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc16(const f16* base, i
 // block qb is multiplied.  Row tiles keep 16-byte chunk c of query row r at c ^ (r mod d/8), the
 // transposed tiles stored chunk c of feature row f at c ^ (f mod 8): every load brings whole
 // rows, and every fragment read (one 16-byte chunk per lane) hits distinct banks.
-template <int D, int NKG>
-__global__ __launch_bounds__(128 * NKG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dkdv_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const f16* __restrict__ doh,
-    const f16* __restrict__ qt16, const f16* __restrict__ dot16, const float* __restrict__ lse,
-    const float* __restrict__ dvec, float* __restrict__ dk, float* __restrict__ dv, int T, int H, int BH, int tp,
-    float scale, float scale_log2) {
+// Operands of the attention backward launch (dK/dV and dQ work-groups in one grid).
+struct BwdAttnArgs {
+  const bf16 *q, *k, *v;
+  const f16 *doh, *v16, *kt16, *qt16, *dot16;
+  const float *lse, *dvec;
+  float *dk, *dv, *dq;
+  int T, H, BH, tp;
+  float scale, scale_log2;
+};
+
+template <int D, int NKG, int TILE>
+__device__ __forceinline__ void dkdv_body(const BwdAttnArgs& A, int item, unsigned char (&qr0)[TILE],
+                                          unsigned char (&qr1)[TILE], unsigned char (&or0)[TILE],
+                                          unsigned char (&or1)[TILE], unsigned char (&qt0)[TILE],
+                                          unsigned char (&qt1)[TILE], unsigned char (&ot0)[TILE],
+                                          unsigned char (&ot1)[TILE], float (&lse_s)[2][kAttnBlock],
+                                          float (&dv_s)[2][kAttnBlock], f16x8 (&p_x)[NKG][2][2][64]) {
+  const bf16* __restrict__ q = A.q;
+  const bf16* __restrict__ k = A.k;
+  const bf16* __restrict__ v = A.v;
+  const f16* __restrict__ doh = A.doh;
+  const f16* __restrict__ qt16 = A.qt16;
+  const f16* __restrict__ dot16 = A.dot16;
+  const float* __restrict__ lse = A.lse;
+  const float* __restrict__ dvec = A.dvec;
+  float* __restrict__ dk = A.dk;
+  float* __restrict__ dv = A.dv;
+  const int T = A.T, H = A.H, tp = A.tp;
+  const float scale = A.scale, scale_log2 = A.scale_log2;
   constexpr int K16 = D / 16, FB = D / 32, NW = 2 * NKG;
   constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per query row, 16-byte chunks per row, rows per 1-KB load
-  constexpr int TILE = kAttnBlock * RB;                    // bytes of a 64-row tile; a transposed tile (d rows of 128 bytes) too
+  static_assert(TILE == kAttnBlock * RB, "a 64-row tile; a transposed tile (d rows of 128 bytes) too");
   constexpr int LD = TILE / 1024, LPT = LD / NW;           // 1-KB loads per tile, of them per wave
   static_assert(LD % NW == 0, "every wave issues the same number of loads per tile");
-  // separate arrays per stage and tile, addressed with compile-time stage numbers
-  __shared__ __align__(16) unsigned char qr0[TILE], qr1[TILE], or0[TILE], or1[TILE], qt0[TILE], qt1[TILE],
-      ot0[TILE], ot1[TILE];
-  __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
-  // P handed from role P to role dS: [key group][32-query half][k-step][lane] 16 bytes
-  __shared__ __align__(16) f16x8 p_x[NKG][2][2][64];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave % NKG, role = wave / NKG;
-  const int nkb = (T + 32 * NKG - 1) / (32 * NKG), item = xcd_item(nkb * BH);
-  if (item < 0) return;
+  const int nkb = (T + 32 * NKG - 1) / (32 * NKG);
   const int bh = item / nkb, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
   const int key = (item % nkb) * (32 * NKG) + 32 * kg + l32;
@@ -528,26 +545,31 @@ __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restr
 // tile keeps 16-byte chunk c of key row r at chunk c ^ (r mod d/8), the K^T tile stored chunk c
 // of feature row f at c ^ (f mod 8): every load brings whole rows, and every fragment read (one
 // 16-byte chunk per lane) hits distinct banks.
-template <int D, int NQG>
-__global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const f16* __restrict__ v16,
-    const f16* __restrict__ kt16, const f16* __restrict__ doh, const float* __restrict__ lse,
-    const float* __restrict__ dvec, float* __restrict__ dq, int T, int H, int BH, int tp, float scale,
-    float scale_log2) {
+template <int D, int NQG, int TILE>
+__device__ __forceinline__ void dq_body(const BwdAttnArgs& A, int item, unsigned char (&kr0)[TILE],
+                                        unsigned char (&kr1)[TILE], unsigned char (&vr0)[TILE],
+                                        unsigned char (&vr1)[TILE], unsigned char (&kt0)[TILE],
+                                        unsigned char (&kt1)[TILE]) {
+  const bf16* __restrict__ q = A.q;
+  const bf16* __restrict__ k = A.k;
+  const f16* __restrict__ v16 = A.v16;
+  const f16* __restrict__ kt16 = A.kt16;
+  const f16* __restrict__ doh = A.doh;
+  const float* __restrict__ lse = A.lse;
+  const float* __restrict__ dvec = A.dvec;
+  float* __restrict__ dq = A.dq;
+  const int T = A.T, H = A.H, tp = A.tp;
+  const float scale = A.scale, scale_log2 = A.scale_log2;
   constexpr int K16 = D / 16, FB = D / 32, NW = 2 * NQG;
   constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;  // bytes per key row, 16-byte chunks per row, rows per 1-KB load
-  constexpr int TILE = kAttnBlock * RB;                    // bytes of a 64-row tile; the K^T tile (d rows of 128 bytes) too
+  static_assert(TILE == kAttnBlock * RB, "a 64-row tile; the K^T tile (d rows of 128 bytes) too");
   constexpr int LD = TILE / 1024;                          // 1-KB loads per tile
   constexpr int LPT = LD / NW;                             // of them per wave
   static_assert(LD % NW == 0, "every wave issues the same number of loads per tile");
-  // Separate arrays per stage and tile, addressed with compile-time stage numbers, so that the
-  // compiler tells the loads in flight into one stage from the reads of the other.
-  __shared__ __align__(16) unsigned char kr0[TILE], kr1[TILE], vr0[TILE], vr1[TILE], kt0[TILE], kt1[TILE];
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qh = wave % NQG, kh = wave / NQG;
-  const int nqb = (T + 32 * NQG - 1) / (32 * NQG), item = xcd_item(nqb * BH);
-  if (item < 0) return;
+  const int nqb = (T + 32 * NQG - 1) / (32 * NQG);
   const int bh = item / nqb, b = bh / H, h = bh % H;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
   const int qi = (item % nqb) * (32 * NQG) + 32 * qh + l32;
@@ -666,17 +688,8 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
     unsigned char* p = a == 0 ? kr0 : a == 1 ? kr1 : a == 2 ? vr0 : vr1;
     return reinterpret_cast<f32x16*>(p + (i % PER) * 4096);
   };
-  // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of query qi; the inter-frame
-  // read's part of dq is loaded before the exchange, to be added to
-  f32x4 prior[FB][4];
+  // lane l, register i: feature 32 fb + 8 (i / 4) + 4 (l / 32) + i % 4 of query qi
   const bool out = !kh && qi < T;
-  if (out) {
-#pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        prior[fb][g4] = *reinterpret_cast<const f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi);
-  }
   __syncthreads();
   if (kh) {
 #pragma unroll
@@ -690,8 +703,31 @@ __global__ __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<f32x4*>(dq + base + (int64_t)qi * rs + 32 * fb + 8 * g4 + 4 * hi) =
-            prior[fb][g4] + f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
+            f32x4{x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]} * scale;
     }
+  }
+}
+
+// The attention backward in one launch: work-groups [0, G) take dK/dV key blocks, the rest dQ
+// query blocks (G = the dK/dV grid rounded up to a multiple of 8, so that both ranges keep the
+// XCD-aware order).  dK/dV comes first: its work-groups run longest, and dQ's fill the CUs it
+// leaves idle.  The two share one set of LDS arrays (dQ uses six of the eight tiles).
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void arl2_bwd_attn_kernel(
+    const BwdAttnArgs A) {
+  constexpr int TILE = kAttnBlock * 2 * D, NG = 4;
+  __shared__ __align__(16) unsigned char t0[TILE], t1[TILE], t2[TILE], t3[TILE], t4[TILE], t5[TILE], t6[TILE],
+      t7[TILE];
+  __shared__ __align__(16) float lse_s[2][kAttnBlock], dv_s[2][kAttnBlock];
+  __shared__ __align__(16) f16x8 p_x[NG][2][2][64];
+  const int nkb = (A.T + 32 * NG - 1) / (32 * NG), nqb = (A.T + 32 * NG - 1) / (32 * NG);
+  const int g1 = xcd_grid(nkb * A.BH), wg = (int)blockIdx.x;
+  if (wg < g1) {
+    const int item = xcd_item_at(wg, nkb * A.BH);
+    if (item >= 0) dkdv_body<D, NG, TILE>(A, item, t0, t1, t2, t3, t4, t5, t6, t7, lse_s, dv_s, p_x);
+  } else {
+    const int item = xcd_item_at(wg - g1, nqb * A.BH);
+    if (item >= 0) dq_body<D, NG, TILE>(A, item, t0, t1, t2, t3, t4, t5);
   }
 }
 
@@ -1122,15 +1158,25 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 
 // --- sums over chunks, frames' end ---------------------------------------------------------------
 
-// gr[bh] (+)= sum over chunks of the read partials, in chunk order.
-__global__ __launch_bounds__(256) void arl2_bwd_gsum_kernel(const float* __restrict__ part, float* __restrict__ gr,
-                                                            int dd, int nch, int first) {
-  const int bh = blockIdx.y, i4 = blockIdx.x * 256 + threadIdx.x;
-  if (4 * i4 >= dd) return;
-  const f32x4* p = reinterpret_cast<const f32x4*>(part + (int64_t)bh * nch * dd) + i4;
-  f32x4 s = first ? f32x4{0.f, 0.f, 0.f, 0.f} : reinterpret_cast<const f32x4*>(gr + (int64_t)bh * dd)[i4];
-  for (int c = 0; c < nch; ++c) s += p[(int64_t)c * (dd / 4)];
-  reinterpret_cast<f32x4*>(gr + (int64_t)bh * dd)[i4] = s;
+// The pass backward's last step: work-groups [0, n_gsum) sum the chunk partials of Q^T dO into
+// gr (per (stream, head), blockIdx.x % gsum_x picks the float4s); the rest add the inter-frame
+// read's part of dq (dq_read) to the softmax branch's (dq), n4 float4 elements.
+__global__ __launch_bounds__(256) void arl2_bwd_finish_kernel(const float* __restrict__ part, float* __restrict__ gr,
+                                                              int dd, int nch, int first, int gsum_x, int n_gsum,
+                                                              float* __restrict__ dq,
+                                                              const float* __restrict__ dq_read, int64_t n4) {
+  if ((int)blockIdx.x < n_gsum) {
+    const int bh = blockIdx.x / gsum_x, i4 = (blockIdx.x % gsum_x) * 256 + threadIdx.x;
+    if (4 * i4 >= dd) return;
+    const f32x4* p = reinterpret_cast<const f32x4*>(part + (int64_t)bh * nch * dd) + i4;
+    f32x4 s = first ? f32x4{0.f, 0.f, 0.f, 0.f} : reinterpret_cast<const f32x4*>(gr + (int64_t)bh * dd)[i4];
+    for (int c = 0; c < nch; ++c) s += p[(int64_t)c * (dd / 4)];
+    reinterpret_cast<f32x4*>(gr + (int64_t)bh * dd)[i4] = s;
+    return;
+  }
+  const int64_t stride = (int64_t)(gridDim.x - n_gsum) * 256;
+  for (int64_t i = (int64_t)(blockIdx.x - n_gsum) * 256 + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<f32x4*>(dq)[i] += reinterpret_cast<const f32x4*>(dq_read)[i];
 }
 
 // End of a frame's backward, per (head, 16 x 16 output tile), streams in order:
@@ -1227,9 +1273,12 @@ hipError_t launch_bwd_stage_d(BwdStage stage, const BwdPassArgs& a, hipStream_t 
   const f16* doh = static_cast<const f16*>(a.do_h);
   const int nch = (a.T + kTokChunk - 1) / kTokChunk;
   switch (stage) {
-    case BwdStage::kRead:
-      hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(xcd_grid(nch * BH)), dim3(512), 0, stream, a.tok);
+    case BwdStage::kRead: {
+      BwdTokArgs t = a.tok;
+      t.dq = a.dq_read;
+      hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(xcd_grid(nch * BH)), dim3(512), 0, stream, t);
       break;
+    }
     case BwdStage::kPrep: {
       const int rows = a.B * a.T * a.H, rpb = 256 / (D / 4);
       hipLaunchKernelGGL(arl2_bwd_rowdot_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, stream, a.d_out,
@@ -1239,26 +1288,39 @@ hipError_t launch_bwd_stage_d(BwdStage stage, const BwdPassArgs& a, hipStream_t 
                          static_cast<f16*>(a.dot16), a.T, a.H, a.tp);
       break;
     }
-    case BwdStage::kDkdv: {
-      constexpr int kKeyGroups = 4;  // 32-key groups per work-group (times two roles: 8 waves)
-      const int nkb = (a.T + 32 * kKeyGroups - 1) / (32 * kKeyGroups);
-      hipLaunchKernelGGL((arl2_bwd_dkdv_kernel<D, kKeyGroups>), dim3(xcd_grid(nkb * BH)), dim3(128 * kKeyGroups), 0,
-                         stream, q, k, v, doh, static_cast<const f16*>(a.qt16), static_cast<const f16*>(a.dot16), a.lse,
-                         a.dvec, a.tok.dk, a.tok.dv, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
+    case BwdStage::kAttn: {
+      BwdAttnArgs A;
+      A.q = q;
+      A.k = k;
+      A.v = v;
+      A.doh = doh;
+      A.v16 = static_cast<const f16*>(a.v16);
+      A.kt16 = static_cast<const f16*>(a.kt16);
+      A.qt16 = static_cast<const f16*>(a.qt16);
+      A.dot16 = static_cast<const f16*>(a.dot16);
+      A.lse = a.lse;
+      A.dvec = a.dvec;
+      A.dk = a.tok.dk;
+      A.dv = a.tok.dv;
+      A.dq = a.tok.dq;
+      A.T = a.T;
+      A.H = a.H;
+      A.BH = BH;
+      A.tp = a.tp;
+      A.scale = a.scale;
+      A.scale_log2 = a.scale_log2;
+      const int nb = (a.T + 127) / 128;  // 128-key (dK/dV) and 128-query (dQ) blocks per head
+      hipLaunchKernelGGL(arl2_bwd_attn_kernel<D>, dim3(2 * xcd_grid(nb * BH)), dim3(512), 0, stream, A);
       break;
     }
-    case BwdStage::kDq: {
-      constexpr int kDqGroups = 4;  // 32-query groups per work-group (times two key halves: 8 waves)
-      const int nqb = (a.T + 32 * kDqGroups - 1) / (32 * kDqGroups);
-      hipLaunchKernelGGL((arl2_bwd_dq_kernel<D, kDqGroups>), dim3(xcd_grid(nqb * BH)), dim3(128 * kDqGroups), 0,
-                         stream, q, k, static_cast<const f16*>(a.v16), static_cast<const f16*>(a.kt16), doh, a.lse,
-                         a.dvec, a.tok.dq, a.T, a.H, BH, a.tp, a.scale, a.scale_log2);
+    case BwdStage::kFinish: {
+      const int gsum_x = (D * D / 4 + 255) / 256, n_gsum = gsum_x * BH;
+      const int64_t n4 = (int64_t)a.B * a.T * a.H * D / 4;
+      const int n_add = (int)std::min<int64_t>((n4 + 255) / 256, 1024);
+      hipLaunchKernelGGL(arl2_bwd_finish_kernel, dim3(n_gsum + n_add), dim3(256), 0, stream, a.tok.part, a.gr, D * D,
+                         nch, a.gr_first ? 1 : 0, gsum_x, n_gsum, a.tok.dq, a.dq_read, n4);
       break;
     }
-    case BwdStage::kGsum:
-      hipLaunchKernelGGL(arl2_bwd_gsum_kernel, dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, stream, a.tok.part,
-                         a.gr, D * D, nch, a.gr_first ? 1 : 0);
-      break;
     default:
       return hipErrorInvalidValue;
   }

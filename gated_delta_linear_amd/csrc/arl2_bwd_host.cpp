@@ -28,6 +28,7 @@ struct arl2_bwd {
   float* o_sm = nullptr;       // recomputed softmax-branch output of a pass, fp32 [B][T][H][d]
   float* lse = nullptr;        // its rows' log-sum-exp, [B][H][T]
   float* dvec = nullptr;       // dO . O per row, [B][H][T]
+  float* dq_read = nullptr;    // a pass's inter-frame read part of dq, [B][T][H][d]
   void* do_h = nullptr;        // d_out in fp16
   void* v16 = nullptr;         // the pass's v in fp16, [B][T][H][d]; k^T, q^T, dO^T in fp16, [B][H][d][tp]
   void* kt16 = nullptr;
@@ -48,11 +49,11 @@ struct arl2_bwd {
   bool have_last_stream = false;
   hipEvent_t handoff = nullptr;
   // A second stream of the object's own (default priority, not blocking with the null stream):
-  // a pass's inter-frame read and its dQ kernel run there, beside the softmax recompute and the
-  // dK/dV kernel on the caller's stream, on the CUs those leave idle.  Forked from and joined
-  // back into the caller's stream within each call.
+  // a pass's inter-frame read runs there, beside the softmax recompute on the caller's stream,
+  // on the CUs that one leaves idle.  Forked from and joined back into the caller's stream
+  // within each call.
   hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_prep = nullptr, ev_join = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -61,10 +62,10 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 void release_sync_objects(arl2_bwd* g) {
   if (g->side) (void)hipStreamDestroy(g->side);
-  for (hipEvent_t ev : {g->handoff, g->ev_fork, g->ev_prep, g->ev_join})
+  for (hipEvent_t ev : {g->handoff, g->ev_fork, g->ev_join})
     if (ev) (void)hipEventDestroy(ev);
   g->side = nullptr;
-  g->handoff = g->ev_fork = g->ev_prep = g->ev_join = nullptr;
+  g->handoff = g->ev_fork = g->ev_join = nullptr;
 }
 
 // `waiter` waits for what `signaller` has enqueued so far
@@ -203,7 +204,7 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
   const size_t hmat = align_up(H * d * d * 4), hmatbf = align_up(H * d * d * 2);
   const size_t rpart = align_up(BH * g->nch * d * d * 4), wpart = align_up(BH * g->nch * 3 * d * d * 4);
   const size_t kt_bf = align_up(BH * d * (size_t)arl2::bwd_key_pitch(c.tokens_per_frame) * 2);
-  g->bytes = tok_f32 + 2 * row_f32 + 2 * tok_bf + 3 * kt_bf + 3 * mat + rpart + wpart + 8 * matbf + 6 * hmatbf + 3 * hmat;
+  g->bytes = 2 * tok_f32 + 2 * row_f32 + 2 * tok_bf + 3 * kt_bf + 3 * mat + rpart + wpart + 8 * matbf + 6 * hmatbf + 3 * hmat;
   if ((e = hipMalloc(&g->slab, g->bytes)) != hipSuccess) {
     (void)hipGetLastError();
     const size_t want = g->bytes;
@@ -212,6 +213,7 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
   }
   char* p = static_cast<char*>(g->slab);
   g->o_sm = reinterpret_cast<float*>(p); p += tok_f32;
+  g->dq_read = reinterpret_cast<float*>(p); p += tok_f32;
   g->lse = reinterpret_cast<float*>(p); p += row_f32;
   g->dvec = reinterpret_cast<float*>(p); p += row_f32;
   g->do_h = p; p += tok_bf;
@@ -238,7 +240,7 @@ arl2_status arl2_bwd_create(const arl2_config* cfg, const void* phi_q, const voi
     delete g;
     return fail(ARL2_E_HIP, "%s: %s", what, hipGetErrorString(err));
   };
-  for (hipEvent_t* ev : {&g->handoff, &g->ev_fork, &g->ev_prep, &g->ev_join})
+  for (hipEvent_t* ev : {&g->handoff, &g->ev_fork, &g->ev_join})
     if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return bail(e, "hipEventCreate");
   if ((e = hipStreamCreateWithFlags(&g->side, hipStreamNonBlocking)) != hipSuccess) return bail(e, "hipStreamCreate");
   if ((e = hipMemcpyAsync(g->phi_q, phi_q, H * d * d * 2, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
@@ -328,10 +330,10 @@ arl2_status arl2_bwd_pass(arl2_bwd* g, const void* q, const void* k, const void*
   a.T = g->cfg.tokens_per_frame;
   a.scale = g->scale;
   a.scale_log2 = g->scale_log2;
-  // Caller's stream: S fragments | recompute, prep ........ | dK/dV | (join) gsum
-  // side stream:                  (fork) read | (prep done) dQ |
-  // The read overwrites dq and the dQ kernel adds to it (one fp32 sum of two terms, the same in
-  // either order).  Each wait is enqueued after the record it waits for.
+  a.dq_read = g->dq_read;
+  // Caller's stream: S fragments | recompute | prep | dK, dV, dQ | (join) gr sums, dq += read's part
+  // side stream:                 (fork) read (dq_read, chunk partials of Q^T dO) |
+  // Each wait is enqueued after the record it waits for.
   using arl2::BwdStage;
   hipError_t e;
   if ((st = frags(g, s_prev, false, stream))) return st;
@@ -341,12 +343,11 @@ arl2_status arl2_bwd_pass(arl2_bwd* g, const void* q, const void* k, const void*
   if ((st = after_launch(g, arl2::launch_fwd(g->d, f, nullptr, stream), stream, "softmax recompute"))) return st;
   if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kPrep, a, stream), stream, "attention backward prep")))
     return st;
-  if ((e = order_after(g->ev_prep, stream, g->side)) != hipSuccess) return hip_fail(g, e, "stream fork");
-  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kDq, a, g->side), g->side, "dQ backward"))) return st;
-  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kDkdv, a, stream), stream, "dK/dV backward")))
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kAttn, a, stream), stream, "attention backward")))
     return st;
   if ((e = order_after(g->ev_join, g->side, stream)) != hipSuccess) return hip_fail(g, e, "stream join");
-  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kGsum, a, stream), stream, "Q^T dO sums"))) return st;
+  if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kFinish, a, stream), stream, "pass backward sums")))
+    return st;
   g->gr_valid = true;
   return ARL2_OK;
 }

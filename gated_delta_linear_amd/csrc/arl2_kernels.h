@@ -221,17 +221,17 @@ struct BwdPassArgs {
   void* qt16;
   void* dot16;
   int tp;                 // T rounded up to whole 64-key blocks
+  float* dq_read;         // workspace: the inter-frame read's part of dq, [B][T][H][d]
   int B, H, T;
   float scale, scale_log2;
 };
 // The pass backward in stages, which the host orders on two streams:
-//   kRead: the inter-frame read (needs the S fragments): dq = its part, and the chunk partials of Q^T dO;
-//   kPrep: dO . O per row and dO in fp16, then the fp16 operands of the attention kernels (needs
-//          the recomputed softmax output and log-sum-exp);
-//   kDkdv: dK, dV of the softmax branch (needs kPrep; overwrites dk, dv);
-//   kDq:   dQ of the softmax branch, added to dq (needs kPrep and kRead);
-//   kGsum: the chunk partials summed into gr (needs kRead).
-enum class BwdStage { kRead, kPrep, kDkdv, kDq, kGsum };
+//   kRead:   the inter-frame read (needs the S fragments): dq_read, and the chunk partials of Q^T dO;
+//   kPrep:   dO . O per row and dO in fp16, then the fp16 operands of the attention kernels (needs
+//            the recomputed softmax output and log-sum-exp);
+//   kAttn:   dK, dV and dQ of the softmax branch in one launch (needs kPrep; overwrites dk, dv, dq);
+//   kFinish: the chunk partials summed into gr, and dq += dq_read (needs kRead and kAttn).
+enum class BwdStage { kRead, kPrep, kAttn, kFinish };
 hipError_t launch_bwd_stage(int d, BwdStage stage, const BwdPassArgs& a, hipStream_t stream);
 int bwd_key_pitch(int T);  // tp: T rounded up to a multiple of 64
 
