@@ -1179,81 +1179,88 @@ __global__ __launch_bounds__(256) void arl2_bwd_finish_kernel(const float* __res
     reinterpret_cast<f32x4*>(dq)[i] += reinterpret_cast<const f32x4*>(dq_read)[i];
 }
 
-// End of a frame's backward, per (head, 16 x 16 output tile), streams in order:
-//   dS_{N-1} = alpha G - sum_chunks K'^T dR + phi_q^T Gr,   dalpha = <G, S_{N-1}>,
+// End of a frame's backward, per (head, strip of RW = 2048 / d rows of the d x d outputs), streams
+// in order:
+//   dS_{N-1} = alpha G - sum_chunks K'^T dR + phi_q^T Gr,   dalpha = <G, S_{N-1}> (strip 0),
 //   dphi_q += Gr S^T,  dphi_k += sum_chunks K^T dU,  dphi_v += sum_chunks V^T dR.
-// Thread t owns element (t / 16, t % 16) of the tile; the strips of Gr, S and phi_q that the
-// d-long dot products read come through LDS.
+// 512 threads (two waves per SIMD); thread t owns row RW strip + t / (d / 4) and the 4 columns
+// 4 (t mod d / 4) ..: the chunk partials come as float4s, and the d-long dot products read
+// phi_q's column strip, Gr and S^T from LDS (per k: two scalars and two float4 for 8
+// multiply-adds).
 template <int D>
-__global__ __launch_bounds__(256) void arl2_bwd_frame_kernel(const BwdFrameArgs a) {
-  constexpr int NB = D / 16, CP = 17, RP = D + 4;
-  __shared__ float gcol[D * CP];  // Gr[k][16 ct + c]
-  __shared__ float phc[D * CP];   // phi_q[k][16 rt + r]
-  __shared__ __align__(16) float grow[16 * RP];  // Gr[16 rt + r][k]
-  __shared__ __align__(16) float srow[16 * RP];  // S[16 ct + c][k]
-  __shared__ float red[256];
-  const int ct = blockIdx.x, rt = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
-  const int r = tid / 16, c = tid % 16, row = 16 * rt + r, col = 16 * ct + c;
+__global__ __launch_bounds__(512) void arl2_bwd_frame_kernel(const BwdFrameArgs a) {
+  constexpr int NT = 512, NB = D / 16, NC = D / 4, RW = NT / NC, GP = D + 4;  // threads per row; rows; LDS pitch
+  __shared__ __align__(16) float phc[D * RW];  // phi_q[k][RW rt + r]
+  __shared__ __align__(16) float grf[D * GP];  // Gr[i][j]
+  __shared__ __align__(16) float stf[D * GP];  // S^T[k][j] = S[j][k]
+  __shared__ float red[NT];
+  const int rt = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int r = tid / NC, c0 = 4 * (tid % NC), row = RW * rt + r;
   const int64_t dd = (int64_t)D * D;
   if (a.gr) {
     const bf16* ph = static_cast<const bf16*>(a.phi_q) + h * dd;
-    for (int i = tid; i < 16 * D; i += 256) phc[(i / 16) * CP + i % 16] = (float)ph[(i / 16) * D + 16 * rt + i % 16];
+    for (int i = tid; i < D * RW; i += NT) phc[i] = (float)ph[(i / RW) * D + RW * rt + i % RW];
   }
-  float aq = 0.f, ak = 0.f, av = 0.f;
+  f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, av = aq;
   for (int b = 0; b < a.B; ++b) {
     const int64_t bh = (int64_t)b * a.H + h;
     const float* G = a.g + bh * dd;
     const float* S = a.s_prev + bh * dd;
-    // the 16-column strips of the three sums, chunk after chunk ([bh][sum][strip][chunk][row][16])
-    const float* part = a.part + ((bh * 3) * NB + ct) * a.chunks * D * 16 + row * 16 + c;
+    // the three sums' partials, [bh][sum][16-column strip][chunk][row][16]: this thread's 4
+    // columns sit in strip c0 / 16 at offset c0 % 16
+    const float* part = a.part + ((bh * 3) * NB + c0 / 16) * a.chunks * D * 16 + row * 16 + c0 % 16;
     const int64_t pstride = (int64_t)NB * a.chunks * D * 16;  // from one sum to the next
-    float ds = a.alpha[bh] * G[row * D + col];
-#pragma unroll 8
+    f32x4 ds = a.alpha[bh] * *reinterpret_cast<const f32x4*>(G + row * D + c0);
+#pragma unroll 4
     for (int ch = 0; ch < a.chunks; ++ch) {
       const float* p = part + (int64_t)ch * D * 16;
-      ds -= p[0];
-      av += p[pstride];
-      ak += p[2 * pstride];
+      ds -= *reinterpret_cast<const f32x4*>(p);
+      av += *reinterpret_cast<const f32x4*>(p + pstride);
+      ak += *reinterpret_cast<const f32x4*>(p + 2 * pstride);
     }
     if (a.gr) {
       const float* gr = a.gr + bh * dd;
-      __syncthreads();  // the previous stream's strips are no longer read
+      __syncthreads();  // the previous stream's Gr and S^T are no longer read
+      for (int i = tid; i < D * D / 4; i += NT) {
+        const int rr = i / (D / 4), cc = 4 * (i % (D / 4));
+        *reinterpret_cast<f32x4*>(grf + rr * GP + cc) = *reinterpret_cast<const f32x4*>(gr + rr * D + cc);
+        // S^T: consecutive threads take consecutive rows of S, so that the transposed stores of
+        // a wave hit consecutive banks
+        const int sr = i % D, sc = 4 * (i / D);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(S + sr * D + sc);
 #pragma unroll
-      for (int it = 0; it < 16 * D / 256; ++it) {
-        const int i = tid + 256 * it;
-        gcol[(i / 16) * CP + i % 16] = gr[(i / 16) * D + 16 * ct + i % 16];
-        grow[(i / D) * RP + i % D] = gr[(16 * rt + i / D) * D + i % D];
-        srow[(i / D) * RP + i % D] = S[(16 * ct + i / D) * D + i % D];
+        for (int e = 0; e < 4; ++e) stf[(sc + e) * GP + sr] = sv[e];
       }
       __syncthreads();
 #pragma unroll 8
       for (int k = 0; k < D; ++k) {
-        ds += phc[k * CP + r] * gcol[k * CP + c];   // (phi_q^T Gr)[row][col]
-        aq += grow[r * RP + k] * srow[c * RP + k];  // (Gr S^T)[row][col]
+        const float pq = phc[k * RW + r], gq = grf[row * GP + k];
+        ds += pq * *reinterpret_cast<const f32x4*>(grf + k * GP + c0);  // (phi_q^T Gr)[row][col]
+        aq += gq * *reinterpret_cast<const f32x4*>(stf + k * GP + c0);  // (Gr S^T)[row][col]
       }
     }
-    a.ds_prev[bh * dd + row * D + col] = ds;
-    if (ct == 0 && rt == 0) {  // dalpha over the whole matrix (all loads of a thread in flight at once)
-      float s = 0.f;
+    *reinterpret_cast<f32x4*>(a.ds_prev + bh * dd + row * D + c0) = ds;
+    if (rt == 0) {  // dalpha over the whole matrix (all loads of a thread in flight at once)
+      float sum = 0.f;
 #pragma unroll
-      for (int it = 0; it < D * D / 1024; ++it) {
-        const int i = tid + 256 * it;
+      for (int it = 0; it < D * D / (4 * NT); ++it) {
+        const int i = tid + NT * it;
         const f32x4 x = reinterpret_cast<const f32x4*>(G)[i], y = reinterpret_cast<const f32x4*>(S)[i];
-        s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        sum += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
       }
-      red[tid] = s;
+      red[tid] = sum;
       __syncthreads();
-      for (int w = 128; w > 0; w >>= 1) {
+      for (int w = NT / 2; w > 0; w >>= 1) {
         if (tid < w) red[tid] += red[tid + w];
         __syncthreads();
       }
       if (tid == 0) a.dalpha[bh] = red[0];
     }
   }
-  const int64_t o = (int64_t)h * dd + row * D + col;
-  a.dphi_q[o] += aq;
-  a.dphi_k[o] += ak;
-  a.dphi_v[o] += av;
+  const int64_t o = (int64_t)h * dd + row * D + c0;
+  *reinterpret_cast<f32x4*>(a.dphi_q + o) += aq;
+  *reinterpret_cast<f32x4*>(a.dphi_k + o) += ak;
+  *reinterpret_cast<f32x4*>(a.dphi_v + o) += av;
 }
 
 // dst[i] = src ? src[i] : 0 (n4 float4 elements); a kernel rather than a memset node, so that the
@@ -1337,7 +1344,7 @@ template <int D>
 hipError_t launch_bwd_commit_d(const BwdTokArgs& t, const BwdFrameArgs& f, hipStream_t stream) {
   const int nch = (t.T + kTokChunk - 1) / kTokChunk;
   hipLaunchKernelGGL(arl2_bwd_write_kernel<D>, dim3(xcd_grid(nch * t.B * t.H)), dim3(512), 0, stream, t);
-  hipLaunchKernelGGL(arl2_bwd_frame_kernel<D>, dim3(D / 16, D / 16, t.H), dim3(256), 0, stream, f);
+  hipLaunchKernelGGL(arl2_bwd_frame_kernel<D>, dim3(D / (2048 / D), t.H), dim3(512), 0, stream, f);
   return hipGetLastError();
 }
 
