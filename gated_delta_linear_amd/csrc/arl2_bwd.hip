@@ -903,6 +903,35 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
     for (int i = 0; i < 4; ++i) part[(16 * mb + 4 * g + i) * D + 16 * (nb0 + n) + l16] = p[n][i];
 }
 
+// B fragments of one 16-column block of NO d x d operands kept in fragment order, every k-step.
+template <int D, int NO>
+struct FragSet {
+  bf16x8 f[NO][BwdShape<D>::KS];
+};
+
+// body(nb, fragments of block nb) for nb = 0 .. d/16 - 1, with block nb + 1's fragment loads
+// issued before block nb's products (two register sets), so that each block's L2 latency hides
+// behind the previous block's MFMAs instead of every MFMA waiting for its own load.
+template <int D, int NO, class Body>
+__device__ __forceinline__ void pipelined_blocks(const bf16* const (&ops)[NO], int lane, Body&& body) {
+  constexpr int KS = BwdShape<D>::KS, NB = BwdShape<D>::NB;
+  FragSet<D, NO> fs[2];
+  auto load = [&](int nb, FragSet<D, NO>& f) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) f.f[o][s] = frag<D>(ops[o], s, nb, lane);
+  };
+  load(0, fs[0]);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (nb + 1 < NB) load(nb + 1, fs[(nb + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    body(nb, fs[nb & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // State write of one frame, per (stream, head, 128-token chunk); wave w owns tokens 16 w ..
 // 16 w + 15.  Per token: U = k phi_k, K' = U / max(|U|, eps), V' = v phi_v, R = V' - K' S,
 // X3 = R G^T, X = K' G, dbeta = x . r, dR = beta X, dK' = beta X3 - dR S^T, dU; dv += dR phi_v^T,
@@ -937,13 +966,14 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
   }
   // C registers: lane l, register i <-> token r0 + 4 (l / 16) + i, feature 16 nb + l % 16
   f32x4 kp[NB];
+  {
+    const bf16* const ops[1] = {phik};
+    pipelined_blocks<D, 1>(ops, lane, [&](int nb, const FragSet<D, 1>& f) {
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) u = mfma16(ka[s], frag<D>(phik, s, nb, lane), u);
-    kp[nb] = u;
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int s = 0; s < KS; ++s) u = mfma16(ka[s], f.f[0][s], u);
+      kp[nb] = u;
+    });
   }
   float nrm[4], inv[4], bet[4];
 #pragma unroll
@@ -961,23 +991,23 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) kp[nb][i] *= inv[i];
     store_rows(abuf, LF, r0, g, 16 * nb + l16, kp[nb]);
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
   }
   __syncthreads();
   bf16x8 kh[KS], kl[KS];  // K' as split A fragments
 #pragma unroll
   for (int s = 0; s < KS; ++s) row_frag<D>(abuf, r0 + l16, 32 * s + 8 * g, kh[s], kl[s]);
   // R = V' - K' S with V' = v phi_v, into bbuf
+  {
+    const bf16* const ops[3] = {phiv, s_hi, s_lo};
+    pipelined_blocks<D, 3>(ops, lane, [&](int nb, const FragSet<D, 3>& f) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      w = mfma16(va[s], frag<D>(phiv, s, nb, lane), w);
-      c = mfma3(c, kh[s], kl[s], frag<D>(s_hi, s, nb, lane), frag<D>(s_lo, s, nb, lane));
-    }
-    store_rows(bbuf, LF, r0, g, 16 * nb + l16, w - c);
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int s = 0; s < KS; ++s) {
+        w = mfma16(va[s], f.f[0][s], w);
+        c = mfma3(c, kh[s], kl[s], f.f[1][s], f.f[2][s]);
+      }
+      store_rows(bbuf, LF, r0, g, 16 * nb + l16, w - c);
+    });
   }
   __syncthreads();
   // X3 = R G^T (becomes dK')
@@ -986,29 +1016,29 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
     bf16x8 rh[KS], rl[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) row_frag<D>(bbuf, r0 + l16, 32 * s + 8 * g, rh[s], rl[s]);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    const bf16* const ops[2] = {gt_hi, gt_lo};
+    pipelined_blocks<D, 2>(ops, lane, [&](int nb, const FragSet<D, 2>& f) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) c = mfma3(c, rh[s], rl[s], frag<D>(gt_hi, s, nb, lane), frag<D>(gt_lo, s, nb, lane));
+      for (int s = 0; s < KS; ++s) c = mfma3(c, rh[s], rl[s], f.f[0][s], f.f[1][s]);
       dkp[nb] = c;
-      if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
-    }
+    });
   }
   // X = K' G; dbeta = x . r; dR = beta X
   f32x4 dr[NB];
   float db[4] = {0.f, 0.f, 0.f, 0.f};
+  {
+    const bf16* const ops[2] = {g_hi, g_lo};
+    pipelined_blocks<D, 2>(ops, lane, [&](int nb, const FragSet<D, 2>& f) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KS; ++s) c = mfma3(c, kh[s], kl[s], f.f[0][s], f.f[1][s]);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) c = mfma3(c, kh[s], kl[s], frag<D>(g_hi, s, nb, lane), frag<D>(g_lo, s, nb, lane));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      db[i] += c[i] * bbuf[(r0 + 4 * g + i) * LF + 16 * nb + l16];  // x . r
-      dr[nb][i] = bet[i] * c[i];
-    }
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int i = 0; i < 4; ++i) {
+        db[i] += c[i] * bbuf[(r0 + 4 * g + i) * LF + 16 * nb + l16];  // x . r
+        dr[nb][i] = bet[i] * c[i];
+      }
+    });
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1025,17 +1055,18 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
   for (int s = 0; s < KS; ++s) row_frag<D>(bbuf, r0 + l16, 32 * s + 8 * g, dh[s], dl[s]);
   // dK' = beta X3 - dR S^T; dU; dv += dR phi_v^T
   float cdot[4] = {0.f, 0.f, 0.f, 0.f};
+  {
+    const bf16* const ops[2] = {st_hi, st_lo};
+    pipelined_blocks<D, 2>(ops, lane, [&](int nb, const FragSet<D, 2>& f) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KS; ++s) c = mfma3(c, dh[s], dl[s], f.f[0][s], f.f[1][s]);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) c = mfma3(c, dh[s], dl[s], frag<D>(st_hi, s, nb, lane), frag<D>(st_lo, s, nb, lane));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dkp[nb][i] = bet[i] * dkp[nb][i] - c[i];
-      cdot[i] += abuf[(r0 + 4 * g + i) * LF + 16 * nb + l16] * dkp[nb][i];  // k' . dK'
-    }
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int i = 0; i < 4; ++i) {
+        dkp[nb][i] = bet[i] * dkp[nb][i] - c[i];
+        cdot[i] += abuf[(r0 + 4 * g + i) * LF + 16 * nb + l16] * dkp[nb][i];  // k' . dK'
+      }
+    });
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1047,21 +1078,31 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       dkp[nb][i] = (dkp[nb][i] - abuf[(r0 + 4 * g + i) * LF + 16 * nb + l16] * cdot[i]) * inv[i];  // dU
+  {
+    // dv before this kernel's share, loaded ahead of the products rather than one element at a
+    // time after each
+    float prior[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 f = frag<D>(phivt, s, nb, lane);
-      c = mfma16(dh[s], f, c);
-      c = mfma16(dl[s], f, c);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + r0 + 4 * g + i;
+        prior[nb][i] = t < T ? a.dv[base + (int64_t)t * rs + 16 * nb + l16] : 0.f;
+      }
+    const bf16* const ops[1] = {phivt};
+    pipelined_blocks<D, 1>(ops, lane, [&](int nb, const FragSet<D, 1>& f) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + r0 + 4 * g + i;
-      if (t < T) a.dv[base + (int64_t)t * rs + 16 * nb + l16] += c[i];
-    }
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int s = 0; s < KS; ++s) {
+        c = mfma16(dh[s], f.f[0][s], c);
+        c = mfma16(dl[s], f.f[0][s], c);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + r0 + 4 * g + i;
+        if (t < T) a.dv[base + (int64_t)t * rs + 16 * nb + l16] = prior[nb][i] + c[i];
+      }
+    });
   }
   // chunk sums K'^T dR and V^T dR: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1)
   const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
@@ -1116,21 +1157,31 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
   // dk += dU phi_k^T
 #pragma unroll
   for (int s = 0; s < KS; ++s) row_frag<D>(abuf, r0 + l16, 32 * s + 8 * g, dh[s], dl[s]);
+  {
+    // dk before this kernel's share, loaded ahead of the products rather than one element at a
+    // time after each
+    float prior[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 f = frag<D>(phikt, s, nb, lane);
-      c = mfma16(dh[s], f, c);
-      c = mfma16(dl[s], f, c);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + r0 + 4 * g + i;
+        prior[nb][i] = t < T ? a.dk[base + (int64_t)t * rs + 16 * nb + l16] : 0.f;
+      }
+    const bf16* const ops[1] = {phikt};
+    pipelined_blocks<D, 1>(ops, lane, [&](int nb, const FragSet<D, 1>& f) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + r0 + 4 * g + i;
-      if (t < T) a.dk[base + (int64_t)t * rs + 16 * nb + l16] += c[i];
-    }
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int s = 0; s < KS; ++s) {
+        c = mfma16(dh[s], f.f[0][s], c);
+        c = mfma16(dl[s], f.f[0][s], c);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + r0 + 4 * g + i;
+        if (t < T) a.dk[base + (int64_t)t * rs + 16 * nb + l16] = prior[nb][i] + c[i];
+      }
+    });
   }
   // chunk sum K^T dU
   {
