@@ -816,6 +816,35 @@ __device__ __forceinline__ float group16_sum(float x) {
   return x;
 }
 
+// B fragments of one 16-column block of NO d x d operands kept in fragment order, every k-step.
+template <int D, int NO>
+struct FragSet {
+  bf16x8 f[NO][BwdShape<D>::KS];
+};
+
+// body(nb, fragments of block nb) for nb = 0 .. d/16 - 1, with block nb + 1's fragment loads
+// issued before block nb's products (two register sets), so that each block's L2 latency hides
+// behind the previous block's MFMAs instead of every MFMA waiting for its own load.
+template <int D, int NO, class Body>
+__device__ __forceinline__ void pipelined_blocks(const bf16* const (&ops)[NO], int lane, Body&& body) {
+  constexpr int KS = BwdShape<D>::KS, NB = BwdShape<D>::NB;
+  FragSet<D, NO> fs[2];
+  auto load = [&](int nb, FragSet<D, NO>& f) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) f.f[o][s] = frag<D>(ops[o], s, nb, lane);
+  };
+  load(0, fs[0]);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (nb + 1 < NB) load(nb + 1, fs[(nb + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    body(nb, fs[nb & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Inter-frame read of one pass, per (stream, head, 128-token chunk); wave w owns tokens 16 w ..
 // 16 w + 15 of the chunk.  dq = (dO S^T) phi_q^T (the dQ kernel adds the softmax branch's part
 // later), and the chunk's partial of Gr = Q^T dO.
@@ -851,32 +880,33 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
     const float x[8] = {u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
     split8(x, xh[s], xl[s]);
   }
+  {
+    const bf16* const ops[2] = {st_hi, st_lo};
+    pipelined_blocks<D, 2>(ops, lane, [&](int nb, const FragSet<D, 2>& f) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) y = mfma3(y, xh[s], xl[s], frag<D>(st_hi, s, nb, lane), frag<D>(st_lo, s, nb, lane));
-    store_rows(ybuf, LF, r0, g, 16 * nb + l16, y);
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int s = 0; s < KS; ++s) y = mfma3(y, xh[s], xl[s], f.f[0][s], f.f[1][s]);
+      store_rows(ybuf, LF, r0, g, 16 * nb + l16, y);
+    });
   }
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < KS; ++s) row_frag<D>(ybuf, r0 + l16, 32 * s + 8 * g, xh[s], xl[s]);
+  {
+    const bf16* const ops[1] = {pqt};
+    pipelined_blocks<D, 1>(ops, lane, [&](int nb, const FragSet<D, 1>& f) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KS; ++s) {
+        c = mfma16(xh[s], f.f[0][s], c);
+        c = mfma16(xl[s], f.f[0][s], c);
+      }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 f = frag<D>(pqt, s, nb, lane);
-      c = mfma16(xh[s], f, c);
-      c = mfma16(xl[s], f, c);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + r0 + 4 * g + i;
-      if (t < T) a.dq[base + (int64_t)t * rs + 16 * nb + l16] = c[i];
-    }
-    if (nb & 1) ARL2_BLOCK_FENCE();  // two blocks' loads in flight
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + r0 + 4 * g + i;
+        if (t < T) a.dq[base + (int64_t)t * rs + 16 * nb + l16] = c[i];
+      }
+    });
   }
   // Gr partial: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1) of Q^T dO
   const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
@@ -901,35 +931,6 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
   for (int n = 0; n < BPW; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[(16 * mb + 4 * g + i) * D + 16 * (nb0 + n) + l16] = p[n][i];
-}
-
-// B fragments of one 16-column block of NO d x d operands kept in fragment order, every k-step.
-template <int D, int NO>
-struct FragSet {
-  bf16x8 f[NO][BwdShape<D>::KS];
-};
-
-// body(nb, fragments of block nb) for nb = 0 .. d/16 - 1, with block nb + 1's fragment loads
-// issued before block nb's products (two register sets), so that each block's L2 latency hides
-// behind the previous block's MFMAs instead of every MFMA waiting for its own load.
-template <int D, int NO, class Body>
-__device__ __forceinline__ void pipelined_blocks(const bf16* const (&ops)[NO], int lane, Body&& body) {
-  constexpr int KS = BwdShape<D>::KS, NB = BwdShape<D>::NB;
-  FragSet<D, NO> fs[2];
-  auto load = [&](int nb, FragSet<D, NO>& f) {
-#pragma unroll
-    for (int o = 0; o < NO; ++o)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) f.f[o][s] = frag<D>(ops[o], s, nb, lane);
-  };
-  load(0, fs[0]);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    if (nb + 1 < NB) load(nb + 1, fs[(nb + 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
-    body(nb, fs[nb & 1]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 }
 
 // State write of one frame, per (stream, head, 128-token chunk); wave w owns tokens 16 w ..
