@@ -111,38 +111,6 @@ __device__ __forceinline__ f32x4 mfma3(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh,
 // loads of every block at once would need more registers than a wave has).
 #define ARL2_BLOCK_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// --- recompute helpers ----------------------------------------------------------------------
-
-// Dv[b][h][t] = dO . O over the row's features with dO rounded to fp16 (the attention backward's
-// MFMA operand, also written out), so that dS = P (dP - Dv) is the gradient of one consistent dO.
-// rows = B T H rows of d values.
-template <int D>
-__global__ __launch_bounds__(256) void arl2_bwd_rowdot_kernel(const float* __restrict__ d_out,
-                                                              const float* __restrict__ o_sm, f16* __restrict__ do_h,
-                                                              float* __restrict__ dvec, int rows, int T, int H) {
-  constexpr int TPR = D / 4, RPB = 256 / TPR;
-  const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR, li = threadIdx.x % TPR;
-  float s = 0.f;
-  if (row < rows) {
-    const int64_t o = (int64_t)row * D + 4 * li;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(d_out + o);
-    const f32x4 y = *reinterpret_cast<const f32x4*>(o_sm + o);
-    f16x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[e] = (f16)x[e];
-      s += (float)w[e] * y[e];  // the rounded dO, as dP = dO V^T sees it
-    }
-    *reinterpret_cast<f16x4*>(do_h + o) = w;
-  }
-#pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) s += __shfl_xor(s, m);
-  if (row < rows && li == 0) {
-    const int h = row % H, t = (row / H) % T, b = row / (H * T);
-    dvec[((int64_t)b * H + h) * T + t] = s;
-  }
-}
-
 // --- attention backward ---------------------------------------------------------------------
 // S = Q K^T in bf16 on the inputs as given; every other product in fp16 (P, dS and dO round with
 // a relative step of 2^-11, four times finer than bf16; the bf16 inputs convert exactly when
@@ -483,16 +451,22 @@ __device__ __forceinline__ void dkdv_body(const BwdAttnArgs& A, int item, unsign
 // [B][H][d][tp] of k, q and the fp16 dO: each head's features as rows of its tokens, 64-token
 // blocks (tokens past T zero), each 16-token group stored as its 4-token quads 0, 2, 1, 3 (the
 // order in which a 32x32x16 MFMA lane takes its 8 k-values when P or dS come straight from C
-// registers, so that a lane's A fragment is one 16-byte chunk).  One work-group per (stream, head, 64-token block); thread j moves
-// rows 4 (j % 16) .. + 3 of 8-feature chunk j / 16, transposing through LDS.
+// registers, so that a lane's A fragment is one 16-byte chunk).  The same pass also rounds dO to
+// fp16 (do_h, the attention backward's MFMA operand) and forms Dv[b][h][t] = dO . O over each
+// row's features with that rounded dO, so that dS = P (dP - Dv) is the gradient of one
+// consistent dO.  One work-group per (stream, head, 64-token block); thread j moves rows
+// 4 (j % 16) .. + 3 of 8-feature chunk j / 16, transposing through LDS; a row's dot product is
+// summed over its chunks in chunk order.
 template <int D>
 __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                           const bf16* __restrict__ v, const f16* __restrict__ doh,
-                                                           f16* __restrict__ v16, f16* __restrict__ kt16,
-                                                           f16* __restrict__ qt16, f16* __restrict__ dot16, int T,
-                                                           int H, int tp) {
+                                                           const bf16* __restrict__ v, const float* __restrict__ d_out,
+                                                           const float* __restrict__ o_sm, f16* __restrict__ doh,
+                                                           float* __restrict__ dvec, f16* __restrict__ v16,
+                                                           f16* __restrict__ kt16, f16* __restrict__ qt16,
+                                                           f16* __restrict__ dot16, int T, int H, int tp) {
   constexpr int CPR = D / 8, TPITCH = kAttnBlock + 8;  // chunks per row; transposing tiles' pitch (f16)
   __shared__ __align__(16) f16 tr[3][D * TPITCH];     // K^T, Q^T, dO^T of the block
+  __shared__ float dpart[kAttnBlock][CPR + 1];        // dO . O per row and chunk
   const int tid = threadIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, k0 = blockIdx.x * kAttnBlock;
   const int64_t rs = (int64_t)H * D, base = ((int64_t)b * T * H + h) * D;
   for (int j = tid; j < 16 * CPR; j += 256) {
@@ -502,13 +476,26 @@ __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restr
     for (int e = 0; e < 4; ++e) {
       const int t = k0 + 4 * rg + e;
       x[0][e] = x[1][e] = x[2][e] = f16x8{};
+      float dot = 0.f;
       if (t < T) {
         const int64_t o = base + (int64_t)t * rs + 8 * cc;
         x[0][e] = to_f16(ld_bf16x8(k + o));
         x[1][e] = to_f16(ld_bf16x8(q + o));
-        x[2][e] = ld_f16x8(doh + o);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(d_out + o), g1 = *reinterpret_cast<const f32x4*>(d_out + o + 4);
+        const f32x4 y0 = *reinterpret_cast<const f32x4*>(o_sm + o), y1 = *reinterpret_cast<const f32x4*>(o_sm + o + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[2][e][c] = (f16)g0[c];
+          x[2][e][4 + c] = (f16)g1[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dot += (float)x[2][e][c] * y0[c];  // the rounded dO, as dP = dO V^T sees it
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dot += (float)x[2][e][4 + c] * y1[c];
+        *reinterpret_cast<f16x8*>(doh + o) = x[2][e];
         *reinterpret_cast<f16x8*>(v16 + o) = to_f16(ld_bf16x8(v + o));
       }
+      dpart[4 * rg + e][cc] = dot;
     }
 #pragma unroll
     for (int m = 0; m < 3; ++m)
@@ -518,6 +505,12 @@ __global__ __launch_bounds__(256) void arl2_bwd_cvt16_kernel(const bf16* __restr
             f16x4{x[m][0][c], x[m][1][c], x[m][2][c], x[m][3][c]};
   }
   __syncthreads();
+  if (tid < kAttnBlock && k0 + tid < T) {
+    float dot = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPR; ++cc) dot += dpart[tid][cc];
+    dvec[(int64_t)bh * T + k0 + tid] = dot;
+  }
   f16* const dst[3] = {kt16, qt16, dot16};
   for (int j = tid; j < 3 * D * (kAttnBlock / 8); j += 256) {
     const int m = j / (D * (kAttnBlock / 8)), jj = j % (D * (kAttnBlock / 8));
@@ -1338,15 +1331,12 @@ hipError_t launch_bwd_stage_d(BwdStage stage, const BwdPassArgs& a, hipStream_t 
       hipLaunchKernelGGL(arl2_bwd_read_kernel<D>, dim3(xcd_grid(nch * BH)), dim3(512), 0, stream, t);
       break;
     }
-    case BwdStage::kPrep: {
-      const int rows = a.B * a.T * a.H, rpb = 256 / (D / 4);
-      hipLaunchKernelGGL(arl2_bwd_rowdot_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0, stream, a.d_out,
-                         a.o_sm, static_cast<f16*>(a.do_h), a.dvec, rows, a.T, a.H);
-      hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, q, k, v, doh,
-                         static_cast<f16*>(a.v16), static_cast<f16*>(a.kt16), static_cast<f16*>(a.qt16),
-                         static_cast<f16*>(a.dot16), a.T, a.H, a.tp);
+    case BwdStage::kPrep:
+      hipLaunchKernelGGL(arl2_bwd_cvt16_kernel<D>, dim3(a.tp / kAttnBlock, BH), dim3(256), 0, stream, q, k, v, a.d_out,
+                         a.o_sm, static_cast<f16*>(a.do_h), a.dvec, static_cast<f16*>(a.v16),
+                         static_cast<f16*>(a.kt16), static_cast<f16*>(a.qt16), static_cast<f16*>(a.dot16), a.T, a.H,
+                         a.tp);
       break;
-    }
     case BwdStage::kAttn: {
       BwdAttnArgs A;
       A.q = q;

@@ -227,8 +227,8 @@ struct BwdPassArgs {
 };
 // The pass backward in stages, which the host orders on two streams:
 //   kRead:   the inter-frame read (needs the S fragments): dq_read, and the chunk partials of Q^T dO;
-//   kPrep:   dO . O per row and dO in fp16, then the fp16 operands of the attention kernels (needs
-//            the recomputed softmax output and log-sum-exp);
+//   kPrep:   dO in fp16, dO . O per row, and the fp16 operands of the attention kernels, in one
+//            kernel (needs the recomputed softmax output);
 //   kAttn:   dK, dV and dQ of the softmax branch in one launch (needs kPrep; overwrites dk, dv, dq);
 //   kFinish: the chunk partials summed into gr, and dq += dq_read (needs kRead and kAttn).
 enum class BwdStage { kRead, kPrep, kAttn, kFinish };
