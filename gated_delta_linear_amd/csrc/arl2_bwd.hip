@@ -16,23 +16,24 @@
 //                   dU_t = (dK'_t - k'_t (k'_t . dK'_t)) / |u_t| (or dK'_t / eps), dK += dU phi_k^T,
 //                   dphi_k += K^T dU
 //
-// Kernels.  The attention backward runs as two MFMA kernels with no atomics (bitwise
-// reproducible), 8 waves per work-group, 32x32x16 MFMAs: dK, dV per 128-key block, four 32-key
-// groups in two wave roles each (scores, P and dV beside dP, dS and dK; P handed over through
-// LDS), and dQ per 128-query block, four 32-query groups times two key halves; 64-row blocks of
-// the other side stream through LDS and the scores are recomputed in each.  Every streamed tile
-// reaches LDS by direct-to-LDS buffer loads, two stages deep (block b + 1 is in flight while
-// block b is multiplied, one barrier per block), with rows chunk-swizzled so that the fragment
-// reads hit distinct banks; no thread converts or transposes anything on the way.  The operands
-// those loads need in another type or layout (V in fp16, and K^T, Q^T, dO^T in fp16, stored in
-// the order in which an MFMA lane takes its k-values) are written once per pass by a conversion
-// kernel.  The score products S = Q K^T run in bf16 on the inputs as given; the others (dP =
-// dO V^T, dV, dK, dQ) in fp16, where P, dS and dO round with a relative step of 2^-11; all
-// accumulate in fp32.  The
+// Kernels.  The attention backward runs as one MFMA launch with no atomics (bitwise
+// reproducible), 8 waves per work-group, 32x32x16 MFMAs: dK, dV work-groups per 128-key block,
+// four 32-key groups in two wave roles each (scores, P and dV beside dP, dS and dK; P handed over
+// through LDS), then dQ work-groups per 128-query block, four 32-query groups times two key
+// halves; 64-row blocks of the other side stream through LDS and the scores are recomputed in
+// each.  Every streamed tile reaches LDS by direct-to-LDS buffer loads, two stages deep (block
+// b + 1 is in flight while block b is multiplied, one barrier per block), with rows
+// chunk-swizzled so that the fragment reads hit distinct banks; no thread converts or transposes
+// anything on the way.  The operands those loads need in another type or layout (dO, V in fp16,
+// and K^T, Q^T, dO^T in fp16, stored in the order in which an MFMA lane takes its k-values) are
+// written once per pass by a conversion kernel, which also forms dO . O per row.  The score
+// products S = Q K^T run in bf16 on the inputs as given; the others (dP = dO V^T, dV, dK, dQ) in
+// fp16, where P, dS and dO round with a relative step of 2^-11; all accumulate in fp32.  The
 // token kernels (inter read, state write) work per 128-token chunk with 16x16x32 MFMAs on
 // split-bf16 operands (hi + lo, three products per term), so that their d x d products keep
-// about fp32 accuracy as the forward's state write does; their sums over tokens leave the chunk
-// as partials that a per-head kernel adds in a fixed order.
+// about fp32 accuracy as the forward's state write does, each product's B fragments read from L2
+// one 16-column block ahead; their sums over tokens leave the chunk as partials that per-head
+// kernels add in a fixed order.
 #include <algorithm>
 #include <type_traits>
 
