@@ -63,7 +63,6 @@ struct BwdShape {
   static constexpr int KS = D / 32;          // 32-deep k-steps over features
   static constexpr int NB = D / 16;          // 16-wide blocks over features
   static constexpr int LF = D + 4;           // fp32 row pitch of the token kernels' row buffers
-  static constexpr int BPW = NB * NB / 8;    // 16x16 blocks of a d x d sum per wave (8 waves)
 };
 
 // B fragment (s, nb) of a d x d matrix kept in fragment order [s][nb][lane][8]: lane l holds
@@ -83,10 +82,6 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 
 // 8 bf16 inputs as fp16 (exact for magnitudes in [2^-14, 65504]; smaller ones keep an absolute
 // accuracy of 2^-25, larger ones become infinite and show up)
@@ -784,17 +779,33 @@ __device__ __forceinline__ void col_frag(const float* buf, int s, int col, int g
   split8(x, hi, lo);
 }
 
-// The same over rows of a bf16 [.][T][H][D] tensor in global memory (rows past T read as zero).
-__device__ __forceinline__ bf16x8 col_frag_global(const bf16* __restrict__ x, int64_t base, int64_t rs, int t0,
-                                                  int T, int col) {
+// The same over rows of a bf16 [.][T][H][D] tensor in global memory: r is a buffer resource
+// over one (stream, head) slice, rows [0, T) (rows past T lie outside it and read as zero), voff
+// the byte offset of the lane's first row and column, rs2 the row pitch in bytes; the row step
+// goes in the scalar offset, so that no load needs address arithmetic of its own.
+__device__ __forceinline__ bf16x8 col_frag_global(__amdgpu_buffer_rsrc_t r, int voff, int rs2) {
   bf16x8 a;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = t0 + j;
-    a[j] = t < T ? x[base + (int64_t)t * rs + col] : (bf16)0.f;
-  }
+  for (int j = 0; j < 8; ++j)
+    a[j] = __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, j * rs2, 0));
   return a;
 }
+
+// Buffer resource over rows [0, T) of one (stream, head) slice of a bf16 [B][T][H][D] tensor.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* x, int64_t base, int T, int64_t rs) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(static_cast<const bf16*>(x) + base), (short)0,
+                                           (int)(((int64_t)(T - 1) * rs + D) * 2), 0x00020000);
+}
+
+// Output blocks of a d x d chunk sum per wave: an MBW x NBW group, so that each column
+// fragment a wave splits from LDS feeds several blocks.
+template <int D>
+struct SumGroup {
+  static constexpr int NB = D / 16;
+  static constexpr int MBW = NB >= 8 ? 2 : 1, NBW = NB * NB / 8 / MBW;
+  static_assert((NB / MBW) * (NB / NBW) == 8, "one group per wave");
+};
 
 __device__ __forceinline__ void store_rows(float* buf, int ld, int r0, int g, int col, const f32x4& c) {
 #pragma unroll
@@ -845,7 +856,7 @@ __device__ __forceinline__ void pipelined_blocks(const bf16* const (&ops)[NO], i
 template <int D>
 __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) {
   using Sh = BwdShape<D>;
-  constexpr int KS = Sh::KS, NB = Sh::NB, LF = Sh::LF, BPW = Sh::BPW;
+  constexpr int KS = Sh::KS, NB = Sh::NB, LF = Sh::LF;
   __shared__ __align__(16) float ybuf[kTokChunk * LF];  // Y = dO S^T rows (each wave its own)
   __shared__ __align__(16) float dbuf[kTokChunk * LF];  // the chunk's dO rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
@@ -902,29 +913,41 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
       }
     });
   }
-  // Gr partial: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1) of Q^T dO
-  const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
-  f32x4 p[BPW];
+  // Gr partial: wave w owns an MBW x NBW group of the 16x16 blocks of Q^T dO
+  using SG = SumGroup<D>;
+  constexpr int MBW = SG::MBW, NBW = SG::NBW;
+  const int mb0 = MBW * (wave % (NB / MBW)), nb0 = NBW * (wave / (NB / MBW));
+  f32x4 p[MBW][NBW];
 #pragma unroll
-  for (int n = 0; n < BPW; ++n) p[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16* qg = static_cast<const bf16*>(a.q);
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) p[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rq = slice_rsrc<D>(a.q, base, T, rs);
+  const int rs2 = (int)(rs * 2);
 #pragma unroll
   for (int s = 0; s < kTokChunk / 32; ++s) {
-    const bf16x8 aq = col_frag_global(qg, base, rs, t0 + 32 * s + 8 * g, T, 16 * mb + l16);
+    bf16x8 aq[MBW];
 #pragma unroll
-    for (int n = 0; n < BPW; ++n) {
+    for (int i = 0; i < MBW; ++i) aq[i] = col_frag_global(rq, (t0 + 32 * s + 8 * g) * rs2 + 2 * (16 * (mb0 + i) + l16), rs2);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
       bf16x8 bh_, bl_;
-      col_frag<D>(dbuf, s, 16 * (nb0 + n) + l16, g, bh_, bl_);
-      p[n] = mfma16(aq, bh_, p[n]);
-      p[n] = mfma16(aq, bl_, p[n]);
+      col_frag<D>(dbuf, s, 16 * (nb0 + j) + l16, g, bh_, bl_);
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) {
+        p[i][j] = mfma16(aq[i], bh_, p[i][j]);
+        p[i][j] = mfma16(aq[i], bl_, p[i][j]);
+      }
     }
     ARL2_BLOCK_FENCE();
   }
   float* part = a.part + ((int64_t)bh * nch + chunk) * D * D;
 #pragma unroll
-  for (int n = 0; n < BPW; ++n)
+  for (int i = 0; i < MBW; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[(16 * mb + 4 * g + i) * D + 16 * (nb0 + n) + l16] = p[n][i];
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[(16 * (mb0 + i) + 4 * g + e) * D + 16 * (nb0 + j) + l16] = p[i][j][e];
 }
 
 // State write of one frame, per (stream, head, 128-token chunk); wave w owns tokens 16 w ..
@@ -934,7 +957,7 @@ __global__ __launch_bounds__(512) void arl2_bwd_read_kernel(const BwdTokArgs a) 
 template <int D>
 __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a) {
   using Sh = BwdShape<D>;
-  constexpr int KS = Sh::KS, NB = Sh::NB, LF = Sh::LF, BPW = Sh::BPW;
+  constexpr int KS = Sh::KS, NB = Sh::NB, LF = Sh::LF;
   __shared__ __align__(16) float abuf[kTokChunk * LF];  // K' rows, later dU rows
   __shared__ __align__(16) float bbuf[kTokChunk * LF];  // R rows, later dR rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
@@ -1077,13 +1100,13 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
     // dv before this kernel's share, loaded ahead of the products rather than one element at a
     // time after each
     float prior[NB][4];
+    float* rowp[4];  // the lane's column in rows t0 + r0 + 4 (l / 16) + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rowp[i] = a.dv + base + (int64_t)(t0 + r0 + 4 * g + i) * rs + l16;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + r0 + 4 * g + i;
-        prior[nb][i] = t < T ? a.dv[base + (int64_t)t * rs + 16 * nb + l16] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) prior[nb][i] = t0 + r0 + 4 * g + i < T ? rowp[i][16 * nb] : 0.f;
     const bf16* const ops[1] = {phivt};
     pipelined_blocks<D, 1>(ops, lane, [&](int nb, const FragSet<D, 1>& f) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -1095,55 +1118,75 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + r0 + 4 * g + i;
-        if (t < T) a.dv[base + (int64_t)t * rs + 16 * nb + l16] = prior[nb][i] + c[i];
+        if (t < T) rowp[i][16 * nb] = prior[nb][i] + c[i];
       }
     });
   }
-  // chunk sums K'^T dR and V^T dR: wave w owns the 16x16 blocks (mb, nb0 .. nb0 + BPW - 1)
-  const int mb = wave * BPW / NB, nb0 = wave * BPW % NB;
+  // chunk sums K'^T dR and V^T dR: wave w owns an MBW x NBW group of the 16x16 blocks
+  using SG = SumGroup<D>;
+  constexpr int MBW = SG::MBW, NBW = SG::NBW;
+  const int mb0 = MBW * (wave % (NB / MBW)), nb0 = NBW * (wave / (NB / MBW));
   // partial sum p of 16-column block nb at [bh][p][nb][chunk][row][16]: each (p, nb) strip of all
   // chunks is contiguous for the per-head kernel that adds them
-  auto pidx = [&](int p, int nb, int row) -> int64_t {
-    return ((((int64_t)bh * 3 + p) * NB + nb) * nch + chunk) * D * 16 + row * 16 + l16;
+  float* const pbase = a.part + (((int64_t)bh * 3 * NB) * nch + chunk) * D * 16 + l16;
+  auto pstore = [&](int p, const f32x4 (&acc)[MBW][NBW]) {
+#pragma unroll
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pbase[((p * NB + nb0 + j) * nch) * D * 16 + (16 * (mb0 + i) + 4 * g + e) * 16] = acc[i][j][e];
+  };
+  const int rs2 = (int)(rs * 2);
+  const __amdgpu_buffer_rsrc_t rkg = slice_rsrc<D>(a.k, base, T, rs), rvg = slice_rsrc<D>(a.v, base, T, rs);
+  // A fragments of the K or V columns of the wave's row blocks for 32-token step s (from global)
+  auto gcols = [&](__amdgpu_buffer_rsrc_t r, int s, bf16x8 (&out)[MBW]) {
+#pragma unroll
+    for (int i = 0; i < MBW; ++i) out[i] = col_frag_global(r, (t0 + 32 * s + 8 * g) * rs2 + 2 * (16 * (mb0 + i) + l16), rs2);
   };
   {
-    f32x4 p[BPW];
+    f32x4 p[MBW][NBW];
 #pragma unroll
-    for (int n = 0; n < BPW; ++n) p[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) p[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kTokChunk / 32; ++s) {
-      bf16x8 ah, al;
-      col_frag<D>(abuf, s, 16 * mb + l16, g, ah, al);
+      bf16x8 ah[MBW], al[MBW];
 #pragma unroll
-      for (int n = 0; n < BPW; ++n) {
+      for (int i = 0; i < MBW; ++i) col_frag<D>(abuf, s, 16 * (mb0 + i) + l16, g, ah[i], al[i]);
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
         bf16x8 bh_, bl_;
-        col_frag<D>(bbuf, s, 16 * (nb0 + n) + l16, g, bh_, bl_);
-        p[n] = mfma3(p[n], ah, al, bh_, bl_);
+        col_frag<D>(bbuf, s, 16 * (nb0 + j) + l16, g, bh_, bl_);
+#pragma unroll
+        for (int i = 0; i < MBW; ++i) p[i][j] = mfma3(p[i][j], ah[i], al[i], bh_, bl_);
         ARL2_BLOCK_FENCE();
       }
     }
+    pstore(0, p);
 #pragma unroll
-    for (int n = 0; n < BPW; ++n)
+    for (int i = 0; i < MBW; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.part[pidx(0, nb0 + n, 16 * mb + 4 * g + i)] = p[n][i];
-#pragma unroll
-    for (int n = 0; n < BPW; ++n) p[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NBW; ++j) p[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kTokChunk / 32; ++s) {
-      const bf16x8 av = col_frag_global(vg, base, rs, t0 + 32 * s + 8 * g, T, 16 * mb + l16);
+      bf16x8 av[MBW];
+      gcols(rvg, s, av);
 #pragma unroll
-      for (int n = 0; n < BPW; ++n) {
+      for (int j = 0; j < NBW; ++j) {
         bf16x8 bh_, bl_;
-        col_frag<D>(bbuf, s, 16 * (nb0 + n) + l16, g, bh_, bl_);
-        p[n] = mfma16(av, bh_, p[n]);
-        p[n] = mfma16(av, bl_, p[n]);
+        col_frag<D>(bbuf, s, 16 * (nb0 + j) + l16, g, bh_, bl_);
+#pragma unroll
+        for (int i = 0; i < MBW; ++i) {
+          p[i][j] = mfma16(av[i], bh_, p[i][j]);
+          p[i][j] = mfma16(av[i], bl_, p[i][j]);
+        }
         ARL2_BLOCK_FENCE();
       }
     }
-#pragma unroll
-    for (int n = 0; n < BPW; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a.part[pidx(1, nb0 + n, 16 * mb + 4 * g + i)] = p[n][i];
+    pstore(1, p);
   }
   __syncthreads();  // K' is no longer read: dU replaces it
 #pragma unroll
@@ -1156,13 +1199,13 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
     // dk before this kernel's share, loaded ahead of the products rather than one element at a
     // time after each
     float prior[NB][4];
+    float* rowp[4];  // the lane's column in rows t0 + r0 + 4 (l / 16) + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rowp[i] = a.dk + base + (int64_t)(t0 + r0 + 4 * g + i) * rs + l16;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + r0 + 4 * g + i;
-        prior[nb][i] = t < T ? a.dk[base + (int64_t)t * rs + 16 * nb + l16] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) prior[nb][i] = t0 + r0 + 4 * g + i < T ? rowp[i][16 * nb] : 0.f;
     const bf16* const ops[1] = {phikt};
     pipelined_blocks<D, 1>(ops, lane, [&](int nb, const FragSet<D, 1>& f) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -1174,31 +1217,34 @@ __global__ __launch_bounds__(512) void arl2_bwd_write_kernel(const BwdTokArgs a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + r0 + 4 * g + i;
-        if (t < T) a.dk[base + (int64_t)t * rs + 16 * nb + l16] = prior[nb][i] + c[i];
+        if (t < T) rowp[i][16 * nb] = prior[nb][i] + c[i];
       }
     });
   }
   // chunk sum K^T dU
   {
-    f32x4 p3[BPW];
+    f32x4 p3[MBW][NBW];
 #pragma unroll
-    for (int n = 0; n < BPW; ++n) p3[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) p3[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kTokChunk / 32; ++s) {
-      const bf16x8 ak = col_frag_global(kg, base, rs, t0 + 32 * s + 8 * g, T, 16 * mb + l16);
+      bf16x8 ak[MBW];
+      gcols(rkg, s, ak);
 #pragma unroll
-      for (int n = 0; n < BPW; ++n) {
+      for (int j = 0; j < NBW; ++j) {
         bf16x8 bh_, bl_;
-        col_frag<D>(abuf, s, 16 * (nb0 + n) + l16, g, bh_, bl_);
-        p3[n] = mfma16(ak, bh_, p3[n]);
-        p3[n] = mfma16(ak, bl_, p3[n]);
+        col_frag<D>(abuf, s, 16 * (nb0 + j) + l16, g, bh_, bl_);
+#pragma unroll
+        for (int i = 0; i < MBW; ++i) {
+          p3[i][j] = mfma16(ak[i], bh_, p3[i][j]);
+          p3[i][j] = mfma16(ak[i], bl_, p3[i][j]);
+        }
       }
       ARL2_BLOCK_FENCE();
     }
-#pragma unroll
-    for (int n = 0; n < BPW; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a.part[pidx(2, nb0 + n, 16 * mb + 4 * g + i)] = p3[n][i];
+    pstore(2, p3);
   }
 }
 
