@@ -72,12 +72,22 @@ __device__ __forceinline__ bf16x8 frag(const bf16* f, int s, int nb, int lane) {
   return ld_bf16x8(f + ((s * BwdShape<D>::NB + nb) * 64 + lane) * 8);
 }
 
+// 8 fp32 values as bf16 hi + lo (split_bf16's rounding), two at a time so that each rounding
+// of a pair is one packed conversion
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const Bf16Pair p = split_bf16(x[j]);
-    hi[j] = p.hi;
-    lo[j] = p.lo;
+  for (int j = 0; j < 8; j += 2) {
+    const f32x2v v = {x[j], x[j + 1]};
+    const bf16x2v h = __builtin_convertvector(v, bf16x2v);
+    const f32x2v hf = __builtin_convertvector(h, f32x2v);
+    const f32x2v r = {v[0] - hf[0], v[1] - hf[1]};
+    const bf16x2v l = __builtin_convertvector(r, bf16x2v);
+    hi[j] = h[0];
+    hi[j + 1] = h[1];
+    lo[j] = l[0];
+    lo[j + 1] = l[1];
   }
 }
 
