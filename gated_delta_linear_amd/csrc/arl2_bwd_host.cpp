@@ -331,13 +331,15 @@ arl2_status arl2_bwd_pass(arl2_bwd* g, const void* q, const void* k, const void*
   a.scale = g->scale;
   a.scale_log2 = g->scale_log2;
   a.dq_read = g->dq_read;
-  // Caller's stream: S fragments | recompute | prep | dK, dV, dQ | (join) gr sums, dq += read's part
-  // side stream:                 (fork) read (dq_read, chunk partials of Q^T dO) |
-  // Each wait is enqueued after the record it waits for.
+  // Caller's stream: recompute | prep | dK, dV, dQ | (join) gr sums, dq += read's part
+  // side stream:     (fork) S fragments | read (dq_read, chunk partials of Q^T dO) |
+  // Only the read takes the S fragments, so they stay off the caller's stream; the fragment
+  // buffers are next written by a later call's work, which the join or the next fork orders
+  // after the read.  Each wait is enqueued after the record it waits for.
   using arl2::BwdStage;
   hipError_t e;
-  if ((st = frags(g, s_prev, false, stream))) return st;
   if ((e = order_after(g->ev_fork, stream, g->side)) != hipSuccess) return hip_fail(g, e, "stream fork");
+  if ((st = frags(g, s_prev, false, g->side))) return st;
   if ((st = after_launch(g, arl2::launch_bwd_stage(g->d, BwdStage::kRead, a, g->side), g->side, "inter-frame read backward")))
     return st;
   if ((st = after_launch(g, arl2::launch_fwd(g->d, f, nullptr, stream), stream, "softmax recompute"))) return st;
