@@ -721,13 +721,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (row0 + r < T) {
       const int64_t o = base + (int64_t)(row0 + r) * rs + 32 * o0 + 4 * c;
       if (!INTER && add) x += *reinterpret_cast<const f32x4*>(add + o);
+      // Streaming (non-temporal) stores: the output is written once and read only by later
+      // kernels, so it need not hold L2 lines that the other work-groups' K and V tiles use.
       if (OUT_BF16) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (bf16)x[e];
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o) = w;
+        __builtin_nontemporal_store(w, reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o));
       } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = x;
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o));
       }
     }
   }
