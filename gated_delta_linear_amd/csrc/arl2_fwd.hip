@@ -721,15 +721,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (row0 + r < T) {
       const int64_t o = base + (int64_t)(row0 + r) * rs + 32 * o0 + 4 * c;
       if (!INTER && add) x += *reinterpret_cast<const f32x4*>(add + o);
-      // Streaming (non-temporal) stores: the output is written once and read only by later
-      // kernels, so it need not hold L2 lines that the other work-groups' K and V tiles use.
+      // The ARL2 pass stores with streaming (non-temporal) stores: its output is written once and
+      // read only by later kernels, so it need not hold L2 lines that the other work-groups' K and
+      // V tiles use.  The plain-attention instance keeps ordinary stores: a backward's recompute
+      // is read by the very next kernel.  (The choice is made at compile time: with a run-time
+      // branch the compiler merges the two stores into an ordinary one.)
       if (OUT_BF16) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (bf16)x[e];
-        __builtin_nontemporal_store(w, reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o));
+        bf16x4* dst = reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(out) + o);
+        if constexpr (INTER) __builtin_nontemporal_store(w, dst);
+        else *dst = w;
       } else {
-        __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o));
+        f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o);
+        if constexpr (INTER) __builtin_nontemporal_store(x, dst);
+        else *dst = x;
       }
     }
   }
